@@ -1,0 +1,212 @@
+/*
+ * svdq.h -- C ABI of the MI355X (gfx950) SVDQuant W4A4 + low-rank linear layer.
+ *
+ * The layer computes (Zhou, SVDQuant reading notes, sec. 4.2, Eq. (7)):
+ *
+ *     Y = Q(X diag(lambda)^-1) Q(R) + (X diag(lambda)^-1 L1) L2 + bias
+ *
+ * with X [M, K] bf16 activations, lambda [K] the smoothing vector (Eq. (3),
+ * (4)), L1 [K, r] / L2 [r, N] bf16 low-rank factors (Eq. (10)), R [K, N] the
+ * residual quantized to 4 bits and Y [M, N] bf16.  Two 4-bit formats:
+ *   SVDQ_INT4_G64   symmetric INT4 codes -7..7, one fp16 scale per 64
+ *                   elements along K (notes sec. 2.2 Eq. (1) and sec. 8);
+ *   SVDQ_MXFP4_G32  E2M1 codes, one E8M0 power-of-two scale per 32
+ *                   elements along K (AutoRound SVDQuant doc, export
+ *                   section: MXFP4 E2M1, group 32, symmetric, dynamic
+ *                   activation quantization).
+ *
+ * Conventions for every entry point:
+ *  - Plain pointers and sizes only.  "host" pointers are CPU memory,
+ *    "device" pointers are HIP device memory on the current device.
+ *  - The caller owns every buffer.  The library allocates no device memory
+ *    and keeps no global mutable state; all entry points are re-entrant.
+ *  - Device calls are asynchronous on `stream` (a hipStream_t, NULL = the
+ *    default stream) and never synchronize.  All arguments are validated on
+ *    the host before any HIP call; a failed validation returns an error and
+ *    launches nothing.
+ *  - Errors are returned as svdq_status; nothing aborts or throws across
+ *    the ABI.  Host entry points leave their outputs unspecified on error.
+ *  - bf16 and fp16 values travel as uint16_t bit patterns.
+ *  - Matrices are row-major.
+ */
+#ifndef SVDQ_H
+#define SVDQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SVDQ_ABI_VERSION 1
+#define SVDQ_MAX_RANK 128   /* msModelSlim doc, svd_res: rank not above 128 recommended */
+
+typedef enum svdq_status {
+  SVDQ_OK = 0,
+  SVDQ_ERR_ARG = 1,          /* NULL pointer, value out of range */
+  SVDQ_ERR_SHAPE = 2,        /* M, K, N or rank not supported */
+  SVDQ_ERR_ALIGN = 3,        /* device pointer not 16-byte aligned */
+  SVDQ_ERR_UNSUPPORTED = 4,  /* unknown format, or the device is not gfx950 */
+  SVDQ_ERR_WORKSPACE = 5,    /* workspace smaller than svdq_workspace_bytes() */
+  SVDQ_ERR_NUMERIC = 6,      /* NaN/Inf in prepare inputs, or the eigen solver did not converge */
+  SVDQ_ERR_DEVICE = 7        /* a HIP call failed */
+} svdq_status;
+
+typedef enum svdq_format { SVDQ_INT4_G64 = 0, SVDQ_MXFP4_G32 = 1 } svdq_format;
+
+/* ------------------------------------------------------------------------
+ * Shape rules (checked by every entry point):
+ *   K % 128 == 0, 128 <= K <= 65536; N % 16 == 0, 16 <= N <= 262144;
+ *   1 <= M <= 1048576 (no alignment; the tail rows are masked);
+ *   0 <= rank <= SVDQ_MAX_RANK and rank % 16 == 0 (rank 0 = plain W4A4).
+ * ---------------------------------------------------------------------- */
+
+/* ---------------------------- device layer ---------------------------- */
+
+/* One prepared layer in kernel layout.  All pointers are device pointers,
+ * 16-byte aligned, caller-owned and never freed by the library.  The buffers
+ * are produced on the host by svdq_kernel_layout() and copied to the device
+ * unchanged; their sizes come from svdq_layer_sizes(). */
+typedef struct svdq_layer {
+  int32_t K, N, rank, fmt;       /* rank = total low-rank width (r, or r + LoRA k) */
+  const float*    smooth_inv;    /* [K] fp32 1/lambda */
+  const uint8_t*  wq;            /* weight codes, kernel layout (wq_bytes) */
+  const uint8_t*  ws;            /* weight scales, kernel layout (ws_bytes) */
+  const uint16_t* l1k;           /* down factor, kernel layout (l1k_bytes); unused if rank == 0 */
+  const uint16_t* l2k;           /* up factor, kernel layout (l2k_bytes); unused if rank == 0 */
+  const uint16_t* bias;          /* [N] bf16, or NULL for no bias */
+} svdq_layer;
+
+typedef struct svdq_sizes {
+  size_t wq_bytes, ws_bytes, l1k_bytes, l2k_bytes;
+  size_t wq_canon_bytes, ws_canon_bytes;   /* canonical [N, K/2] codes and [N, K/G] scales */
+} svdq_sizes;
+
+/* Byte sizes of the kernel-layout and canonical buffers of a layer.
+ * Errors: SVDQ_ERR_ARG (out NULL), SVDQ_ERR_SHAPE, SVDQ_ERR_UNSUPPORTED (fmt). */
+svdq_status svdq_layer_sizes(int32_t K, int32_t N, int32_t rank, int32_t fmt, svdq_sizes* out);
+
+/* --------------------------- workspace ------------------------------- */
+
+/* Per-call device workspace.  Regions, each 256-byte aligned:
+ *   xq   activation codes [M, K/2], two 4-bit codes per byte (MXFP4:
+ *        canonical order; INT4: the bytes of each 128-element step permuted
+ *        as for the weight codes)
+ *   xs   activation scales (INT4: canonical [M, K/64] fp16 bits; MXFP4:
+ *        E8M0 bytes in the permuted per-row layout of the weight scales)
+ *   z    down-projection partial sums, fp32 [zsplit][M][rank rounded up to 32]
+ * svdq_unpack_activations() turns a host copy into canonical form. */
+typedef struct svdq_ws_layout {
+  size_t xq_off, xq_bytes, xs_off, xs_bytes, z_off, z_bytes, total;
+  int32_t zsplit;                 /* number of K splits of the down projection */
+} svdq_ws_layout;
+
+svdq_status svdq_workspace_layout(int32_t M, int32_t K, int32_t rank, int32_t fmt, svdq_ws_layout* out);
+size_t svdq_workspace_bytes(int32_t M, int32_t K, int32_t rank, int32_t fmt);  /* 0 on invalid shape */
+
+/* ------------------------- host preparation --------------------------- */
+
+/* Running per-channel absolute maximum over calibration activations
+ * (notes, Algorithm 1 step 1: statistics from calibration inputs):
+ * amax[k] = max(amax[k], |x[i,k]|) for all rows i.  x: host [rows, K] bf16;
+ * amax: host [K] fp32, in/out (start from zeros).  Errors: ARG, NUMERIC
+ * (NaN/Inf in x). */
+svdq_status svdq_calib_absmax(const uint16_t* x, int64_t rows, int32_t K, float* amax);
+
+typedef struct svdq_prepare_opts {
+  int32_t        lora_rank;       /* k >= 0, rank + k <= SVDQ_MAX_RANK, multiple of 16 */
+  const float*   lora_a;          /* host [K, k] (adapter A, unsmoothed coordinates) */
+  const float*   lora_b;          /* host [k, N] */
+  float          lora_strength;   /* absorbed into B */
+  int32_t        threads;         /* host threads; 0 = all available */
+  int32_t        max_iters;       /* eigen solver iteration cap per value; 0 = default, < 0 forces
+                                     SVDQ_ERR_NUMERIC (test hook) */
+} svdq_prepare_opts;
+
+/* Canonical host outputs of svdq_prepare (caller-allocated). */
+typedef struct svdq_prepared {
+  float*    lambda;       /* [K] fp32 lambda (optional, may be NULL) */
+  float*    smooth_inv;   /* [K] fp32 1/lambda (required) */
+  uint16_t* l1;           /* [K, rank + k] bf16 L1' = [L1 | bf16(D A)] (required if rank + k > 0) */
+  uint16_t* l2;           /* [rank + k, N] bf16 L2' = [L2 ; bf16(s B)] (required if rank + k > 0) */
+  float*    residual;     /* [K, N] fp32 R (optional) */
+  double*   sigma;        /* [rank] leading singular values of diag(lambda) W (optional) */
+  uint8_t*  wq;           /* [N, K/2] canonical codes of R^T (required) */
+  uint8_t*  ws;           /* [N, K/G] canonical scales: fp16 bits (INT4) or E8M0 bytes (MXFP4) (required) */
+} svdq_prepared;
+
+/* Offline preparation of one layer (notes, Algorithm 1; AutoRound doc,
+ * "Residual iteration" with residual_iters = 1):
+ *   lambda_i = amaxX_i^alpha / amaxW_i^(1-alpha)  (Eq. (4); 1 when either is 0)
+ *   W~ = diag(lambda) W                            (Eq. (3))
+ *   L1 = U_r S_r, L2 = V_r^T of W~                 (Eq. (10), exact top-r)
+ *   L1b, L2b = bf16(L1), bf16(L2); R = W~ - L1b L2b (fp64, stored fp32)
+ *   codes/scales = RTN of R^T grouped along K in `fmt`.
+ * W: host [K, N] fp32; act_amax: host [K] fp32 (svdq_calib_absmax);
+ * alpha in [0, 1].  A grouped projection (e.g. Q|K|V) is passed as the
+ * column concatenation of its weights: one lambda, one shared L1, and the
+ * separate up factors are the column blocks of L2.
+ * Errors: ARG, SHAPE, UNSUPPORTED, NUMERIC (NaN/Inf inputs, solver failure). */
+svdq_status svdq_prepare(const float* W, const float* act_amax, int32_t K, int32_t N, double alpha,
+                         int32_t rank, int32_t fmt, const svdq_prepare_opts* opts, svdq_prepared* out);
+
+/* RTN quantization of a host [rows, K] fp32 matrix, grouped along K, into
+ * canonical codes [rows, K/2] (element 2j in the low nibble of byte j) and
+ * canonical scales [rows, K/G] (fp16 bits or E8M0 bytes).  Errors: ARG, SHAPE. */
+svdq_status svdq_pack_host(const float* x, int32_t rows, int32_t K, int32_t fmt,
+                           uint8_t* codes, uint8_t* scales);
+
+/* LoRA attach (notes sec. 7, Eq. (13)): l1_out = [l1 | bf16(diag(lambda) A)],
+ * l2_out = [l2 ; bf16(strength B)].  The residual codes are unchanged.
+ * l1: [K, rank] bf16, l2: [rank, N] bf16, A: [K, k] fp32, B: [k, N] fp32;
+ * l1_out: [K, rank + k], l2_out: [rank + k, N].  Errors: ARG, SHAPE. */
+svdq_status svdq_attach_lora(const float* lambda, const uint16_t* l1, const uint16_t* l2,
+                             int32_t K, int32_t N, int32_t rank, const float* A, const float* B,
+                             int32_t k, float strength, uint16_t* l1_out, uint16_t* l2_out);
+
+/* Canonical host buffers -> kernel-layout host buffers (sizes from
+ * svdq_layer_sizes).  l1 may be NULL when rank == 0.  The down factor is
+ * stored pre-multiplied by diag(smooth_inv), split into a bf16 hi/lo pair. */
+svdq_status svdq_kernel_layout(int32_t K, int32_t N, int32_t rank, int32_t fmt,
+                               const float* smooth_inv, const uint8_t* wq, const uint8_t* ws,
+                               const uint16_t* l1, const uint16_t* l2,
+                               uint8_t* wq_k, uint8_t* ws_k, uint16_t* l1k, uint16_t* l2k);
+
+/* Host copy of a workspace -> canonical activation codes [M, K/2], scales
+ * [M, K/G] and (if z != NULL) the summed down projection z [M, rank] fp32. */
+svdq_status svdq_unpack_activations(const void* ws_host, int32_t M, int32_t K, int32_t rank, int32_t fmt,
+                                    uint8_t* xq, uint8_t* xs, float* z);
+
+/* ---------------------------- device path ----------------------------- */
+
+/* K-A: fused smoothing + group absmax + 4-bit quantize/pack + lora_down
+ * (notes, Algorithm 2 steps 1-3; AutoRound/msModelSlim "lora_down").
+ * Reads X once: x~ = fp32(x * smooth_inv), per-group scales and codes into
+ * the workspace, z = X diag(smooth_inv) L1' as fp32 partial sums.
+ * X: device [M, K] bf16.  Errors: ARG, SHAPE, ALIGN, WORKSPACE, UNSUPPORTED, DEVICE. */
+svdq_status svdq_quantize_lora_down(const svdq_layer* layer, const uint16_t* X, int32_t M,
+                                    void* ws, size_t ws_bytes, void* stream);
+
+/* K-B: W4A4 GEMM with per-group scales, lora_up epilogue (z L2') and bias,
+ * one bf16 store of Y (notes, Algorithm 2 steps 4-7).
+ * Y: device [M, N] bf16.  Errors: as above. */
+svdq_status svdq_gemm_lora_up(const svdq_layer* layer, const void* ws, size_t ws_bytes, int32_t M,
+                              uint16_t* Y, void* stream);
+
+/* K-A then K-B on `stream`. */
+svdq_status svdq_linear_forward(const svdq_layer* layer, const uint16_t* X, int32_t M, uint16_t* Y,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------ misc ---------------------------------- */
+
+const char* svdq_status_str(svdq_status s);
+int32_t svdq_abi_version(void);
+/* SVDQ_OK if `device` is a gfx950 GPU, SVDQ_ERR_UNSUPPORTED otherwise,
+ * SVDQ_ERR_DEVICE if HIP cannot be queried (e.g. no GPU present). */
+svdq_status svdq_device_check(int32_t device);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SVDQ_H */

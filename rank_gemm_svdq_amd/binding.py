@@ -1,2 +1,297 @@
-"""ctypes binding of the C-ABI library (filled in with the library)."""
-__all__ = []
+"""ctypes binding of libsvdq (include/svdq.h).
+
+Argument marshalling only: every step of the layer runs in the C++ host code
+or the HIP kernels of the library.  Host arrays are numpy arrays; device
+buffers are torch CUDA tensors (torch supplies memory and streams).  A
+missing library raises ImportError-like RuntimeError on first use; there is
+no fallback.
+"""
+
+import ctypes as C
+import os
+
+import numpy as np
+
+__all__ = [
+    "INT4", "MXFP4", "SvdqError", "lib", "status_str", "abi_version", "device_check",
+    "layer_sizes", "workspace_layout", "workspace_bytes", "calib_absmax", "pack_host",
+    "prepare", "attach_lora", "kernel_layout", "unpack_activations", "DeviceLayer",
+    "quantize_lora_down", "gemm_lora_up", "linear_forward", "fmt_code", "LIB_PATH",
+]
+
+INT4 = 0
+MXFP4 = 1
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libsvdq.so")
+
+
+def fmt_code(fmt):
+    if fmt in (INT4, "int4"):
+        return INT4
+    if fmt in (MXFP4, "mxfp4"):
+        return MXFP4
+    raise ValueError(f"unknown format {fmt!r}")
+
+
+class SvdqError(RuntimeError):
+    def __init__(self, status, where):
+        super().__init__(f"{where}: {status_str(status)} (status {status})")
+        self.status = status
+
+
+class Layer(C.Structure):
+    _fields_ = [("K", C.c_int32), ("N", C.c_int32), ("rank", C.c_int32), ("fmt", C.c_int32),
+                ("smooth_inv", C.c_void_p), ("wq", C.c_void_p), ("ws", C.c_void_p),
+                ("l1k", C.c_void_p), ("l2k", C.c_void_p), ("bias", C.c_void_p)]
+
+
+class Sizes(C.Structure):
+    _fields_ = [(n, C.c_size_t) for n in ("wq_bytes", "ws_bytes", "l1k_bytes", "l2k_bytes",
+                                           "wq_canon_bytes", "ws_canon_bytes")]
+
+
+class WsLayout(C.Structure):
+    _fields_ = [(n, C.c_size_t) for n in ("xq_off", "xq_bytes", "xs_off", "xs_bytes", "z_off",
+                                           "z_bytes", "total")] + [("zsplit", C.c_int32)]
+
+
+class PrepareOpts(C.Structure):
+    _fields_ = [("lora_rank", C.c_int32), ("lora_a", C.c_void_p), ("lora_b", C.c_void_p),
+                ("lora_strength", C.c_float), ("threads", C.c_int32), ("max_iters", C.c_int32)]
+
+
+class Prepared(C.Structure):
+    _fields_ = [("lambda_", C.c_void_p), ("smooth_inv", C.c_void_p), ("l1", C.c_void_p),
+                ("l2", C.c_void_p), ("residual", C.c_void_p), ("sigma", C.c_void_p),
+                ("wq", C.c_void_p), ("ws", C.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libsvdq.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libsvdq.so not built ({LIB_PATH}); run __graft_entry__.build()")
+    L = C.CDLL(LIB_PATH)
+    i32, sz, vp = C.c_int32, C.c_size_t, C.c_void_p
+    L.svdq_status_str.restype = C.c_char_p
+    L.svdq_status_str.argtypes = [C.c_int]
+    L.svdq_abi_version.restype = i32
+    L.svdq_device_check.argtypes = [i32]
+    L.svdq_layer_sizes.argtypes = [i32, i32, i32, i32, C.POINTER(Sizes)]
+    L.svdq_workspace_layout.argtypes = [i32, i32, i32, i32, C.POINTER(WsLayout)]
+    L.svdq_workspace_bytes.restype = sz
+    L.svdq_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    L.svdq_calib_absmax.argtypes = [vp, C.c_int64, i32, vp]
+    L.svdq_pack_host.argtypes = [vp, i32, i32, i32, vp, vp]
+    L.svdq_prepare.argtypes = [vp, vp, i32, i32, C.c_double, i32, i32, C.POINTER(PrepareOpts), C.POINTER(Prepared)]
+    L.svdq_attach_lora.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, i32, C.c_float, vp, vp]
+    L.svdq_kernel_layout.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.svdq_unpack_activations.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp]
+    L.svdq_quantize_lora_down.argtypes = [C.POINTER(Layer), vp, i32, vp, sz, vp]
+    L.svdq_gemm_lora_up.argtypes = [C.POINTER(Layer), vp, sz, i32, vp, vp]
+    L.svdq_linear_forward.argtypes = [C.POINTER(Layer), vp, i32, vp, vp, sz, vp]
+    for name in ("svdq_device_check", "svdq_layer_sizes", "svdq_workspace_layout", "svdq_calib_absmax",
+                 "svdq_pack_host", "svdq_prepare", "svdq_attach_lora", "svdq_kernel_layout",
+                 "svdq_unpack_activations", "svdq_quantize_lora_down", "svdq_gemm_lora_up",
+                 "svdq_linear_forward"):
+        getattr(L, name).restype = C.c_int
+    _lib = L
+    return L
+
+
+def status_str(s):
+    return lib().svdq_status_str(int(s)).decode()
+
+
+def _check(s, where):
+    if s != 0:
+        raise SvdqError(s, where)
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def abi_version():
+    return lib().svdq_abi_version()
+
+
+def device_check(device=0):
+    return lib().svdq_device_check(device)
+
+
+def layer_sizes(K, N, rank, fmt):
+    s = Sizes()
+    _check(lib().svdq_layer_sizes(K, N, rank, fmt_code(fmt), C.byref(s)), "svdq_layer_sizes")
+    return {f: getattr(s, f) for f, _ in Sizes._fields_}
+
+
+def workspace_layout(M, K, rank, fmt):
+    w = WsLayout()
+    _check(lib().svdq_workspace_layout(M, K, rank, fmt_code(fmt), C.byref(w)), "svdq_workspace_layout")
+    return {f: getattr(w, f) for f, _ in WsLayout._fields_}
+
+
+def workspace_bytes(M, K, rank, fmt):
+    return lib().svdq_workspace_bytes(M, K, rank, fmt_code(fmt))
+
+
+def calib_absmax(x_bits, amax=None):
+    """Running per-channel max |x| of bf16 bit patterns [rows, K]."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    rows, K = x_bits.shape
+    amax = np.zeros(K, np.float32) if amax is None else np.ascontiguousarray(amax, np.float32).copy()
+    _check(lib().svdq_calib_absmax(_p(x_bits), rows, K, _p(amax)), "svdq_calib_absmax")
+    return amax
+
+
+def pack_host(x, fmt):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, K = x.shape
+    f = fmt_code(fmt)
+    codes = np.empty((rows, K // 2), np.uint8)
+    g, sb = (64, 2) if f == INT4 else (32, 1)
+    scales = np.empty((rows, (K // g) * sb), np.uint8)
+    _check(lib().svdq_pack_host(_p(x), rows, K, f, _p(codes), _p(scales)), "svdq_pack_host")
+    return codes, (scales.view(np.uint16) if f == INT4 else scales)
+
+
+def prepare(W, act_amax, alpha, rank, fmt, lora=None, threads=0, want_residual=False, max_iters=0):
+    """Offline prepare (svdq_prepare).  Returns canonical host arrays."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    act_amax = np.ascontiguousarray(act_amax, dtype=np.float32)
+    K, N = W.shape
+    f = fmt_code(fmt)
+    k = 0 if lora is None else lora["A"].shape[1]
+    rt = rank + k
+    out = {
+        "lambda": np.empty(K, np.float32), "smooth_inv": np.empty(K, np.float32),
+        "l1": np.empty((K, rt), np.uint16), "l2": np.empty((rt, N), np.uint16),
+        "sigma": np.empty(max(rank, 1), np.float64), "wq": np.empty((N, K // 2), np.uint8),
+        "ws": np.empty((N, (K // 64) * 2 if f == INT4 else K // 32), np.uint8),
+    }
+    if want_residual:
+        out["residual"] = np.empty((K, N), np.float32)
+    opts = PrepareOpts(0, None, None, 1.0, threads, max_iters)
+    keep = []
+    if lora is not None:
+        a = np.ascontiguousarray(lora["A"], np.float32)
+        b = np.ascontiguousarray(lora["B"], np.float32)
+        keep += [a, b]
+        opts.lora_rank, opts.lora_a, opts.lora_b = k, _p(a).value, _p(b).value
+        opts.lora_strength = float(lora.get("strength", 1.0))
+    pr = Prepared(_p(out["lambda"]).value, _p(out["smooth_inv"]).value,
+                  _p(out["l1"]).value if rt else None, _p(out["l2"]).value if rt else None,
+                  _p(out["residual"]).value if want_residual else None, _p(out["sigma"]).value,
+                  _p(out["wq"]).value, _p(out["ws"]).value)
+    _check(lib().svdq_prepare(_p(W), _p(act_amax), K, N, float(alpha), rank, f, C.byref(opts), C.byref(pr)),
+           "svdq_prepare")
+    if f == INT4:
+        out["ws"] = out["ws"].view(np.uint16)
+    out["sigma"] = out["sigma"][:rank]
+    out.update(K=K, N=N, rank=rt, fmt=f)
+    return out
+
+
+def attach_lora(lam, l1, l2, A, B, strength=1.0):
+    lam = np.ascontiguousarray(lam, np.float32)
+    l1 = np.ascontiguousarray(l1, np.uint16)
+    l2 = np.ascontiguousarray(l2, np.uint16)
+    A = np.ascontiguousarray(A, np.float32)
+    B = np.ascontiguousarray(B, np.float32)
+    K, rank = l1.shape
+    N = l2.shape[1]
+    k = A.shape[1]
+    l1o = np.empty((K, rank + k), np.uint16)
+    l2o = np.empty((rank + k, N), np.uint16)
+    _check(lib().svdq_attach_lora(_p(lam), _p(l1), _p(l2), K, N, rank, _p(A), _p(B), k, float(strength),
+                                  _p(l1o), _p(l2o)), "svdq_attach_lora")
+    return l1o, l2o
+
+
+def kernel_layout(prep):
+    """Canonical prepare outputs -> kernel-layout host arrays."""
+    K, N, rank, f = prep["K"], prep["N"], prep["rank"], prep["fmt"]
+    s = layer_sizes(K, N, rank, f)
+    out = {"wq_k": np.empty(s["wq_bytes"], np.uint8), "ws_k": np.empty(s["ws_bytes"], np.uint8),
+           "l1k": np.empty(max(s["l1k_bytes"] // 2, 8), np.uint16),
+           "l2k": np.empty(max(s["l2k_bytes"] // 2, 8), np.uint16)}
+    sinv = np.ascontiguousarray(prep["smooth_inv"], np.float32)
+    wq = np.ascontiguousarray(prep["wq"], np.uint8)
+    ws = np.ascontiguousarray(prep["ws"]).view(np.uint8)
+    l1 = np.ascontiguousarray(prep["l1"], np.uint16) if rank else None
+    l2 = np.ascontiguousarray(prep["l2"], np.uint16) if rank else None
+    _check(lib().svdq_kernel_layout(K, N, rank, f, _p(sinv), _p(wq), _p(ws), _p(l1), _p(l2),
+                                    _p(out["wq_k"]), _p(out["ws_k"]), _p(out["l1k"]), _p(out["l2k"])),
+           "svdq_kernel_layout")
+    return out
+
+
+def unpack_activations(ws_host, M, K, rank, fmt):
+    """Host copy of a workspace -> canonical (xq [M, K/2] u8, xs, z [M, rank] fp32)."""
+    f = fmt_code(fmt)
+    ws_host = np.ascontiguousarray(ws_host).view(np.uint8)
+    xq = np.empty((M, K // 2), np.uint8)
+    xs = np.empty((M, (K // 64) * 2 if f == INT4 else K // 32), np.uint8)
+    z = np.empty((M, max(rank, 1)), np.float32)
+    _check(lib().svdq_unpack_activations(_p(ws_host), M, K, rank, f, _p(xq), _p(xs), _p(z) if rank else None),
+           "svdq_unpack_activations")
+    return xq, (xs.view(np.uint16) if f == INT4 else xs), z[:, :rank]
+
+
+# ------------------------------------------------------------ device side
+
+def _torch():
+    import torch
+    return torch
+
+
+class DeviceLayer:
+    """Kernel-layout buffers of one layer in device memory (torch tensors)."""
+
+    def __init__(self, prep, bias_bits=None, device="cuda"):
+        torch = _torch()
+        kl = kernel_layout(prep)
+        self.K, self.N, self.rank, self.fmt = prep["K"], prep["N"], prep["rank"], prep["fmt"]
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+        self.smooth_inv = t(prep["smooth_inv"].astype(np.float32))
+        self.wq = t(kl["wq_k"])
+        self.ws = t(kl["ws_k"])
+        self.l1k = t(kl["l1k"].view(np.int16))
+        self.l2k = t(kl["l2k"].view(np.int16))
+        self.bias = None if bias_bits is None else t(np.asarray(bias_bits, np.uint16).view(np.int16))
+        self.struct = Layer(self.K, self.N, self.rank, self.fmt, self.smooth_inv.data_ptr(),
+                            self.wq.data_ptr(), self.ws.data_ptr(), self.l1k.data_ptr(), self.l2k.data_ptr(),
+                            None if self.bias is None else self.bias.data_ptr())
+
+    def workspace(self, M):
+        torch = _torch()
+        return torch.empty(workspace_bytes(M, self.K, self.rank, self.fmt), dtype=torch.uint8,
+                           device=self.wq.device)
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def quantize_lora_down(layer, X, ws, stream=None):
+    M = X.shape[0]
+    _check(lib().svdq_quantize_lora_down(C.byref(layer.struct), X.data_ptr(), M, ws.data_ptr(), ws.numel(),
+                                         _stream(stream)), "svdq_quantize_lora_down")
+
+
+def gemm_lora_up(layer, ws, M, Y, stream=None):
+    _check(lib().svdq_gemm_lora_up(C.byref(layer.struct), ws.data_ptr(), ws.numel(), M, Y.data_ptr(),
+                                   _stream(stream)), "svdq_gemm_lora_up")
+
+
+def linear_forward(layer, X, Y, ws, stream=None):
+    M = X.shape[0]
+    _check(lib().svdq_linear_forward(C.byref(layer.struct), X.data_ptr(), M, Y.data_ptr(), ws.data_ptr(),
+                                     ws.numel(), _stream(stream)), "svdq_linear_forward")

@@ -1,0 +1,554 @@
+// gfx950 kernels of the SVDQuant W4A4 + low-rank linear layer and the device
+// entry points of the C ABI.
+//
+// Dataflow (Zhou, SVDQuant reading notes, sec. 6.1, Algorithm 2): K-A reads a
+// tile of X once and produces both the 4-bit activation codes/scales and the
+// down projection Z = X^ L1'; K-B runs the 4-bit main contraction and merges
+// Z L2' and the bias into the same fp32 accumulators before the single bf16
+// store of Y.
+//
+// MFMA operand conventions (checked on the device by lane-layout probes):
+// for v_mfma_*_16x16x{32 bf16, 64 i8, 128 f4}, lane l supplies row l % 16 of
+// A (and column l % 16 of B) for the K slice owned by lane group l / 16; the
+// K slices of A and B pair up by lane group.  The 16x16 fp32 result lives in
+// lane l, register i at row 4 (l / 16) + i, column l % 16.  The scaled FP4
+// MFMA applies lane l's E8M0 byte to the 32 values lane l supplies.
+//
+// K-B computes Y^T tiles: A = weights (rows n), B = activations (rows m), so
+// each lane owns 4 consecutive outputs n of one token m (an 8-byte store).
+//
+// Layouts (all per row, K split into 128-element steps):
+//   MXFP4 codes: canonical, element 2j in the low nibble of byte j.
+//   MXFP4 scales: row of ceil(steps/4) * 16 bytes, block b = 4t + g at
+//     byte 16 (t / 4) + 4 g + (t % 4) (one dword per lane serves 4 steps).
+//   INT4 codes: within a step's 64 bytes, element k (G = k / 64, g = k % 64
+//     / 16, j = k % 16) sits at byte 16 g + 8 G + j / 2, nibble j % 2, so the
+//     16 bytes of lane group g hold 16 elements of each of the step's two
+//     64-element groups.
+//   INT4 activation scales: canonical [M][K/64] fp16.
+//   INT4 weight scales: [N/4][steps][4 rows][2 groups] fp16.
+//   Down factor: bf16 hi/lo split of diag(1/lambda) L1', ordered
+//     [step][hi/lo][s][n-tile][lane][8] with k = 128 step + 32 (lane/16) + 8 s + i.
+//   Up factor: L2'^T, [N][rpad] bf16, rpad = rank rounded up to 32.
+//   Z partial sums: fp32 [zsplit][M][rpad].
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "host_internal.h"
+
+namespace svdq {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// ----------------------------------------------------------------- K-A
+
+// One wave handles 16 rows and the K range of one split; lane l owns row
+// l % 16 and the 32 consecutive elements 32 (l / 16) .. +32 of each step.
+template <int FMT, int NT>
+__global__ __launch_bounds__(256) void ka_kernel(const uint16_t* __restrict__ X, int M, int K,
+                                                 const float* __restrict__ sinv,
+                                                 const v8bf* __restrict__ l1k,
+                                                 uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
+                                                 float* __restrict__ zp, int steps_per_split, int rpad) {
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int row0 = wave * 16;
+  if (row0 >= M) return;
+  const int r = lane & 15, g = lane >> 4;
+  const int row = row0 + r;
+  const int rowc = row < M ? row : M - 1;
+  const bool live = row < M;
+  const int steps = K / 128;
+  const int ks4 = (steps + 3) / 4;
+  const int split = blockIdx.y;
+  const int t0 = split * steps_per_split;
+  const uint16_t* xrow = X + (size_t)rowc * K;
+  v4f acc[NT > 0 ? NT : 1];
+#pragma unroll
+  for (int nt = 0; nt < (NT > 0 ? NT : 1); ++nt) acc[nt] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  for (int t = t0; t < t0 + steps_per_split; ++t) {
+    const int k0 = t * 128 + 32 * g;
+    v4i raw[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) raw[c] = *reinterpret_cast<const v4i*>(xrow + k0 + 8 * c);
+    float xh[32];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const v4f iv = *reinterpret_cast<const v4f*>(sinv + k0 + 4 * c);
+      const uint32_t w0 = (uint32_t)raw[c >> 1][(c & 1) * 2], w1 = (uint32_t)raw[c >> 1][(c & 1) * 2 + 1];
+      xh[4 * c + 0] = bf16_lo(w0) * iv[0];
+      xh[4 * c + 1] = bf16_hi(w0) * iv[1];
+      xh[4 * c + 2] = bf16_lo(w1) * iv[2];
+      xh[4 * c + 3] = bf16_hi(w1) * iv[3];
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(xh[i]));
+
+    if constexpr (FMT == SVDQ_MXFP4_G32) {
+      // smallest e with amax <= 6 * 2^e, clamped to [-127, 127]
+      const uint32_t ab = __float_as_uint(amax);
+      const int ex = (int)(ab >> 23);
+      int e = ex == 0 ? -127 : ex - 129 + ((ab & 0x7FFFFFu) > 0x400000u ? 1 : 0);
+      e = e < -127 ? -127 : (e > 127 ? 127 : e);
+      v4i packed;
+      if (e >= -126) {
+        const float scale = __uint_as_float((uint32_t)(e + 127) << 23);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t d = 0;
+          d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, xh[8 * w + 0], xh[8 * w + 1], scale, 0);
+          d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, xh[8 * w + 2], xh[8 * w + 3], scale, 1);
+          d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, xh[8 * w + 4], xh[8 * w + 5], scale, 2);
+          d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, xh[8 * w + 6], xh[8 * w + 7], scale, 3);
+          packed[w] = (int)d;
+        }
+      } else {
+        // block maximum below 6 * 2^-126: exact comparison against the E2M1
+        // midpoints of |x| * 2^127 (no denormal scale operand)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t d = 0;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float v = xh[8 * w + j];
+            const float a = fabsf(v) * 1.7014118346046923e38f;   // 2^127
+            uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) +
+                         (a > 5.0f);
+            c |= (__float_as_uint(v) >> 28) & 8u;
+            d |= c << (4 * j);
+          }
+          packed[w] = (int)d;
+        }
+      }
+      if (live) {
+        *reinterpret_cast<v4i*>(xq + (size_t)row * (K / 2) + (size_t)t * 64 + 16 * g) = packed;
+        const int b = 4 * t + g;
+        xs[(size_t)row * ks4 * 16 + (size_t)(b >> 4) * 16 + (b & 3) * 4 + ((b >> 2) & 3)] = (uint8_t)(e + 127);
+      }
+    } else {
+      // INT4: the 64-element group spans lane groups g and g ^ 1
+      const float amax64 = fmaxf(amax, __shfl_xor(amax, 16));
+      const float s32 = amax64 / 7.0f;
+      const _Float16 s16 = (_Float16)s32;
+      const float sf = (float)s16;
+      uint32_t d[4] = {0u, 0u, 0u, 0u};
+      if (sf != 0.f) {
+        const float rcp = 1.0f / sf;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          float q = __builtin_rintf(xh[i] * rcp);
+          q = fminf(fmaxf(q, -7.f), 7.f);
+          d[i >> 3] |= ((uint32_t)(int)q & 0xFu) << (4 * (i & 7));
+        }
+      }
+      if (live) {
+        const int G = g >> 1, half = g & 1;
+        uint8_t* base = xq + (size_t)row * (K / 2) + (size_t)t * 64 + 32 * half + 8 * G;
+        *reinterpret_cast<uint2*>(base) = make_uint2(d[0], d[1]);
+        *reinterpret_cast<uint2*>(base + 16) = make_uint2(d[2], d[3]);
+        if (half == 0) {
+          uint16_t sb;
+          __builtin_memcpy(&sb, &s16, 2);
+          reinterpret_cast<uint16_t*>(xs)[(size_t)row * (K / 64) + 2 * t + G] = sb;
+        }
+      }
+    }
+
+    if constexpr (NT > 0) {
+      // Z += X diag(1/lambda) L1' with the scaling folded into the factor;
+      // the raw bf16 X words are the A operand.
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const v8bf a = __builtin_bit_cast(v8bf, raw[s]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const v8bf b = l1k[((((size_t)t * 2 + h) * 4 + s) * NT + nt) * 64 + lane];
+            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[nt], 0, 0, 0);
+          }
+      }
+    }
+  }
+  if constexpr (NT > 0) {
+    // result rows 4 g + i of the wave's 16, column 16 nt + r
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = row0 + 4 * g + i;
+        if (m < M) zp[((size_t)split * M + m) * rpad + 16 * nt + r] = acc[nt][i];
+      }
+  }
+}
+
+// ----------------------------------------------------------------- K-B
+
+constexpr int BM = 128, BN = 128;          // tile: tokens x out-features
+constexpr int LDS_TILE = (BM + BN) * 64;   // one step of both operands, bytes
+
+// swizzled byte offset of 16-byte chunk c of row r inside a [rows][64 B] tile
+__device__ __forceinline__ int swz(int r, int c) { return r * 64 + 16 * (c ^ ((r >> 2) & 3)); }
+
+template <int FMT, int NTR>
+__global__ __launch_bounds__(256) void kb_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
+                                                 const float* __restrict__ zp, int zsplit,
+                                                 const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws,
+                                                 const uint16_t* __restrict__ l2k, const uint16_t* __restrict__ bias,
+                                                 uint16_t* __restrict__ Y, int M, int N, int K, int rpad) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * LDS_TILE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int tile_n = blockIdx.x * BN, tile_m = blockIdx.y * BM;
+  const int steps = K / 128;
+  const size_t rowbytes = (size_t)K / 2;
+
+  v4f acc[4][4];   // [n-tile][m-tile]
+
+  // ---- bias and low-rank up projection initialise the accumulators
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int n0 = tile_n + 64 * wn + 16 * nt + 4 * g;   // this lane's 4 output rows n
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (bias != nullptr) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = n0 + i < N ? n0 + i : N - 1;
+        bv[i] = __uint_as_float((uint32_t)bias[n] << 16);
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[nt][mt] = (v4f){bv[0], bv[1], bv[2], bv[3]};
+  }
+  if constexpr (NTR > 0) {
+#pragma unroll
+    for (int u = 0; u < NTR; ++u) {
+      v8bf af[4], bh[4], bl[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        int n = tile_n + 64 * wn + 16 * nt + l16;
+        n = n < N ? n : N - 1;
+        af[nt] = *reinterpret_cast<const v8bf*>(l2k + (size_t)n * rpad + 32 * u + 8 * g);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        int m = tile_m + 64 * wm + 16 * mt + l16;
+        m = m < M ? m : M - 1;
+        float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int p = 0; p < zsplit; ++p) {
+          const float* src = zp + ((size_t)p * M + m) * rpad + 32 * u + 8 * g;
+          const v4f z0 = *reinterpret_cast<const v4f*>(src), z1 = *reinterpret_cast<const v4f*>(src + 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) { z[i] += z0[i]; z[4 + i] += z1[i]; }
+        }
+        uint16_t hi[8], lo[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t hb = bf16_rne(z[i]);
+          hi[i] = (uint16_t)hb;
+          lo[i] = (uint16_t)bf16_rne(z[i] - __uint_as_float(hb << 16));
+        }
+        bh[mt] = __builtin_bit_cast(v8bf, *reinterpret_cast<v4i*>(hi));
+        bl[mt] = __builtin_bit_cast(v8bf, *reinterpret_cast<v4i*>(lo));
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[nt], bh[mt], acc[nt][mt], 0, 0, 0);
+          acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[nt], bl[mt], acc[nt][mt], 0, 0, 0);
+        }
+    }
+  }
+
+  // ---- global -> LDS staging: thread tid moves 16 B of 2 rows of each operand
+  const int ld_row = tid >> 2, ld_chunk = tid & 3;
+  int xrow[2], wrow[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int m = tile_m + ld_row + 64 * j, n = tile_n + ld_row + 64 * j;
+    xrow[j] = m < M ? m : M - 1;
+    wrow[j] = n < N ? n : N - 1;
+  }
+  v4i stage[4];
+  auto gload = [&](int t) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      stage[j] = *reinterpret_cast<const v4i*>(xq + (size_t)xrow[j] * rowbytes + (size_t)t * 64 + 16 * ld_chunk);
+      stage[2 + j] = *reinterpret_cast<const v4i*>(wq + (size_t)wrow[j] * rowbytes + (size_t)t * 64 + 16 * ld_chunk);
+    }
+  };
+  auto lstore = [&](int buf) {
+    uint8_t* base = lds + buf * LDS_TILE;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      *reinterpret_cast<v4i*>(base + swz(ld_row + 64 * j, ld_chunk)) = stage[j];
+      *reinterpret_cast<v4i*>(base + BM * 64 + swz(ld_row + 64 * j, ld_chunk)) = stage[2 + j];
+    }
+  };
+
+  // per-lane operand rows (for scales)
+  int arow[4], brow[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int n = tile_n + 64 * wn + 16 * q + l16, m = tile_m + 64 * wm + 16 * q + l16;
+    arow[q] = n < N ? n : N - 1;
+    brow[q] = m < M ? m : M - 1;
+  }
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+
+  for (int t = 0; t < steps; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < steps) gload(t + 1);
+    const uint8_t* base = lds + buf * LDS_TILE;
+    v4i af[4], bf[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      af[q] = *reinterpret_cast<const v4i*>(base + BM * 64 + swz(64 * wn + 16 * q + l16, g));
+      bf[q] = *reinterpret_cast<const v4i*>(base + swz(64 * wm + 16 * q + l16, g));
+    }
+    if constexpr (FMT == SVDQ_MXFP4_G32) {
+      const int ks4 = (steps + 3) / 4;
+      const size_t soff = (size_t)(t >> 2) * 16 + 4 * g;
+      const int sh = 8 * (t & 3);
+      int asc[4], bsc[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        asc[q] = (int)((*reinterpret_cast<const uint32_t*>(ws + (size_t)arow[q] * ks4 * 16 + soff)) >> sh);
+        bsc[q] = (int)((*reinterpret_cast<const uint32_t*>(xs + (size_t)brow[q] * ks4 * 16 + soff)) >> sh);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const v8i a = (v8i){af[nt][0], af[nt][1], af[nt][2], af[nt][3], 0, 0, 0, 0};
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const v8i b = (v8i){bf[mt][0], bf[mt][1], bf[mt][2], bf[mt][3], 0, 0, 0, 0};
+          acc[nt][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[nt][mt], 4, 4, 0, asc[nt], 0,
+                                                                        bsc[mt]);
+        }
+      }
+    } else {
+      // INT4 on int8 MFMA: nibble q -> byte 16 q (products carry 2^8, folded
+      // into the scale product); one MFMA per 64-element group, then
+      // acc += float(I) * sw * sx.
+      float sw[4][4][2], sx[4][2];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        int n0 = tile_n + 64 * wn + 16 * nt + 4 * g;
+        n0 = n0 < N ? n0 : N - 4;
+        const v4i v = *reinterpret_cast<const v4i*>(ws + (((size_t)(n0 >> 2)) * steps + t) * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t w = (uint32_t)v[i];
+          sw[nt][i][0] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFF));
+          sw[nt][i][1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(xs + ((size_t)brow[mt] * (K / 64) + 2 * t) * 2);
+        sx[mt][0] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFF)) * (1.0f / 256.0f);
+        sx[mt][1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)) * (1.0f / 256.0f);
+      }
+      const uint32_t MSK = 0xF0F0F0F0u;
+#pragma unroll
+      for (int G = 0; G < 2; ++G) {
+        v4i a8[4], b8[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t a0 = (uint32_t)af[q][2 * G], a1 = (uint32_t)af[q][2 * G + 1];
+          const uint32_t b0 = (uint32_t)bf[q][2 * G], b1 = (uint32_t)bf[q][2 * G + 1];
+          a8[q] = (v4i){(int)((a0 << 4) & MSK), (int)(a0 & MSK), (int)((a1 << 4) & MSK), (int)(a1 & MSK)};
+          b8[q] = (v4i){(int)((b0 << 4) & MSK), (int)(b0 & MSK), (int)((b1 << 4) & MSK), (int)(b1 & MSK)};
+        }
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            const v4i I = __builtin_amdgcn_mfma_i32_16x16x64_i8(a8[nt], b8[mt], (v4i){0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[nt][mt][i] = __builtin_fmaf((float)I[i], sw[nt][i][G] * sx[mt][G], acc[nt][mt][i]);
+          }
+      }
+    }
+    if (t + 1 < steps) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- single bf16 store: lane owns Y[m][n0 .. n0 + 3]
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int m = tile_m + 64 * wm + 16 * mt + l16;
+    if (m >= M) continue;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int n0 = tile_n + 64 * wn + 16 * nt + 4 * g;
+      if (n0 >= N) continue;
+      const uint32_t lo = bf16_rne(acc[nt][mt][0]) | (bf16_rne(acc[nt][mt][1]) << 16);
+      const uint32_t hi = bf16_rne(acc[nt][mt][2]) | (bf16_rne(acc[nt][mt][3]) << 16);
+      *reinterpret_cast<uint2*>(Y + (size_t)m * N + n0) = make_uint2(lo, hi);
+    }
+  }
+}
+
+// ------------------------------------------------------------ dispatch
+
+template <int FMT>
+static hipError_t launch_ka(const svdq_layer& L, const uint16_t* X, int M, uint8_t* ws, const svdq_ws_layout& W,
+                            hipStream_t st) {
+  const int rp = rank_pad(L.rank);
+  const int steps = L.K / 128;
+  const int zs = L.rank > 0 ? W.zsplit : 1;
+  const int waves = (M + 15) / 16;
+  dim3 grid((waves + 3) / 4, zs), block(256);
+  uint8_t* xq = ws + W.xq_off;
+  uint8_t* xs = ws + W.xs_off;
+  float* zp = reinterpret_cast<float*>(ws + W.z_off);
+  const v8bf* l1 = reinterpret_cast<const v8bf*>(L.l1k);
+  const int sps = steps / zs;
+  switch (rp / 16) {
+    case 0: hipLaunchKernelGGL((ka_kernel<FMT, 0>), grid, block, 0, st, X, M, L.K, L.smooth_inv, l1, xq, xs, zp, sps, rp); break;
+    case 2: hipLaunchKernelGGL((ka_kernel<FMT, 2>), grid, block, 0, st, X, M, L.K, L.smooth_inv, l1, xq, xs, zp, sps, rp); break;
+    case 4: hipLaunchKernelGGL((ka_kernel<FMT, 4>), grid, block, 0, st, X, M, L.K, L.smooth_inv, l1, xq, xs, zp, sps, rp); break;
+    case 6: hipLaunchKernelGGL((ka_kernel<FMT, 6>), grid, block, 0, st, X, M, L.K, L.smooth_inv, l1, xq, xs, zp, sps, rp); break;
+    case 8: hipLaunchKernelGGL((ka_kernel<FMT, 8>), grid, block, 0, st, X, M, L.K, L.smooth_inv, l1, xq, xs, zp, sps, rp); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t launch_kb(const svdq_layer& L, const uint8_t* ws, const svdq_ws_layout& W, int M, uint16_t* Y,
+                            hipStream_t st) {
+  const int rp = rank_pad(L.rank);
+  dim3 grid((L.N + BN - 1) / BN, (M + BM - 1) / BM), block(256);
+  const uint8_t* xq = ws + W.xq_off;
+  const uint8_t* xs = ws + W.xs_off;
+  const float* zp = reinterpret_cast<const float*>(ws + W.z_off);
+  switch (rp / 32) {
+    case 0: hipLaunchKernelGGL((kb_kernel<FMT, 0>), grid, block, 0, st, xq, xs, zp, W.zsplit, L.wq, L.ws, L.l2k, L.bias, Y, M, L.N, L.K, rp); break;
+    case 1: hipLaunchKernelGGL((kb_kernel<FMT, 1>), grid, block, 0, st, xq, xs, zp, W.zsplit, L.wq, L.ws, L.l2k, L.bias, Y, M, L.N, L.K, rp); break;
+    case 2: hipLaunchKernelGGL((kb_kernel<FMT, 2>), grid, block, 0, st, xq, xs, zp, W.zsplit, L.wq, L.ws, L.l2k, L.bias, Y, M, L.N, L.K, rp); break;
+    case 3: hipLaunchKernelGGL((kb_kernel<FMT, 3>), grid, block, 0, st, xq, xs, zp, W.zsplit, L.wq, L.ws, L.l2k, L.bias, Y, M, L.N, L.K, rp); break;
+    case 4: hipLaunchKernelGGL((kb_kernel<FMT, 4>), grid, block, 0, st, xq, xs, zp, W.zsplit, L.wq, L.ws, L.l2k, L.bias, Y, M, L.N, L.K, rp); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static svdq_status check_layer(const svdq_layer* L, int32_t M) {
+  if (!L) return SVDQ_ERR_ARG;
+  if (!valid_fmt(L->fmt)) return SVDQ_ERR_UNSUPPORTED;
+  if (!valid_kn(L->K, L->N) || !valid_rank(L->rank) || M < 1 || M > (1 << 20)) return SVDQ_ERR_SHAPE;
+  if (!L->smooth_inv || !L->wq || !L->ws) return SVDQ_ERR_ARG;
+  if (L->rank > 0 && (!L->l1k || !L->l2k)) return SVDQ_ERR_ARG;
+  if (!aligned16(L->smooth_inv) || !aligned16(L->wq) || !aligned16(L->ws) ||
+      (L->rank > 0 && (!aligned16(L->l1k) || !aligned16(L->l2k))) || (L->bias && !aligned16(L->bias)))
+    return SVDQ_ERR_ALIGN;
+  return SVDQ_OK;
+}
+
+// gfx950 check, cached per device (write-once flags)
+static std::atomic<int> g_dev_ok[64];
+
+static svdq_status device_ok() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SVDQ_ERR_DEVICE;
+  if (dev < 0 || dev >= 64) return svdq_device_check(dev);
+  int v = g_dev_ok[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    svdq_status s = svdq_device_check(dev);
+    if (s == SVDQ_ERR_DEVICE) return s;
+    v = s == SVDQ_OK ? 1 : 2;
+    g_dev_ok[dev].store(v, std::memory_order_relaxed);
+  }
+  return v == 1 ? SVDQ_OK : SVDQ_ERR_UNSUPPORTED;
+}
+
+}  // namespace svdq
+
+using namespace svdq;
+
+extern "C" {
+
+svdq_status svdq_device_check(int32_t device) {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) return SVDQ_ERR_DEVICE;
+  if (device < 0 || device >= n) return SVDQ_ERR_ARG;
+  hipDeviceProp_t p;
+  if (hipGetDeviceProperties(&p, device) != hipSuccess) return SVDQ_ERR_DEVICE;
+  return std::strncmp(p.gcnArchName, "gfx950", 6) == 0 ? SVDQ_OK : SVDQ_ERR_UNSUPPORTED;
+}
+
+svdq_status svdq_quantize_lora_down(const svdq_layer* layer, const uint16_t* X, int32_t M, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  svdq_status s = check_layer(layer, M);
+  if (s != SVDQ_OK) return s;
+  if (!X || !ws) return SVDQ_ERR_ARG;
+  if (!aligned16(X) || !aligned16(ws)) return SVDQ_ERR_ALIGN;
+  svdq_ws_layout W;
+  if ((s = svdq_workspace_layout(M, layer->K, layer->rank, layer->fmt, &W)) != SVDQ_OK) return s;
+  if (ws_bytes < W.total) return SVDQ_ERR_WORKSPACE;
+  if ((s = device_ok()) != SVDQ_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = layer->fmt == SVDQ_MXFP4_G32
+                     ? launch_ka<SVDQ_MXFP4_G32>(*layer, X, M, static_cast<uint8_t*>(ws), W, st)
+                     : launch_ka<SVDQ_INT4_G64>(*layer, X, M, static_cast<uint8_t*>(ws), W, st);
+  return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_DEVICE;
+}
+
+svdq_status svdq_gemm_lora_up(const svdq_layer* layer, const void* ws, size_t ws_bytes, int32_t M, uint16_t* Y,
+                              void* stream) {
+  svdq_status s = check_layer(layer, M);
+  if (s != SVDQ_OK) return s;
+  if (!Y || !ws) return SVDQ_ERR_ARG;
+  if (!aligned16(Y) || !aligned16(ws)) return SVDQ_ERR_ALIGN;
+  svdq_ws_layout W;
+  if ((s = svdq_workspace_layout(M, layer->K, layer->rank, layer->fmt, &W)) != SVDQ_OK) return s;
+  if (ws_bytes < W.total) return SVDQ_ERR_WORKSPACE;
+  if ((s = device_ok()) != SVDQ_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = layer->fmt == SVDQ_MXFP4_G32
+                     ? launch_kb<SVDQ_MXFP4_G32>(*layer, static_cast<const uint8_t*>(ws), W, M, Y, st)
+                     : launch_kb<SVDQ_INT4_G64>(*layer, static_cast<const uint8_t*>(ws), W, M, Y, st);
+  return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_DEVICE;
+}
+
+svdq_status svdq_linear_forward(const svdq_layer* layer, const uint16_t* X, int32_t M, uint16_t* Y, void* ws,
+                                size_t ws_bytes, void* stream) {
+  // validate everything for both kernels before the first launch
+  svdq_status s = check_layer(layer, M);
+  if (s != SVDQ_OK) return s;
+  if (!X || !Y || !ws) return SVDQ_ERR_ARG;
+  if (!aligned16(X) || !aligned16(Y) || !aligned16(ws)) return SVDQ_ERR_ALIGN;
+  if ((s = svdq_quantize_lora_down(layer, X, M, ws, ws_bytes, stream)) != SVDQ_OK) return s;
+  return svdq_gemm_lora_up(layer, ws, ws_bytes, M, Y, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,507 @@
+// Host side of the C ABI: argument checks, sizes and layouts, calibration
+// statistics, RTN packers, the offline prepare, LoRA attach, kernel-layout
+// conversion and the workspace read-back helper.
+//
+// Compiled without fp contraction: the packers must reproduce IEEE fp32
+// products and divisions exactly (the quantized codes and scales are
+// specified bit for bit).
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+#include "host_internal.h"
+
+namespace svdq {
+
+// ---------------------------------------------------------------- shapes
+
+bool valid_kn(int32_t K, int32_t N) {
+  return K >= kStep && K <= 65536 && K % kStep == 0 && N >= 16 && N <= 262144 && N % 16 == 0;
+}
+bool valid_rank(int32_t rank) { return rank >= 0 && rank <= SVDQ_MAX_RANK && rank % 16 == 0; }
+bool valid_fmt(int32_t fmt) { return fmt == SVDQ_INT4_G64 || fmt == SVDQ_MXFP4_G32; }
+
+bool geometry(int32_t K, int32_t N, int32_t rank, int32_t fmt, Geometry* g) {
+  if (!valid_kn(K, N) || !valid_rank(rank) || !valid_fmt(fmt)) return false;
+  g->K = K; g->N = N; g->rank = rank; g->rpad = rank_pad(rank); g->fmt = fmt;
+  g->steps = K / kStep;
+  g->ks4 = (g->steps + 3) / 4;
+  g->wq_bytes = (size_t)N * K / 2;
+  g->ws_bytes = fmt == SVDQ_INT4_G64 ? (size_t)N * (K / 64) * 2 : (size_t)N * g->ks4 * 16;
+  g->l1k_bytes = (size_t)K * g->rpad * 2 * 2;
+  g->l2k_bytes = (size_t)N * g->rpad * 2;
+  return true;
+}
+
+int32_t choose_zsplit(int32_t M, int32_t K) {
+  const int32_t steps = K / kStep;
+  const int64_t rowwaves = ((int64_t)M + 15) / 16;
+  int32_t z = 1;
+  while (z * 2 <= 4 && steps % (z * 2) == 0 && rowwaves * z < 2048) z *= 2;
+  return z;
+}
+
+int default_threads(int requested) {
+  if (requested > 0) return requested;
+  unsigned h = std::thread::hardware_concurrency();
+  return h ? (int)std::min(h, 64u) : 1;
+}
+
+// ----------------------------------------------------------- conversions
+
+uint16_t bf16_from_double(double x) {
+  uint64_t b;
+  std::memcpy(&b, &x, 8);
+  const uint16_t sign = (uint16_t)((b >> 48) & 0x8000);
+  const int ex = (int)((b >> 52) & 0x7FF);
+  const uint64_t man = b & ((1ull << 52) - 1);
+  if (ex == 0x7FF) return sign | (man ? 0x7FC0 : 0x7F80);
+  if (ex == 0) return sign;                       // binary64 subnormals are far below bf16's range
+  int e = ex - 1023;
+  if (e >= -126) {                                // normal bf16: keep 7 fraction bits
+    uint64_t keep = man >> 45, rest = man & ((1ull << 45) - 1);
+    const uint64_t half = 1ull << 44;
+    if (rest > half || (rest == half && (keep & 1))) ++keep;
+    if (keep == 128) { keep = 0; ++e; }
+    if (e > 127) return sign | 0x7F80;
+    return sign | (uint16_t)((e + 127) << 7) | (uint16_t)keep;
+  }
+  // subnormal bf16: multiples of 2^-133; x = full * 2^(e-52)
+  const int sh = -81 - e;                         // q = full / 2^sh, sh >= 46
+  if (sh >= 64) return sign;
+  const uint64_t full = man | (1ull << 52);
+  uint64_t q = full >> sh, rest = full & ((1ull << sh) - 1);
+  const uint64_t half = 1ull << (sh - 1);
+  if (rest > half || (rest == half && (q & 1))) ++q;
+  return sign | (uint16_t)q;                      // q == 128 is the smallest normal
+}
+
+double double_from_bf16(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+uint16_t half_from_float(float f) {
+  uint32_t x;
+  std::memcpy(&x, &f, 4);
+  const uint16_t sign = (uint16_t)((x >> 16) & 0x8000);
+  const uint32_t ax = x & 0x7FFFFFFFu;
+  if (ax >= 0x7F800000u) return sign | 0x7C00 | (ax > 0x7F800000u ? 0x200 : 0);
+  const int e = (int)(ax >> 23) - 127;
+  const uint32_t m = ax & 0x7FFFFFu;
+  if (e >= -14) {
+    uint32_t h = ((uint32_t)(e + 15) << 10) | (m >> 13);
+    const uint32_t rest = m & 0x1FFFu;
+    if (rest > 0x1000u || (rest == 0x1000u && (h & 1))) ++h;   // may carry into the exponent
+    if (h >= 0x7C00u) return sign | 0x7C00;
+    return sign | (uint16_t)h;
+  }
+  if (e < -25) return sign;
+  // subnormal binary16: q * 2^-24 with q = full * 2^(e+1), full the 24-bit significand
+  const uint32_t full = m | 0x800000u;
+  const int sh = -(e + 1);                        // 14..24
+  uint32_t q = full >> sh, rest = full & ((1u << sh) - 1);
+  const uint32_t half = 1u << (sh - 1);
+  if (rest > half || (rest == half && (q & 1))) ++q;
+  return sign | (uint16_t)q;
+}
+
+float float_from_half(uint16_t h) {
+  const uint32_t sign = (uint32_t)(h & 0x8000) << 16;
+  const int ex = (h >> 10) & 0x1F;
+  const uint32_t m = h & 0x3FF;
+  float f;
+  if (ex == 0) {
+    f = std::ldexp((float)m, -24);
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    u |= sign;
+    std::memcpy(&f, &u, 4);
+    return f;
+  }
+  uint32_t u = ex == 0x1F ? (sign | 0x7F800000u | (m << 13)) : (sign | ((uint32_t)(ex - 15 + 127) << 23) | (m << 13));
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+// ------------------------------------------------------------ quantizers
+
+// INT4 (Zhou notes sec. 2.2 Eq. (1); 64 elements, fp16 scale): s32 = amax/7
+// in fp32, s16 = fp16(s32), codes = clamp(rint(x * fp32(1/s16)), -7, 7).
+void quant_int4_group(const float* x, uint8_t* nib, uint16_t* scale_bits) {
+  float amax = 0.0f;
+  for (int i = 0; i < 64; ++i) amax = std::max(amax, std::fabs(x[i]));
+  const float s32 = amax / 7.0f;
+  const uint16_t s16 = half_from_float(s32);
+  const float sf = float_from_half(s16);
+  *scale_bits = s16;
+  if (sf == 0.0f) {
+    std::memset(nib, 0, 64);
+    return;
+  }
+  const float rcp = 1.0f / sf;
+  for (int i = 0; i < 64; ++i) {
+    float y = x[i] * rcp;
+    float q = std::nearbyint(y);
+    q = std::min(7.0f, std::max(-7.0f, q));
+    nib[i] = (uint8_t)((int)q & 0xF);
+  }
+}
+
+// MXFP4 (E2M1, 32 elements, E8M0 scale): e = smallest integer with
+// amax <= 6 * 2^e (clamped to [-127, 127]); code = nearest E2M1 magnitude of
+// |x| 2^-e with ties to the even mantissa; bit 3 = sign of x.
+void quant_mxfp4_group(const float* x, uint8_t* nib, uint8_t* scale_byte) {
+  float amax = 0.0f;
+  for (int i = 0; i < 32; ++i) amax = std::max(amax, std::fabs(x[i]));
+  int e;
+  if (amax == 0.0f) {
+    e = -127;
+  } else {
+    int E;
+    const float f = std::frexp(amax, &E);
+    e = f <= 0.75f ? E - 3 : E - 2;
+    e = std::min(127, std::max(-127, e));
+  }
+  *scale_byte = (uint8_t)(e + 127);
+  const double inv = std::ldexp(1.0, -e);
+  for (int i = 0; i < 32; ++i) {
+    const double a = std::fabs((double)x[i]) * inv;
+    const int c = (a > 0.25) + (a >= 0.75) + (a > 1.25) + (a >= 1.75) + (a > 2.5) + (a >= 3.5) + (a > 5.0);
+    nib[i] = (uint8_t)(c | (std::signbit(x[i]) ? 8 : 0));
+  }
+}
+
+static bool all_finite(const float* p, size_t n) {
+  for (size_t i = 0; i < n; ++i)
+    if (!std::isfinite(p[i])) return false;
+  return true;
+}
+
+}  // namespace svdq
+
+using namespace svdq;
+
+// ============================================================== C ABI
+
+extern "C" {
+
+const char* svdq_status_str(svdq_status s) {
+  switch (s) {
+    case SVDQ_OK: return "ok";
+    case SVDQ_ERR_ARG: return "invalid argument";
+    case SVDQ_ERR_SHAPE: return "unsupported shape";
+    case SVDQ_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case SVDQ_ERR_UNSUPPORTED: return "unsupported format or device";
+    case SVDQ_ERR_WORKSPACE: return "workspace too small";
+    case SVDQ_ERR_NUMERIC: return "non-finite input or solver failure";
+    case SVDQ_ERR_DEVICE: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t svdq_abi_version(void) { return SVDQ_ABI_VERSION; }
+
+svdq_status svdq_layer_sizes(int32_t K, int32_t N, int32_t rank, int32_t fmt, svdq_sizes* out) {
+  if (!out) return SVDQ_ERR_ARG;
+  if (!valid_fmt(fmt)) return SVDQ_ERR_UNSUPPORTED;
+  Geometry g;
+  if (!geometry(K, N, rank, fmt, &g)) return SVDQ_ERR_SHAPE;
+  out->wq_bytes = g.wq_bytes;
+  out->ws_bytes = g.ws_bytes;
+  out->l1k_bytes = g.l1k_bytes;
+  out->l2k_bytes = g.l2k_bytes;
+  out->wq_canon_bytes = (size_t)N * K / 2;
+  out->ws_canon_bytes = fmt == SVDQ_INT4_G64 ? (size_t)N * (K / 64) * 2 : (size_t)N * (K / 32);
+  return SVDQ_OK;
+}
+
+svdq_status svdq_workspace_layout(int32_t M, int32_t K, int32_t rank, int32_t fmt, svdq_ws_layout* out) {
+  if (!out) return SVDQ_ERR_ARG;
+  if (!valid_fmt(fmt)) return SVDQ_ERR_UNSUPPORTED;
+  if (M < 1 || M > (1 << 20) || !valid_kn(K, 16) || !valid_rank(rank)) return SVDQ_ERR_SHAPE;
+  const int32_t steps = K / kStep, ks4 = (steps + 3) / 4;
+  out->zsplit = rank > 0 ? choose_zsplit(M, K) : 0;
+  out->xq_off = 0;
+  out->xq_bytes = (size_t)M * K / 2;
+  out->xs_off = align256(out->xq_bytes);
+  out->xs_bytes = fmt == SVDQ_INT4_G64 ? (size_t)M * (K / 64) * 2 : (size_t)M * ks4 * 16;
+  out->z_off = align256(out->xs_off + out->xs_bytes);
+  out->z_bytes = rank > 0 ? (size_t)out->zsplit * M * rank_pad(rank) * 4 : 0;
+  out->total = align256(out->z_off + out->z_bytes);
+  return SVDQ_OK;
+}
+
+size_t svdq_workspace_bytes(int32_t M, int32_t K, int32_t rank, int32_t fmt) {
+  svdq_ws_layout l;
+  return svdq_workspace_layout(M, K, rank, fmt, &l) == SVDQ_OK ? l.total : 0;
+}
+
+svdq_status svdq_calib_absmax(const uint16_t* x, int64_t rows, int32_t K, float* amax) {
+  if (!x || !amax || rows < 0 || K <= 0) return SVDQ_ERR_ARG;
+  for (int64_t i = 0; i < rows; ++i) {
+    const uint16_t* row = x + i * K;
+    for (int32_t k = 0; k < K; ++k) {
+      const uint16_t h = row[k];
+      if ((h & 0x7F80) == 0x7F80) return SVDQ_ERR_NUMERIC;
+      const float a = (float)std::fabs(double_from_bf16(h));
+      if (a > amax[k]) amax[k] = a;
+    }
+  }
+  return SVDQ_OK;
+}
+
+svdq_status svdq_pack_host(const float* x, int32_t rows, int32_t K, int32_t fmt, uint8_t* codes, uint8_t* scales) {
+  if (!x || !codes || !scales || rows < 0) return SVDQ_ERR_ARG;
+  if (!valid_fmt(fmt)) return SVDQ_ERR_UNSUPPORTED;
+  const int G = group_size(fmt);
+  if (K <= 0 || K % G != 0) return SVDQ_ERR_SHAPE;
+  parallel_for(rows, default_threads(0), [&](int64_t lo, int64_t hi) {
+    uint8_t nib[64];
+    for (int64_t r = lo; r < hi; ++r) {
+      for (int32_t g = 0; g < K / G; ++g) {
+        const float* src = x + (size_t)r * K + (size_t)g * G;
+        if (fmt == SVDQ_INT4_G64) {
+          uint16_t sb;
+          quant_int4_group(src, nib, &sb);
+          std::memcpy(scales + ((size_t)r * (K / 64) + g) * 2, &sb, 2);
+        } else {
+          quant_mxfp4_group(src, nib, scales + (size_t)r * (K / 32) + g);
+        }
+        uint8_t* dst = codes + (size_t)r * (K / 2) + (size_t)g * (G / 2);
+        for (int i = 0; i < G / 2; ++i) dst[i] = (uint8_t)(nib[2 * i] | (nib[2 * i + 1] << 4));
+      }
+    }
+  });
+  return SVDQ_OK;
+}
+
+svdq_status svdq_attach_lora(const float* lambda, const uint16_t* l1, const uint16_t* l2, int32_t K, int32_t N,
+                             int32_t rank, const float* A, const float* B, int32_t k, float strength,
+                             uint16_t* l1_out, uint16_t* l2_out) {
+  if (!lambda || !A || !B || !l1_out || !l2_out || (rank > 0 && (!l1 || !l2))) return SVDQ_ERR_ARG;
+  if (!valid_kn(K, N) || !valid_rank(rank) || k < 0 || k % 16 || rank + k > SVDQ_MAX_RANK) return SVDQ_ERR_SHAPE;
+  const int32_t rt = rank + k;
+  for (int32_t i = 0; i < K; ++i) {
+    for (int32_t j = 0; j < rank; ++j) l1_out[(size_t)i * rt + j] = l1[(size_t)i * rank + j];
+    for (int32_t j = 0; j < k; ++j)
+      l1_out[(size_t)i * rt + rank + j] = bf16_from_double((double)lambda[i] * (double)A[(size_t)i * k + j]);
+  }
+  for (int32_t j = 0; j < rank; ++j)
+    std::memcpy(l2_out + (size_t)j * N, l2 + (size_t)j * N, sizeof(uint16_t) * N);
+  for (int32_t j = 0; j < k; ++j)
+    for (int32_t n = 0; n < N; ++n)
+      l2_out[(size_t)(rank + j) * N + n] = bf16_from_double((double)strength * (double)B[(size_t)j * N + n]);
+  return SVDQ_OK;
+}
+
+svdq_status svdq_prepare(const float* W, const float* act_amax, int32_t K, int32_t N, double alpha, int32_t rank,
+                         int32_t fmt, const svdq_prepare_opts* opts, svdq_prepared* out) {
+  if (!W || !act_amax || !out || !out->smooth_inv || !out->wq || !out->ws) return SVDQ_ERR_ARG;
+  if (!valid_fmt(fmt)) return SVDQ_ERR_UNSUPPORTED;
+  if (!valid_kn(K, N) || !valid_rank(rank) || rank > std::min(K, N)) return SVDQ_ERR_SHAPE;
+  if (!(alpha >= 0.0 && alpha <= 1.0)) return SVDQ_ERR_ARG;
+  const int32_t lk = opts ? opts->lora_rank : 0;
+  if (lk < 0 || lk % 16 || rank + lk > SVDQ_MAX_RANK) return SVDQ_ERR_SHAPE;
+  if (lk > 0 && (!opts->lora_a || !opts->lora_b)) return SVDQ_ERR_ARG;
+  if (rank + lk > 0 && (!out->l1 || !out->l2)) return SVDQ_ERR_ARG;
+  if (rank > 0 && std::min(K, N) > 16384) return SVDQ_ERR_SHAPE;
+  const int threads = default_threads(opts ? opts->threads : 0);
+  const int max_iters = opts ? opts->max_iters : 0;
+  if (!all_finite(W, (size_t)K * N) || !all_finite(act_amax, K)) return SVDQ_ERR_NUMERIC;
+  for (int32_t i = 0; i < K; ++i)
+    if (act_amax[i] < 0.0f) return SVDQ_ERR_ARG;
+  if (lk > 0 && (!all_finite(opts->lora_a, (size_t)K * lk) || !all_finite(opts->lora_b, (size_t)lk * N) ||
+                 !std::isfinite(opts->lora_strength)))
+    return SVDQ_ERR_NUMERIC;
+
+  // lambda (Eq. (4)); a zero statistic leaves the channel unscaled
+  std::vector<float> lam(K), inv(K);
+  for (int32_t i = 0; i < K; ++i) {
+    float aw = 0.0f;
+    const float* row = W + (size_t)i * N;
+    for (int32_t j = 0; j < N; ++j) aw = std::max(aw, std::fabs(row[j]));
+    const double ax = act_amax[i];
+    double l = 1.0;
+    if (ax > 0.0 && aw > 0.0f) l = std::pow(ax, alpha) / std::pow((double)aw, 1.0 - alpha);
+    lam[i] = (float)l;
+    if (!std::isfinite(lam[i]) || lam[i] == 0.0f) return SVDQ_ERR_NUMERIC;
+    inv[i] = 1.0f / lam[i];
+  }
+  // W~ = diag(lambda) W (exact in fp64)
+  std::vector<double> wt((size_t)K * N);
+  parallel_for(K, threads, [&](int64_t lo, int64_t hi) {
+    for (int64_t i = lo; i < hi; ++i)
+      for (int32_t j = 0; j < N; ++j) wt[(size_t)i * N + j] = (double)lam[i] * (double)W[(size_t)i * N + j];
+  });
+  // top-r split and bf16 factors
+  std::vector<double> L1, L2, sig;
+  if (!truncated_svd(wt.data(), K, N, rank, threads, max_iters, L1, L2, sig)) return SVDQ_ERR_NUMERIC;
+  std::vector<uint16_t> l1b((size_t)K * rank), l2b((size_t)rank * N);
+  std::vector<double> l1d((size_t)K * rank), l2d((size_t)rank * N);
+  for (size_t i = 0; i < l1b.size(); ++i) { l1b[i] = bf16_from_double(L1[i]); l1d[i] = double_from_bf16(l1b[i]); }
+  for (size_t i = 0; i < l2b.size(); ++i) { l2b[i] = bf16_from_double(L2[i]); l2d[i] = double_from_bf16(l2b[i]); }
+  // R = W~ - L1b L2b in fp64, stored fp32; R^T feeds the packer
+  std::vector<float> rt((size_t)N * K);
+  parallel_for(K, threads, [&](int64_t lo, int64_t hi) {
+    std::vector<double> acc(N);
+    for (int64_t i = lo; i < hi; ++i) {
+      for (int32_t j = 0; j < N; ++j) acc[j] = 0.0;
+      for (int32_t p = 0; p < rank; ++p) {
+        const double a = l1d[(size_t)i * rank + p];
+        const double* b = &l2d[(size_t)p * N];
+        for (int32_t j = 0; j < N; ++j) acc[j] += a * b[j];
+      }
+      for (int32_t j = 0; j < N; ++j) {
+        const float r = (float)(wt[(size_t)i * N + j] - acc[j]);
+        rt[(size_t)j * K + i] = r;
+        if (out->residual) out->residual[(size_t)i * N + j] = r;
+      }
+    }
+  });
+  svdq_status st = svdq_pack_host(rt.data(), N, K, fmt, out->wq, out->ws);
+  if (st != SVDQ_OK) return st;
+  for (int32_t i = 0; i < K; ++i) {
+    out->smooth_inv[i] = inv[i];
+    if (out->lambda) out->lambda[i] = lam[i];
+  }
+  if (out->sigma)
+    for (int32_t j = 0; j < rank; ++j) out->sigma[j] = sig[j];
+  if (rank + lk > 0) {
+    if (lk > 0) {
+      st = svdq_attach_lora(lam.data(), l1b.data(), l2b.data(), K, N, rank, opts->lora_a, opts->lora_b, lk,
+                            opts->lora_strength, out->l1, out->l2);
+      if (st != SVDQ_OK) return st;
+    } else {
+      std::memcpy(out->l1, l1b.data(), l1b.size() * 2);
+      std::memcpy(out->l2, l2b.data(), l2b.size() * 2);
+    }
+  }
+  return SVDQ_OK;
+}
+
+svdq_status svdq_kernel_layout(int32_t K, int32_t N, int32_t rank, int32_t fmt, const float* smooth_inv,
+                               const uint8_t* wq, const uint8_t* ws, const uint16_t* l1, const uint16_t* l2,
+                               uint8_t* wq_k, uint8_t* ws_k, uint16_t* l1k, uint16_t* l2k) {
+  if (!smooth_inv || !wq || !ws || !wq_k || !ws_k) return SVDQ_ERR_ARG;
+  if (!valid_fmt(fmt)) return SVDQ_ERR_UNSUPPORTED;
+  Geometry g;
+  if (!geometry(K, N, rank, fmt, &g)) return SVDQ_ERR_SHAPE;
+  if (rank > 0 && (!l1 || !l2 || !l1k || !l2k)) return SVDQ_ERR_ARG;
+  const int32_t steps = g.steps, rp = g.rpad;
+  // codes
+  if (fmt == SVDQ_MXFP4_G32) {
+    std::memcpy(wq_k, wq, g.wq_bytes);
+  } else {
+    parallel_for(N, default_threads(0), [&](int64_t lo, int64_t hi) {
+      for (int64_t n = lo; n < hi; ++n)
+        for (int32_t t = 0; t < steps; ++t) {
+          const uint8_t* src = wq + (size_t)n * (K / 2) + (size_t)t * 64;
+          uint8_t* dst = wq_k + (size_t)n * (K / 2) + (size_t)t * 64;
+          std::memset(dst, 0, 64);
+          for (int k = 0; k < kStep; ++k) {
+            const uint8_t v = (src[k >> 1] >> ((k & 1) * 4)) & 0xF;
+            const int j = (k & 63) & 15;
+            dst[int4_step_byte(k)] |= (uint8_t)(v << ((j & 1) * 4));
+          }
+        }
+    });
+  }
+  // scales
+  if (fmt == SVDQ_MXFP4_G32) {
+    for (int32_t n = 0; n < N; ++n) {
+      uint8_t* dst = ws_k + (size_t)n * g.ks4 * 16;
+      std::memset(dst, 127, (size_t)g.ks4 * 16);
+      for (int32_t b = 0; b < K / 32; ++b) dst[mx_scale_index(b)] = ws[(size_t)n * (K / 32) + b];
+    }
+  } else {
+    // [N/4][steps][4 rows][2 groups] fp16
+    const uint16_t* s = reinterpret_cast<const uint16_t*>(ws);
+    uint16_t* d = reinterpret_cast<uint16_t*>(ws_k);
+    for (int32_t n = 0; n < N; ++n)
+      for (int32_t t = 0; t < steps; ++t)
+        for (int G = 0; G < 2; ++G)
+          d[((size_t)(n / 4) * steps + t) * 8 + (n % 4) * 2 + G] = s[(size_t)n * (K / 64) + 2 * t + G];
+  }
+  if (rank == 0) return SVDQ_OK;
+  // down factor: hi/lo bf16 split of diag(smooth_inv) L1', order
+  // [step][hi/lo][s 0..3][n-tile][lane 0..63][i 0..7] with
+  // k = 128 step + 32 (lane / 16) + 8 s + i and n = 16 tile + lane % 16
+  const int32_t ntile = rp / 16;
+  parallel_for(steps, default_threads(0), [&](int64_t lo, int64_t hi) {
+    for (int64_t t = lo; t < hi; ++t)
+      for (int h = 0; h < 2; ++h)
+        for (int s = 0; s < 4; ++s)
+          for (int32_t nt = 0; nt < ntile; ++nt)
+            for (int lane = 0; lane < 64; ++lane)
+              for (int i = 0; i < 8; ++i) {
+                const int32_t k = (int32_t)t * kStep + 32 * (lane / 16) + 8 * s + i;
+                const int32_t n = 16 * nt + lane % 16;
+                uint16_t out = 0;
+                if (n < rank) {
+                  const double v = (double)smooth_inv[k] * double_from_bf16(l1[(size_t)k * rank + n]);
+                  const uint16_t hb = bf16_from_double(v);
+                  out = h == 0 ? hb : bf16_from_double(v - double_from_bf16(hb));
+                }
+                const size_t idx = ((((((size_t)t * 2 + h) * 4 + s) * ntile + nt) * 64 + lane) * 8) + i;
+                l1k[idx] = out;
+              }
+  });
+  // up factor: L2'^T padded to rpad columns
+  for (int32_t n = 0; n < N; ++n)
+    for (int32_t j = 0; j < rp; ++j) l2k[(size_t)n * rp + j] = j < rank ? l2[(size_t)j * N + n] : 0;
+  return SVDQ_OK;
+}
+
+svdq_status svdq_unpack_activations(const void* ws_host, int32_t M, int32_t K, int32_t rank, int32_t fmt,
+                                    uint8_t* xq, uint8_t* xs, float* z) {
+  if (!ws_host || !xq || !xs) return SVDQ_ERR_ARG;
+  svdq_ws_layout L;
+  svdq_status st = svdq_workspace_layout(M, K, rank, fmt, &L);
+  if (st != SVDQ_OK) return st;
+  const uint8_t* base = static_cast<const uint8_t*>(ws_host);
+  const uint8_t* q = base + L.xq_off;
+  const int32_t steps = K / kStep, ks4 = (steps + 3) / 4;
+  for (int32_t m = 0; m < M; ++m) {
+    for (int32_t t = 0; t < steps; ++t) {
+      const uint8_t* src = q + (size_t)m * (K / 2) + (size_t)t * 64;
+      uint8_t* dst = xq + (size_t)m * (K / 2) + (size_t)t * 64;
+      if (fmt == SVDQ_MXFP4_G32) {
+        std::memcpy(dst, src, 64);
+      } else {
+        std::memset(dst, 0, 64);
+        for (int k = 0; k < kStep; ++k) {
+          const int j = (k & 63) & 15;
+          const uint8_t v = (src[int4_step_byte(k)] >> ((j & 1) * 4)) & 0xF;
+          dst[k >> 1] |= (uint8_t)(v << ((k & 1) * 4));
+        }
+      }
+    }
+  }
+  const uint8_t* s = base + L.xs_off;
+  if (fmt == SVDQ_MXFP4_G32) {
+    for (int32_t m = 0; m < M; ++m)
+      for (int32_t b = 0; b < K / 32; ++b) xs[(size_t)m * (K / 32) + b] = s[(size_t)m * ks4 * 16 + mx_scale_index(b)];
+  } else {
+    std::memcpy(xs, s, (size_t)M * (K / 64) * 2);
+  }
+  if (z && rank > 0) {
+    const int32_t rp = rank_pad(rank);
+    const float* zp = reinterpret_cast<const float*>(base + L.z_off);
+    for (int32_t m = 0; m < M; ++m)
+      for (int32_t j = 0; j < rank; ++j) {
+        float acc = 0.0f;
+        for (int32_t p = 0; p < L.zsplit; ++p) acc += zp[((size_t)p * M + m) * rp + j];
+        z[(size_t)m * rank + j] = acc;
+      }
+  }
+  return SVDQ_OK;
+}
+
+}  // extern "C"

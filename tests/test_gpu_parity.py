@@ -1,0 +1,99 @@
+"""GPU parity of the device path (K-A + K-B through the C ABI) against the
+fp64 oracle: activation codes and scales bit-exact, the down projection Z to
+fp32 accumulation accuracy, Y within 5e-3 relative Frobenius error (the
+tolerance the method's target states)."""
+import numpy as np
+import pytest
+
+import rank_gemm_svdq_amd as B
+from rank_gemm_svdq_amd import synthetic as S
+from oracle import forward as F
+from oracle import prepare as P
+from oracle import quantizers as Q
+from tests.gpu_util import GpuRun, bf16_to_f64, oracle_layer, oracle_scales_bits, rel_fro
+
+pytestmark = pytest.mark.gpu
+Y_TOL = 5e-3
+
+
+def _check_full(run, po, x, bias, z_tol=2e-5):
+    of = F.forward(x, po, bias)
+    assert np.array_equal(run.prep["smooth_inv"], po["inv_lambda"])
+    xq, xs, z = run.activations()
+    assert np.array_equal(xq, of["xq"]), f"codes differ at {np.argwhere(xq != of['xq'])[:5]}"
+    assert np.array_equal(xs, oracle_scales_bits(of["xs"], run.fmt))
+    if run.rank:
+        # Z itself depends on the sign of each singular vector; Z L2' does not
+        zl2 = z.astype(np.float64) @ bf16_to_f64(run.prep["l2"])
+        assert rel_fro(zl2, of["z"] @ po["l2p"]) <= z_tol
+    err = rel_fro(run.y(), of["y"])
+    assert err <= Y_TOL, err
+    return err
+
+
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+@pytest.mark.parametrize("use_bias", [True, False])
+def test_tiny_layer(fmt, use_bias):
+    s = S.spec("tiny", fmt=fmt)
+    d = S.make_layer(s)
+    run = GpuRun(d, fmt, s.rank, s.alpha, use_bias=use_bias).forward()
+    po = oracle_layer(d, fmt, s.rank, s.alpha)
+    _check_full(run, po, d["X"], d["bias"] if use_bias else None)
+
+
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+@pytest.mark.parametrize("M,K,N,rank", [
+    (1, 512, 512, 16), (17, 512, 512, 16), (255, 512, 512, 16),   # ragged token counts
+    (300, 1024, 400, 32),                                          # several tiles, ragged N
+    (130, 128, 144, 0),                                            # one K step, plain W4A4
+    (64, 768, 272, 48),                                            # rank 48 (padded to 64)
+])
+def test_shapes_and_tails(fmt, M, K, N, rank):
+    s = S.spec("tiny", M=M, K=K, N=N, rank=rank, fmt=fmt)
+    d = S.make_layer(s)
+    run = GpuRun(d, fmt, rank, s.alpha).forward()
+    po = oracle_layer(d, fmt, rank, s.alpha)
+    _check_full(run, po, d["X"], d["bias"])
+
+
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+def test_lora_rank48(fmt):
+    s = S.spec("flux_lora", M=200, K=512, N=640, fmt=fmt)
+    d = S.make_layer(s)
+    lora = {"A": d["lora_A"], "B": d["lora_B"], "strength": 1.0}
+    run = GpuRun(d, fmt, s.rank, s.alpha, lora=lora).forward()
+    po = oracle_layer(d, fmt, s.rank, s.alpha, lora=lora)
+    _check_full(run, po, d["X"], d["bias"])
+
+
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+def test_quantizer_edge_values(fmt):
+    """Zero rows, bf16 subnormals (MXFP4 scale clamped at 2^-127), huge
+    values and exact ties go through K-A; codes and scales bit-exact."""
+    M, K, N = 48, 512, 64
+    x = S.random_bf16(5, (M, K), 2.0)
+    x[0] = 0.0
+    x[1, :64] = -0.0
+    x[2] = S.to_bf16_values(np.full(K, 3e-39))                   # bf16 subnormals
+    x[3, :] = S.to_bf16_values(np.linspace(-6, 6, K))
+    x[4, :32] = S.to_bf16_values(np.array([7.0, 2.5, -2.5, 0.5, -0.5, 1.5, 3.5, -6.5] * 4))
+    x[5] = S.to_bf16_values(S.random_bf16(6, (K,), 1.0) * 1e30)
+    x[6, :] = S.to_bf16_values(np.full(K, 1e-36))
+    d = {"spec": S.spec("tiny"), "X": x, "X_cal": np.abs(x) + 1.0,
+         "W": S.random_bf16(7, (K, N), 0.05), "bias": S.random_bf16(8, (N,), 0.1)}
+    run = GpuRun(d, fmt, 0, 0.5).forward()
+    po = oracle_layer(d, fmt, 0, 0.5)
+    of = F.forward(x, po, d["bias"])
+    xq, xs, _ = run.activations()
+    assert np.array_equal(xq, of["xq"])
+    assert np.array_equal(xs, oracle_scales_bits(of["xs"], fmt))
+
+
+def test_workspace_reuse_and_determinism():
+    s = S.spec("tiny", M=300, K=1024, N=400, rank=32, fmt="mxfp4")
+    d = S.make_layer(s)
+    run = GpuRun(d, "mxfp4", 32, s.alpha).forward()
+    y1 = run.Y.clone()
+    run.ws.fill_(0x5A)
+    run.forward()
+    assert bool((run.Y == y1).all())

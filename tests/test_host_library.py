@@ -1,0 +1,220 @@
+"""CPU tests of the C-ABI library's host half: symbol exports, argument
+checks, the RTN packers (bit-exact against the oracle), the offline prepare
+(against the oracle's own prepare), LoRA attach and the kernel layouts.
+No device compute is called here."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import rank_gemm_svdq_amd as B
+from rank_gemm_svdq_amd import synthetic as S
+from oracle import prepare as P
+from oracle import quantizers as Q
+from oracle.rounding import bf16_from_bits
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "svdq.h")).read()
+    names = set(re.findall(r"\b(svdq_[a-z_0-9]+)\s*\(", hdr))
+    assert len(names) >= 15
+    lib = B.lib()
+    for n in sorted(names):
+        assert hasattr(lib, n), n
+    assert B.abi_version() == 1
+    assert B.status_str(0) == "ok"
+
+
+def _oracle_scales(ws, fmt):
+    return np.float16(ws).view(np.uint16) if fmt == "int4" else ws
+
+
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+def test_packer_bit_exact_against_oracle(fmt):
+    rng = np.random.default_rng(3)
+    x = (rng.standard_t(3, (64, 1024)) * 0.7).astype(np.float32)
+    x[0, :64] = 0.0                                  # all-zero group
+    x[1, :64] = 0.0
+    x[1, 0] = 5e-7                                   # fp16-subnormal INT4 scale
+    x[2, :64] = np.array([7.0, 2.5, -2.5, 0.5, -0.5, 1.5, 3.5, -6.5] + [0.0] * 56, np.float32)  # exact ties
+    x[3, :32] = np.linspace(-6, 6, 32).astype(np.float32)                                     # E2M1 grid
+    x[4, :32] = -0.0
+    x[5, :32] = 1e-39                                # MXFP4 scale clamped at 2^-127
+    x[6] *= 1e4
+    codes, scales = B.pack_host(x, fmt)
+    q = Q.quantize(x, fmt)
+    assert np.array_equal(codes, q["packed"])
+    assert np.array_equal(scales, _oracle_scales(q["scales"], fmt))
+
+
+def test_calib_absmax_matches_and_rejects_nan():
+    x = S.random_bf16(1, (33, 256), 3.0)
+    got = B.calib_absmax(S.bf16_bits_of(x))
+    assert np.array_equal(got, P.calib_amax(x))
+    bits = S.bf16_bits_of(x).copy()
+    bits[3, 7] = 0x7FC0
+    with pytest.raises(B.SvdqError) as e:
+        B.calib_absmax(bits)
+    assert e.value.status == 6
+
+
+def _compare_prepare(W, amax, alpha, rank, fmt, lora=None):
+    pc = B.prepare(W, amax, alpha, rank, fmt, lora=lora, want_residual=True)
+    po = P.prepare(W, amax, alpha, rank, fmt, lora=lora)
+    assert np.array_equal(pc["lambda"], po["lam32"])
+    assert np.array_equal(pc["smooth_inv"], po["inv_lambda"])
+    l1, l2 = bf16_from_bits(pc["l1"]), bf16_from_bits(pc["l2"])
+    if rank:
+        ref = po["l1p"] @ po["l2p"]
+        assert np.linalg.norm(l1 @ l2 - ref) <= 1e-4 * np.linalg.norm(ref)
+        assert np.allclose(pc["sigma"], po["sigma"][:rank], rtol=1e-10, atol=0)
+    assert np.linalg.norm(pc["residual"] - po["r32"]) <= 1e-4 * np.linalg.norm(po["r32"])
+    # codes and scales: bit-exact except where the two SVDs land a residual
+    # element on the other side of a rounding boundary (never observed here)
+    mism = np.mean(pc["wq"] != po["wq_packed"])
+    assert mism <= 1e-5
+    assert np.mean(pc["ws"] != _oracle_scales(po["ws"], fmt)) <= 1e-5
+    return pc, po
+
+
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+def test_prepare_matches_oracle_tiny(fmt):
+    s = S.spec("tiny")
+    d = S.make_layer(s)
+    pc, po = _compare_prepare(d["W"], P.calib_amax(d["X_cal"]), s.alpha, s.rank, fmt)
+    assert np.array_equal(pc["wq"], po["wq_packed"])
+
+
+@pytest.mark.parametrize("name,shape,alpha", [
+    ("flux_qkv", {"K": 768, "N": 1152}, 0.5),
+    ("flux_mlp_down", {"K": 1536, "N": 384}, 0.3),     # K > N: Gram on the N side
+    ("flux_mlp_down", {"K": 1536, "N": 384}, 0.7),
+    ("flux_mlp_up", {"K": 768, "N": 1536}, 0.5),
+])
+def test_prepare_matches_oracle_medium(name, shape, alpha):
+    s = S.spec(name, **shape)
+    d = S.make_layer(s, with_x=False)
+    _compare_prepare(d["W"], P.calib_amax(d["X_cal"]), alpha, s.rank, s.fmt)
+
+
+def test_prepare_full_rank_and_rank_zero():
+    rng = np.random.default_rng(4)
+    W = S.to_bf16_values(rng.standard_normal((128, 64)))
+    amax = np.abs(rng.standard_normal(128)).astype(np.float32) + 0.1
+    pc = B.prepare(W, amax, 0.5, 64, "int4", want_residual=True)
+    wt = pc["lambda"][:, None].astype(np.float64) * W
+    # factors in bf16 leave a residual of bf16-rounding size only
+    assert np.linalg.norm(pc["residual"]) < 1e-2 * np.linalg.norm(wt)
+    p0 = B.prepare(W, amax, 0.5, 0, "int4", want_residual=True)
+    assert np.array_equal(p0["residual"], wt.astype(np.float32))
+
+
+def test_prepare_lora_matches_oracle():
+    s = S.spec("flux_lora", M=256, K=512, N=768)
+    d = S.make_layer(s, with_x=False)
+    lora = {"A": d["lora_A"], "B": d["lora_B"], "strength": 0.75}
+    pc, po = _compare_prepare(d["W"], P.calib_amax(d["X_cal"]), s.alpha, s.rank, s.fmt, lora=lora)
+    assert pc["l1"].shape == (512, 48) and pc["l2"].shape == (48, 768)
+    # the adapter columns are exactly bf16(D A) and bf16(s B)
+    assert np.array_equal(bf16_from_bits(pc["l1"])[:, 32:], po["l1p"][:, 32:])
+    assert np.array_equal(bf16_from_bits(pc["l2"])[32:], po["l2p"][32:])
+
+
+def test_error_codes_host():
+    lib = B.lib()
+    W = np.zeros((128, 64), np.float32)
+    amax = np.ones(128, np.float32)
+    # bad shapes / formats / alpha / numerics
+    with pytest.raises(B.SvdqError) as e:
+        B.prepare(np.zeros((100, 64), np.float32), np.ones(100, np.float32), 0.5, 16, "int4")
+    assert e.value.status == 2
+    with pytest.raises(B.SvdqError) as e:
+        B.prepare(W, amax, 1.5, 16, "int4")
+    assert e.value.status == 1
+    with pytest.raises(B.SvdqError) as e:
+        B.prepare(W, amax, 0.5, 24, "int4")
+    assert e.value.status == 2
+    Wn = W.copy()
+    Wn[3, 3] = np.nan
+    with pytest.raises(B.SvdqError) as e:
+        B.prepare(Wn, amax, 0.5, 16, "int4")
+    assert e.value.status == 6
+    Wr = np.random.default_rng(0).standard_normal((128, 64)).astype(np.float32)
+    with pytest.raises(B.SvdqError) as e:
+        B.prepare(Wr, amax, 0.5, 16, "int4", max_iters=-1)     # forced solver failure
+    assert e.value.status == 6
+    assert lib.svdq_layer_sizes(128, 64, 16, 7, C.byref(B.binding.Sizes())) == 4
+    assert lib.svdq_layer_sizes(128, 60, 16, 0, C.byref(B.binding.Sizes())) == 2
+    assert lib.svdq_layer_sizes(128, 64, 16, 0, None) == 1
+    assert B.workspace_bytes(0, 128, 16, 0) == 0
+    assert lib.svdq_prepare(None, None, 128, 64, 0.5, 16, 0, None, None) == 1
+
+
+def test_error_codes_device_entry_points_validate_before_hip():
+    """Invalid arguments are rejected on the host before any HIP call (the
+    device pointers below are never dereferenced)."""
+    lib = B.lib()
+    L = B.binding.Layer(256, 256, 32, 1, 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, None)
+    ws = B.workspace_bytes(64, 256, 32, 1)
+    assert lib.svdq_linear_forward(None, 0x1000, 64, 0x2000, 0x3000, ws, None) == 1
+    assert lib.svdq_linear_forward(C.byref(L), None, 64, 0x2000, 0x3000, ws, None) == 1
+    assert lib.svdq_linear_forward(C.byref(L), 0x1008, 64, 0x2000, 0x3000, ws, None) == 3
+    assert lib.svdq_linear_forward(C.byref(L), 0x1000, 64, 0x2000, 0x3000, ws - 1, None) == 5
+    assert lib.svdq_linear_forward(C.byref(L), 0x1000, 0, 0x2000, 0x3000, ws, None) == 2
+    bad = B.binding.Layer(256, 256, 40, 1, 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, None)
+    assert lib.svdq_quantize_lora_down(C.byref(bad), 0x1000, 64, 0x3000, ws, None) == 2
+    badf = B.binding.Layer(256, 256, 32, 3, 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, None)
+    assert lib.svdq_gemm_lora_up(C.byref(badf), 0x3000, ws, 64, 0x2000, None) == 4
+    mis = B.binding.Layer(256, 256, 32, 1, 0x1004, 0x2000, 0x3000, 0x4000, 0x5000, None)
+    assert lib.svdq_gemm_lora_up(C.byref(mis), 0x3000, ws, 64, 0x2000, None) == 3
+
+
+def test_workspace_layout_regions():
+    for M, K, r, f in [(1, 128, 0, 0), (4096, 3072, 32, 1), (8192, 3072, 48, 0), (17, 512, 16, 1)]:
+        w = B.workspace_layout(M, K, r, f)
+        assert w["xq_off"] % 256 == 0 and w["xs_off"] % 256 == 0 and w["z_off"] % 256 == 0
+        assert w["xq_bytes"] == M * K // 2
+        assert w["xs_off"] >= w["xq_off"] + w["xq_bytes"] and w["z_off"] >= w["xs_off"] + w["xs_bytes"]
+        assert w["total"] >= w["z_off"] + w["z_bytes"]
+        if r:
+            assert (K // 128) % w["zsplit"] == 0 and 1 <= w["zsplit"] <= 4
+            assert w["z_bytes"] == w["zsplit"] * M * ((r + 31) // 32 * 32) * 4
+
+
+def test_int4_kernel_layout_positions():
+    """Element k of a 128-element step sits at byte 16 g + 8 G + j/2 (nibble
+    j % 2) with G = k // 64, g = (k % 64) // 16, j = k % 16."""
+    K, N = 256, 16
+    rng = np.random.default_rng(0)
+    nib = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    prep = {"K": K, "N": N, "rank": 0, "fmt": 0, "smooth_inv": np.ones(K, np.float32),
+            "wq": Q.pack_nibbles(nib), "ws": np.ones((N, K // 64), np.float16).view(np.uint16)}
+    kl = B.kernel_layout(prep)
+    wk = kl["wq_k"].reshape(N, K // 2)
+    for n in range(N):
+        for k in range(K):
+            t, kk = divmod(k, 128)
+            G, g, j = kk // 64, (kk % 64) // 16, kk % 16
+            byte = wk[n, 64 * t + 16 * g + 8 * G + j // 2]
+            assert (byte >> (4 * (j % 2))) & 0xF == nib[n, k]
+    ws = kl["ws_k"].view(np.uint16).reshape(N // 4, K // 128, 4, 2)
+    assert np.all(ws == np.float16(1).view(np.uint16))
+
+
+def test_mxfp4_scale_layout_positions():
+    K, N = 1024, 16
+    rng = np.random.default_rng(1)
+    sc = rng.integers(100, 150, (N, K // 32)).astype(np.uint8)
+    prep = {"K": K, "N": N, "rank": 0, "fmt": 1, "smooth_inv": np.ones(K, np.float32),
+            "wq": np.zeros((N, K // 2), np.uint8), "ws": sc}
+    kl = B.kernel_layout(prep)
+    steps = K // 128
+    row = kl["ws_k"].reshape(N, -1)
+    assert row.shape[1] == (steps + 3) // 4 * 16
+    for b in range(K // 32):
+        t, g = divmod(b, 4)
+        assert np.array_equal(row[:, 16 * (t // 4) + 4 * g + t % 4], sc[:, b])
