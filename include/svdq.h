@@ -59,6 +59,8 @@ typedef enum svdq_format { SVDQ_INT4_G64 = 0, SVDQ_MXFP4_G32 = 1 } svdq_format;
  * Shape rules (checked by every entry point):
  *   K % 128 == 0, 128 <= K <= 65536; N % 16 == 0, 16 <= N <= 262144;
  *   1 <= M <= 1048576 (no alignment; the tail rows are masked);
+ *   M * K <= 2^32 and N * K <= 2^32 for the device path (4-bit code buffers
+ *   below 2 GiB);
  *   0 <= rank <= SVDQ_MAX_RANK and rank % 16 == 0 (rank 0 = plain W4A4).
  * ---------------------------------------------------------------------- */
 
@@ -95,7 +97,8 @@ svdq_status svdq_layer_sizes(int32_t K, int32_t N, int32_t rank, int32_t fmt, sv
  *        as for the weight codes)
  *   xs   activation scales (INT4: canonical [M, K/64] fp16 bits; MXFP4:
  *        E8M0 bytes in the permuted per-row layout of the weight scales)
- *   z    down-projection partial sums, fp32 [zsplit][M][rank rounded up to 32]
+ *   z    down projection Z, fp32 [zsplit][M][rank rounded up to 32]; zsplit
+ *        is 1 in this version (partial sums are reduced inside K-A)
  * svdq_unpack_activations() turns a host copy into canonical form. */
 typedef struct svdq_ws_layout {
   size_t xq_off, xq_bytes, xs_off, xs_bytes, z_off, z_bytes, total;

@@ -30,7 +30,7 @@
 //   Down factor: bf16 hi/lo split of diag(1/lambda) L1', ordered
 //     [step][hi/lo][s][n-tile][lane][8] with k = 128 step + 32 (lane/16) + 8 s + i.
 //   Up factor: L2'^T, [N][rpad] bf16, rpad = rank rounded up to 32.
-//   Z partial sums: fp32 [zsplit][M][rpad].
+//   Z (down projection): fp32 [M][rpad].
 
 #include <hip/hip_runtime.h>
 
@@ -59,36 +59,52 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 
 // ----------------------------------------------------------------- K-A
 
-// One wave handles 16 rows and the K range of one split; lane l owns row
-// l % 16 and the 32 consecutive elements 32 (l / 16) .. +32 of each step.
+constexpr int KA_WAVES = 8;
+
+// One block handles 16 rows; its 8 waves split the K steps evenly and the
+// down-projection partial sums are reduced in LDS, so Z leaves the kernel
+// once.  Lane l owns row l % 16 and the 32 consecutive elements
+// 32 (l / 16) .. +32 of each 128-element step; the next step's X is loaded
+// while the current one is processed.
 template <int FMT, int NT>
-__global__ __launch_bounds__(256) void ka_kernel(const uint16_t* __restrict__ X, int M, int K,
-                                                 const float* __restrict__ sinv,
-                                                 const v8bf* __restrict__ l1k,
-                                                 uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
-                                                 float* __restrict__ zp, int steps_per_split, int rpad) {
+__global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __restrict__ X, int M, int K,
+                                                          const float* __restrict__ sinv,
+                                                          const v8bf* __restrict__ l1k,
+                                                          uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
+                                                          float* __restrict__ zout, int rpad) {
+  constexpr int NTZ = NT > 0 ? NT : 1;
+  __shared__ float zred[NT > 0 ? KA_WAVES * 16 * NT * 16 : 1];
   const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int row0 = wave * 16;
-  if (row0 >= M) return;
+  const int wave = threadIdx.x >> 6;
+  const int row0 = blockIdx.x * 16;
   const int r = lane & 15, g = lane >> 4;
   const int row = row0 + r;
   const int rowc = row < M ? row : M - 1;
   const bool live = row < M;
   const int steps = K / 128;
   const int ks4 = (steps + 3) / 4;
-  const int split = blockIdx.y;
-  const int t0 = split * steps_per_split;
-  const uint16_t* xrow = X + (size_t)rowc * K;
-  v4f acc[NT > 0 ? NT : 1];
+  const int spw = (steps + KA_WAVES - 1) / KA_WAVES;
+  const int t0 = wave * spw;
+  const int t1 = min(steps, t0 + spw);
+  const uint16_t* xrow = X + (size_t)rowc * K + 32 * g;
+  v4f acc[NTZ];
 #pragma unroll
-  for (int nt = 0; nt < (NT > 0 ? NT : 1); ++nt) acc[nt] = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int nt = 0; nt < NTZ; ++nt) acc[nt] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  for (int t = t0; t < t0 + steps_per_split; ++t) {
-    const int k0 = t * 128 + 32 * g;
+  v4i nxt[4];
+  if (t0 < t1) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) nxt[c] = *reinterpret_cast<const v4i*>(xrow + (size_t)t0 * 128 + 8 * c);
+  }
+  for (int t = t0; t < t1; ++t) {
     v4i raw[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) raw[c] = *reinterpret_cast<const v4i*>(xrow + k0 + 8 * c);
+    for (int c = 0; c < 4; ++c) raw[c] = nxt[c];
+    if (t + 1 < t1) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) nxt[c] = *reinterpret_cast<const v4i*>(xrow + (size_t)(t + 1) * 128 + 8 * c);
+    }
+    const int k0 = t * 128 + 32 * g;
     float xh[32];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -190,14 +206,20 @@ __global__ __launch_bounds__(256) void ka_kernel(const uint16_t* __restrict__ X,
     }
   }
   if constexpr (NT > 0) {
-    // result rows 4 g + i of the wave's 16, column 16 nt + r
+    // partial sums of wave w: rows 4 g + i, columns 16 nt + r
+    constexpr int W = NT * 16;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = row0 + 4 * g + i;
-        if (m < M) zp[((size_t)split * M + m) * rpad + 16 * nt + r] = acc[nt][i];
-      }
+      for (int i = 0; i < 4; ++i) zred[(wave * 16 + 4 * g + i) * W + 16 * nt + r] = acc[nt][i];
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 16 * W; idx += 64 * KA_WAVES) {
+      const int rr = idx / W, cc = idx % W;
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < KA_WAVES; ++w) sum += zred[(w * 16 + rr) * W + cc];
+      if (row0 + rr < M) zout[(size_t)(row0 + rr) * rpad + cc] = sum;
+    }
   }
 }
 
@@ -206,8 +228,12 @@ __global__ __launch_bounds__(256) void ka_kernel(const uint16_t* __restrict__ X,
 constexpr int BM = 128, BN = 128;          // tile: tokens x out-features
 constexpr int LDS_TILE = (BM + BN) * 64;   // one step of both operands, bytes
 
-// swizzled byte offset of 16-byte chunk c of row r inside a [rows][64 B] tile
-__device__ __forceinline__ int swz(int r, int c) { return r * 64 + 16 * (c ^ ((r >> 2) & 3)); }
+// swizzled byte offset of 16-byte chunk c of row r inside a [rows][64 B] tile.
+// A fragment read has 16 consecutive rows at one chunk; with f(r) =
+// ((r >> 1) ^ (r >> 3)) & 3 any 8 consecutive rows hit 8 distinct 16-byte
+// slots of a 128-byte bank line and any 16 rows 16 slots of 256 bytes.
+__device__ __forceinline__ int swz_f(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int swz(int r, int c) { return r * 64 + 16 * (c ^ swz_f(r)); }
 
 template <int FMT, int NTR>
 __global__ __launch_bounds__(256) void kb_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
@@ -415,36 +441,316 @@ __global__ __launch_bounds__(256) void kb_kernel(const uint8_t* __restrict__ xq,
   }
 }
 
+// ----------------------------------------------------- K-B, MXFP4, large tile
+//
+// 256 (tokens) x 256 (out-features) per block of 4 waves, one wave per SIMD;
+// wave w owns tokens 128 (w & 1) .. +128 and out-features 128 (w >> 1) ..
+// +128, i.e. 8 x 8 MFMA tiles of 16 x 16 (256 fp32 accumulators per lane).
+// Codes travel global -> LDS by direct-to-LDS loads (no register staging)
+// into a ring of three 32 KB step buffers, three steps ahead of the MFMAs;
+// scale dwords (one per row and 4 steps) travel the same way into a double
+// buffer.  The fragments of step t + 1 are read from LDS while the 64 scaled
+// FP4 MFMAs of step t run (register double buffering), so after the first
+// step the MFMA pipe does not wait on LDS.
+
+constexpr int MX_BM = 256, MX_BN = 256, MX_THREADS = 256;
+constexpr int MX_STEP_BYTES = (MX_BM + MX_BN) * 64;   // codes of one step, both operands
+constexpr int MX_NBUF = 3;
+constexpr int MX_SC_BYTES = (MX_BM + MX_BN) * 16;     // scale dwords of one 4-step group
+constexpr int MX_LDS = MX_NBUF * MX_STEP_BYTES + 2 * MX_SC_BYTES;
+
+#define SVDQ_AS3 __attribute__((address_space(3)))
+
+// One wave-wide 1 KB direct-to-LDS copy: lane i's 16 bytes at sbase + voff
+// (sbase wave-uniform, voff per lane) land at LDS byte lds_base + 16 i.  Issued from asm so that the compiler does not
+// serialise it against unrelated LDS reads; completion is tracked with
+// explicit vmcnt waits.  M0 is restored before the asm block ends.
+__device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_base), "v"(voff), "s"(sbase)
+      : "memory");
+}
+
+// Blocks are dealt to the 8 XCDs round robin; give each XCD a contiguous run
+// of tile ids, and walk tile ids token-tile fastest so the blocks resident on
+// one XCD share out-feature columns of the weight in its L2.
+__device__ __forceinline__ void mx_tile_of(int b, int tiles_m, int tiles_n, int* tm, int* tn) {
+  const int total = tiles_m * tiles_n;
+  const int per = total / 8;
+  int id = b;
+  if (per * 8 == total) id = (b & 7) * per + (b >> 3);
+  *tm = id % tiles_m;
+  *tn = id / tiles_m;
+}
+
+struct MxFrag {
+  v4i a[8];            // weight rows (out-features) of the wave, one per 16-row tile
+  v4i b[8];            // token rows
+};
+
+template <int NTR>
+__global__ __launch_bounds__(MX_THREADS, 1) void kb_mx_kernel(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const float* __restrict__ zp, int zsplit,
+    const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws, const uint16_t* __restrict__ l2k,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int M, int N, int K, int rpad) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[MX_LDS];
+  const uint32_t lds_u32 = (uint32_t)(size_t)(SVDQ_AS3 uint8_t*)lds;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int tiles_m = (M + MX_BM - 1) / MX_BM, tiles_n = (N + MX_BN - 1) / MX_BN;
+  int tm, tn;
+  mx_tile_of(blockIdx.x, tiles_m, tiles_n, &tm, &tn);
+  const int tile_m = tm * MX_BM, tile_n = tn * MX_BN;
+  const int steps = K / 128;
+  const int ks4 = (steps + 3) / 4;
+  const size_t rowbytes = (size_t)K / 2;
+  const int m_base = tile_m + 128 * wm, n_base = tile_n + 128 * wn;
+
+  // ---- DMA plan.  Codes: wave w moves the 1 KB units 8w .. 8w+7 of a step
+  // buffer (units 0-15: 16 token rows each, units 16-31: 16 out-feature rows
+  // each); lane i fills 16-byte slot p = 64 (u mod 16) + i of its operand
+  // tile, i.e. row p / 4 at swizzled chunk position p mod 4.
+  // Waves 0-1 move token rows, waves 2-3 weight rows; offsets are 32-bit
+  // (operands are below 2 GiB, checked on the host).
+  const uint8_t* cbase = wave < 2 ? xq : wq;
+  uint32_t coff[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int u = 8 * wave + j;
+    const int p = 64 * (u & 15) + lane, r = p >> 2, c = (p & 3) ^ swz_f(r);
+    const int row = wave < 2 ? min(tile_m + r, M - 1) : min(tile_n + r, N - 1);
+    coff[j] = (uint32_t)row * (uint32_t)rowbytes + 16u * c;
+  }
+  // Scales: units 0-3 hold token rows 64 u + lane, units 4-7 out-feature
+  // rows 64 (u - 4) + lane; 16 bytes (4 dwords, one per lane group) per row.
+  // Wave w moves units 2w and 2w + 1.
+  const uint8_t* sbase = wave < 2 ? xs : ws;
+  uint32_t soff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int u = 2 * wave + j;
+    const int row = u < 4 ? min(tile_m + 64 * u + lane, M - 1) : min(tile_n + 64 * (u - 4) + lane, N - 1);
+    soff[j] = (uint32_t)row * (uint32_t)(ks4 * 16);
+  }
+  const uint32_t scale_lds = lds_u32 + MX_NBUF * MX_STEP_BYTES;
+  auto issue_codes = [&](int t) {
+    const uint32_t b = lds_u32 + (uint32_t)(t % MX_NBUF) * MX_STEP_BYTES + (uint32_t)wave * 8192u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dma16(cbase + (size_t)t * 64, coff[j], b + 1024u * j);
+  };
+  auto issue_scales = [&](int grp) {
+    const uint32_t b = scale_lds + (uint32_t)(grp & 1) * MX_SC_BYTES + (uint32_t)wave * 2048u;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma16(sbase + (size_t)grp * 16, soff[j], b + 1024u * j);
+  };
+  // Fragment q of a wave reads row R + 16 q (R = 128 wm + l16, or
+  // 128 wn + l16 in the weight half) at chunk g; swz_f of that row only
+  // depends on the parity of q, so two lane addresses per operand and
+  // immediate offsets of 1 KB per q cover all 16 reads of a step.
+  uint32_t fb_off[2], fa_off[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    fb_off[par] = (uint32_t)swz(128 * wm + 16 * par + l16, g) - 1024u * par;
+    fa_off[par] = (uint32_t)(MX_BM * 64 + swz(128 * wn + 16 * par + l16, g)) - 1024u * par;
+  }
+  auto read_frags = [&](int t, MxFrag& f) {
+    const uint32_t buf = (uint32_t)(t % MX_NBUF) * MX_STEP_BYTES;
+    const uint8_t* pb0 = lds + buf + fb_off[0];
+    const uint8_t* pb1 = lds + buf + fb_off[1];
+    const uint8_t* pa0 = lds + buf + fa_off[0];
+    const uint8_t* pa1 = lds + buf + fa_off[1];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      f.b[q] = *reinterpret_cast<const v4i*>(((q & 1) ? pb1 : pb0) + 1024 * q);
+      f.a[q] = *reinterpret_cast<const v4i*>(((q & 1) ? pa1 : pa0) + 1024 * q);
+    }
+  };
+  auto read_scales = [&](int grp, uint32_t* asc, uint32_t* bsc) {
+    const uint32_t* sc = reinterpret_cast<const uint32_t*>(lds + MX_NBUF * MX_STEP_BYTES + (grp & 1) * MX_SC_BYTES);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      bsc[q] = sc[(128 * wm + 16 * q + l16) * 4 + g];
+      asc[q] = sc[(MX_BM + 128 * wn + 16 * q + l16) * 4 + g];
+    }
+  };
+
+  issue_scales(0);
+  issue_codes(0);
+  if (steps > 1) issue_codes(1);
+  if (steps > 2) issue_codes(2);
+
+  // ---- bias and the low-rank up projection initialise the accumulators
+  // (overlapping the first code loads)
+  v4f acc[8][8];   // [n-tile][m-tile]
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) {
+    const int n0 = n_base + 16 * nt + 4 * g;
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (bias != nullptr) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = n0 + i < N ? n0 + i : N - 1;
+        bv[i] = __uint_as_float((uint32_t)bias[n] << 16);
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) acc[nt][mt] = (v4f){bv[0], bv[1], bv[2], bv[3]};
+  }
+  if constexpr (NTR > 0) {
+    for (int u = 0; u < NTR; ++u) {
+      v8bf bh[8], bl[8];
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        int m = m_base + 16 * mt + l16;
+        m = m < M ? m : M - 1;
+        float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int p = 0; p < zsplit; ++p) {
+          const float* src = zp + ((size_t)p * M + m) * rpad + 32 * u + 8 * g;
+          const v4f z0 = *reinterpret_cast<const v4f*>(src), z1 = *reinterpret_cast<const v4f*>(src + 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) { z[i] += z0[i]; z[4 + i] += z1[i]; }
+        }
+        uint16_t hi[8], lo[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t hb = bf16_rne(z[i]);
+          hi[i] = (uint16_t)hb;
+          lo[i] = (uint16_t)bf16_rne(z[i] - __uint_as_float(hb << 16));
+        }
+        bh[mt] = __builtin_bit_cast(v8bf, *reinterpret_cast<v4i*>(hi));
+        bl[mt] = __builtin_bit_cast(v8bf, *reinterpret_cast<v4i*>(lo));
+      }
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        int n = n_base + 16 * nt + l16;
+        n = n < N ? n : N - 1;
+        const v8bf af = *reinterpret_cast<const v8bf*>(l2k + (size_t)n * rpad + 32 * u + 8 * g);
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+          acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bh[mt], acc[nt][mt], 0, 0, 0);
+          acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bl[mt], acc[nt][mt], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- main loop
+  auto mfma_step = [&](const MxFrag& f, const uint32_t* asc, const uint32_t* bsc, int t) {
+    const int sh = 8 * (t & 3);
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      const v8i a = (v8i){f.a[nt][0], f.a[nt][1], f.a[nt][2], f.a[nt][3], 0, 0, 0, 0};
+      const int as = (int)(asc[nt] >> sh);
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        const v8i b = (v8i){f.b[mt][0], f.b[mt][1], f.b[mt][2], f.b[mt][3], 0, 0, 0, 0};
+        acc[nt][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[nt][mt], 4, 4, 0, as, 0,
+                                                                      (int)(bsc[mt] >> sh));
+      }
+    }
+  };
+  // waits: before reading step s's buffer, every DMA issued before s's own
+  // must be done; the only younger ones are those of step s + 1 (8 per wave)
+  auto wait_for = [&](int s) {
+    if (s + 1 < steps)
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  MxFrag f0, f1;
+  uint32_t asc[8], bsc[8];
+  wait_for(0);
+  read_frags(0, f0);
+  // iteration t: buffer (t+1) becomes readable, step t+3 is fetched into the
+  // buffer step t used (all waves are past their reads of it), the fragments
+  // of t+1 are read while the MFMAs of t run.
+  auto iter = [&](int t, MxFrag& cur, MxFrag& nxt) {
+    if (t + 1 < steps) wait_for(t + 1);
+    if ((t & 3) == 0 && (t >> 2) + 1 < ks4) issue_scales((t >> 2) + 1);
+    if (t + 3 < steps) issue_codes(t + 3);
+    if (t + 1 < steps) read_frags(t + 1, nxt);
+    if ((t & 3) == 0) read_scales(t >> 2, asc, bsc);
+    mfma_step(cur, asc, bsc, t);
+  };
+  int t = 0;
+  for (; t + 1 < steps; t += 2) {
+    iter(t, f0, f1);
+    iter(t + 1, f1, f0);
+  }
+  if (t < steps) iter(t, f0, f1);
+
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+    const int m = m_base + 16 * mt + l16;
+    if (m >= M) continue;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      const int n0 = n_base + 16 * nt + 4 * g;
+      if (n0 >= N) continue;
+      const uint32_t lo = bf16_rne(acc[nt][mt][0]) | (bf16_rne(acc[nt][mt][1]) << 16);
+      const uint32_t hi = bf16_rne(acc[nt][mt][2]) | (bf16_rne(acc[nt][mt][3]) << 16);
+      *reinterpret_cast<uint2*>(Y + (size_t)m * N + n0) = make_uint2(lo, hi);
+    }
+  }
+}
+
 // ------------------------------------------------------------ dispatch
 
 template <int FMT>
 static hipError_t launch_ka(const svdq_layer& L, const uint16_t* X, int M, uint8_t* ws, const svdq_ws_layout& W,
                             hipStream_t st) {
   const int rp = rank_pad(L.rank);
-  const int steps = L.K / 128;
-  const int zs = L.rank > 0 ? W.zsplit : 1;
-  const int waves = (M + 15) / 16;
-  dim3 grid((waves + 3) / 4, zs), block(256);
+  dim3 grid((M + 15) / 16), block(64 * KA_WAVES);
   uint8_t* xq = ws + W.xq_off;
   uint8_t* xs = ws + W.xs_off;
-  float* zp = reinterpret_cast<float*>(ws + W.z_off);
+  float* z = reinterpret_cast<float*>(ws + W.z_off);
   const v8bf* l1 = reinterpret_cast<const v8bf*>(L.l1k);
-  const int sps = steps / zs;
   switch (rp / 16) {
-    case 0: hipLaunchKernelGGL((ka_kernel<FMT, 0>), grid, block, 0, st, X, M, L.K, L.smooth_inv, l1, xq, xs, zp, sps, rp); break;
-    case 2: hipLaunchKernelGGL((ka_kernel<FMT, 2>), grid, block, 0, st, X, M, L.K, L.smooth_inv, l1, xq, xs, zp, sps, rp); break;
-    case 4: hipLaunchKernelGGL((ka_kernel<FMT, 4>), grid, block, 0, st, X, M, L.K, L.smooth_inv, l1, xq, xs, zp, sps, rp); break;
-    case 6: hipLaunchKernelGGL((ka_kernel<FMT, 6>), grid, block, 0, st, X, M, L.K, L.smooth_inv, l1, xq, xs, zp, sps, rp); break;
-    case 8: hipLaunchKernelGGL((ka_kernel<FMT, 8>), grid, block, 0, st, X, M, L.K, L.smooth_inv, l1, xq, xs, zp, sps, rp); break;
+    case 0: hipLaunchKernelGGL((ka_kernel<FMT, 0>), grid, block, 0, st, X, M, L.K, L.smooth_inv, l1, xq, xs, z, rp); break;
+    case 2: hipLaunchKernelGGL((ka_kernel<FMT, 2>), grid, block, 0, st, X, M, L.K, L.smooth_inv, l1, xq, xs, z, rp); break;
+    case 4: hipLaunchKernelGGL((ka_kernel<FMT, 4>), grid, block, 0, st, X, M, L.K, L.smooth_inv, l1, xq, xs, z, rp); break;
+    case 6: hipLaunchKernelGGL((ka_kernel<FMT, 6>), grid, block, 0, st, X, M, L.K, L.smooth_inv, l1, xq, xs, z, rp); break;
+    case 8: hipLaunchKernelGGL((ka_kernel<FMT, 8>), grid, block, 0, st, X, M, L.K, L.smooth_inv, l1, xq, xs, z, rp); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int NTR>
+static void launch_kb_mx(const svdq_layer& L, const uint8_t* ws, const svdq_ws_layout& W, int M, uint16_t* Y,
+                         hipStream_t st) {
+  const int rp = rank_pad(L.rank);
+  const int tiles = ((M + MX_BM - 1) / MX_BM) * ((L.N + MX_BN - 1) / MX_BN);
+  hipLaunchKernelGGL((kb_mx_kernel<NTR>), dim3(tiles), dim3(MX_THREADS), 0, st, ws + W.xq_off, ws + W.xs_off,
+                     reinterpret_cast<const float*>(ws + W.z_off), W.zsplit, L.wq, L.ws, L.l2k, L.bias, Y, M, L.N,
+                     L.K, rp);
 }
 
 template <int FMT>
 static hipError_t launch_kb(const svdq_layer& L, const uint8_t* ws, const svdq_ws_layout& W, int M, uint16_t* Y,
                             hipStream_t st) {
   const int rp = rank_pad(L.rank);
+  if constexpr (FMT == SVDQ_MXFP4_G32) {
+    switch (rp / 32) {
+      case 0: launch_kb_mx<0>(L, ws, W, M, Y, st); break;
+      case 1: launch_kb_mx<1>(L, ws, W, M, Y, st); break;
+      case 2: launch_kb_mx<2>(L, ws, W, M, Y, st); break;
+      case 3: launch_kb_mx<3>(L, ws, W, M, Y, st); break;
+      case 4: launch_kb_mx<4>(L, ws, W, M, Y, st); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   dim3 grid((L.N + BN - 1) / BN, (M + BM - 1) / BM), block(256);
   const uint8_t* xq = ws + W.xq_off;
   const uint8_t* xs = ws + W.xs_off;
@@ -466,6 +772,8 @@ static svdq_status check_layer(const svdq_layer* L, int32_t M) {
   if (!L) return SVDQ_ERR_ARG;
   if (!valid_fmt(L->fmt)) return SVDQ_ERR_UNSUPPORTED;
   if (!valid_kn(L->K, L->N) || !valid_rank(L->rank) || M < 1 || M > (1 << 20)) return SVDQ_ERR_SHAPE;
+  // code buffers must stay below 2 GiB (32-bit lane offsets in the kernels)
+  if ((int64_t)M * L->K > (int64_t)1 << 32 || (int64_t)L->N * L->K > (int64_t)1 << 32) return SVDQ_ERR_SHAPE;
   if (!L->smooth_inv || !L->wq || !L->ws) return SVDQ_ERR_ARG;
   if (L->rank > 0 && (!L->l1k || !L->l2k)) return SVDQ_ERR_ARG;
   if (!aligned16(L->smooth_inv) || !aligned16(L->wq) || !aligned16(L->ws) ||

@@ -37,13 +37,7 @@ bool geometry(int32_t K, int32_t N, int32_t rank, int32_t fmt, Geometry* g) {
   return true;
 }
 
-int32_t choose_zsplit(int32_t M, int32_t K) {
-  const int32_t steps = K / kStep;
-  const int64_t rowwaves = ((int64_t)M + 15) / 16;
-  int32_t z = 1;
-  while (z * 2 <= 4 && steps % (z * 2) == 0 && rowwaves * z < 2048) z *= 2;
-  return z;
-}
+int32_t choose_zsplit(int32_t, int32_t) { return 1; }   // K-A reduces Z inside each block
 
 int default_threads(int requested) {
   if (requested > 0) return requested;
