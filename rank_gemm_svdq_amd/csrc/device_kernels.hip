@@ -35,6 +35,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <type_traits>
 #include <cstdint>
 #include <cstring>
 
@@ -443,28 +444,37 @@ __global__ __launch_bounds__(256) void kb_kernel(const uint8_t* __restrict__ xq,
 
 // ----------------------------------------------------- K-B, MXFP4, large tile
 //
-// 256 (tokens) x 256 (out-features) per block of 4 waves, one wave per SIMD;
-// wave w owns tokens 128 (w & 1) .. +128 and out-features 128 (w >> 1) ..
-// +128, i.e. 8 x 8 MFMA tiles of 16 x 16 (256 fp32 accumulators per lane).
+// 256 (tokens) x 256 (out-features) per block of 8 waves, two per SIMD; wave
+// w owns tokens 128 (w & 1) .. +128 and out-features 64 (w >> 1) .. +64, i.e.
+// 4 x 8 MFMA tiles of 16 x 16 (128 fp32 accumulators per lane).
+//
 // Codes travel global -> LDS by direct-to-LDS loads (no register staging)
-// into a ring of three 32 KB step buffers, three steps ahead of the MFMAs;
+// into a ring of four 32 KB step buffers, three steps ahead of the MFMAs;
 // scale dwords (one per row and 4 steps) travel the same way into a double
-// buffer.  The fragments of step t + 1 are read from LDS while the 64 scaled
-// FP4 MFMAs of step t run (register double buffering), so after the first
-// step the MFMA pipe does not wait on LDS.
+// buffer.  Inside a step, the token fragments of the next step and the next
+// weight fragment are read from LDS while the current MFMAs run, so the
+// barrier at the top of each step does not expose LDS latency.  The low-rank
+// epilogue (Z L2') is applied after the main loop from Z and L2' tiles that
+// were DMA'd into ring buffers freed by the last steps.
+//
+// Weight rows are permuted inside each pair of 16-row MFMA tiles (2p, 2p+1):
+// MFMA row q of tile 2p + h is out-feature 32 p + 8 (q / 4) + 4 h + q % 4, so
+// the 4 + 4 accumulators a lane holds for the pair are 8 consecutive
+// out-features of one token: one 16-byte store.
 
-constexpr int MX_BM = 256, MX_BN = 256, MX_THREADS = 256;
+constexpr int MX_BM = 256, MX_BN = 256, MX_THREADS = 512;
 constexpr int MX_STEP_BYTES = (MX_BM + MX_BN) * 64;   // codes of one step, both operands
-constexpr int MX_NBUF = 3;
+constexpr int MX_NBUF = 4;
 constexpr int MX_SC_BYTES = (MX_BM + MX_BN) * 16;     // scale dwords of one 4-step group
 constexpr int MX_LDS = MX_NBUF * MX_STEP_BYTES + 2 * MX_SC_BYTES;
 
 #define SVDQ_AS3 __attribute__((address_space(3)))
 
 // One wave-wide 1 KB direct-to-LDS copy: lane i's 16 bytes at sbase + voff
-// (sbase wave-uniform, voff per lane) land at LDS byte lds_base + 16 i.  Issued from asm so that the compiler does not
-// serialise it against unrelated LDS reads; completion is tracked with
-// explicit vmcnt waits.  M0 is restored before the asm block ends.
+// (sbase wave-uniform, voff per lane) land at LDS byte lds_base + 16 i.
+// Issued from asm so that the compiler does not serialise it against
+// unrelated LDS reads; completion is tracked with explicit vmcnt waits.
+// M0 is restored before the asm block ends.
 __device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, uint32_t lds_base) {
   uint32_t saved;
   asm volatile(
@@ -473,7 +483,7 @@ __device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, uint3
       "global_load_lds_dwordx4 %2, %3\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(lds_base), "v"(voff), "s"(sbase)
+      : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(sbase)
       : "memory");
 }
 
@@ -489,12 +499,12 @@ __device__ __forceinline__ void mx_tile_of(int b, int tiles_m, int tiles_n, int*
   *tn = id / tiles_m;
 }
 
-struct MxFrag {
-  v4i a[8];            // weight rows (out-features) of the wave, one per 16-row tile
-  v4i b[8];            // token rows
-};
+// out-feature (relative to the wave's 64) of MFMA row q of weight tile nt
+__device__ __forceinline__ int mx_nrow(int nt, int q) {
+  return 32 * (nt >> 1) + 8 * (q >> 2) + 4 * (nt & 1) + (q & 3);
+}
 
-template <int NTR>
+template <int NTR, bool ODD>
 __global__ __launch_bounds__(MX_THREADS, 1) void kb_mx_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const float* __restrict__ zp, int zsplit,
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws, const uint16_t* __restrict__ l2k,
@@ -511,195 +521,280 @@ __global__ __launch_bounds__(MX_THREADS, 1) void kb_mx_kernel(
   const int tile_m = tm * MX_BM, tile_n = tn * MX_BN;
   const int steps = K / 128;
   const int ks4 = (steps + 3) / 4;
-  const size_t rowbytes = (size_t)K / 2;
-  const int m_base = tile_m + 128 * wm, n_base = tile_n + 128 * wn;
+  const uint32_t rowbytes = (uint32_t)K / 2;
+  const int m_base = tile_m + 128 * wm, n_base = tile_n + 64 * wn;
 
-  // ---- DMA plan.  Codes: wave w moves the 1 KB units 8w .. 8w+7 of a step
-  // buffer (units 0-15: 16 token rows each, units 16-31: 16 out-feature rows
-  // each); lane i fills 16-byte slot p = 64 (u mod 16) + i of its operand
-  // tile, i.e. row p / 4 at swizzled chunk position p mod 4.
-  // Waves 0-1 move token rows, waves 2-3 weight rows; offsets are 32-bit
-  // (operands are below 2 GiB, checked on the host).
-  const uint8_t* cbase = wave < 2 ? xq : wq;
-  uint32_t coff[8];
+  // ---- DMA plan.  Codes: wave w moves the 1 KB units 4w .. 4w+3 of a step
+  // buffer (units 0-15: 16 token rows each, units 16-31: 16 weight rows each);
+  // lane i fills 16-byte slot p = 64 (u mod 16) + i of its operand tile, i.e.
+  // row p / 4 at swizzled chunk position p mod 4.  Waves 0-3 move token rows,
+  // waves 4-7 weight rows; lane offsets are 32-bit (operands below 2 GiB,
+  // checked on the host).
+  const uint8_t* cbase = wave < 4 ? xq : wq;
+  uint32_t coff[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int u = 8 * wave + j;
+  for (int j = 0; j < 4; ++j) {
+    const int u = 4 * wave + j;
     const int p = 64 * (u & 15) + lane, r = p >> 2, c = (p & 3) ^ swz_f(r);
-    const int row = wave < 2 ? min(tile_m + r, M - 1) : min(tile_n + r, N - 1);
-    coff[j] = (uint32_t)row * (uint32_t)rowbytes + 16u * c;
+    const int row = wave < 4 ? min(tile_m + r, M - 1) : min(tile_n + r, N - 1);
+    coff[j] = (uint32_t)row * rowbytes + 16u * c;
   }
-  // Scales: units 0-3 hold token rows 64 u + lane, units 4-7 out-feature
-  // rows 64 (u - 4) + lane; 16 bytes (4 dwords, one per lane group) per row.
-  // Wave w moves units 2w and 2w + 1.
-  const uint8_t* sbase = wave < 2 ? xs : ws;
-  uint32_t soff[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int u = 2 * wave + j;
-    const int row = u < 4 ? min(tile_m + 64 * u + lane, M - 1) : min(tile_n + 64 * (u - 4) + lane, N - 1);
-    soff[j] = (uint32_t)row * (uint32_t)(ks4 * 16);
-  }
+  // Scales: wave w < 4 moves token rows 64 w + lane, w >= 4 weight rows
+  // 64 (w - 4) + lane; 16 bytes (4 dwords, one per lane group) per row.
+  const uint8_t* sbase = wave < 4 ? xs : ws;
+  const int srow = wave < 4 ? min(tile_m + 64 * wave + lane, M - 1) : min(tile_n + 64 * (wave - 4) + lane, N - 1);
+  const uint32_t soff = (uint32_t)srow * (uint32_t)(ks4 * 16);
   const uint32_t scale_lds = lds_u32 + MX_NBUF * MX_STEP_BYTES;
-  auto issue_codes = [&](int t) {
-    const uint32_t b = lds_u32 + (uint32_t)(t % MX_NBUF) * MX_STEP_BYTES + (uint32_t)wave * 8192u;
+  auto issue_codes = [&](int t) __attribute__((always_inline)) {
+    const uint32_t b = lds_u32 + (uint32_t)(t % MX_NBUF) * MX_STEP_BYTES + (uint32_t)wave * 4096u;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) dma16(cbase + (size_t)t * 64, coff[j], b + 1024u * j);
+    for (int j = 0; j < 4; ++j) dma16(cbase + (size_t)t * 64, coff[j], b + 1024u * j);
   };
-  auto issue_scales = [&](int grp) {
-    const uint32_t b = scale_lds + (uint32_t)(grp & 1) * MX_SC_BYTES + (uint32_t)wave * 2048u;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) dma16(sbase + (size_t)grp * 16, soff[j], b + 1024u * j);
-  };
-  // Fragment q of a wave reads row R + 16 q (R = 128 wm + l16, or
-  // 128 wn + l16 in the weight half) at chunk g; swz_f of that row only
-  // depends on the parity of q, so two lane addresses per operand and
-  // immediate offsets of 1 KB per q cover all 16 reads of a step.
-  uint32_t fb_off[2], fa_off[2];
-#pragma unroll
-  for (int par = 0; par < 2; ++par) {
-    fb_off[par] = (uint32_t)swz(128 * wm + 16 * par + l16, g) - 1024u * par;
-    fa_off[par] = (uint32_t)(MX_BM * 64 + swz(128 * wn + 16 * par + l16, g)) - 1024u * par;
-  }
-  auto read_frags = [&](int t, MxFrag& f) {
-    const uint32_t buf = (uint32_t)(t % MX_NBUF) * MX_STEP_BYTES;
-    const uint8_t* pb0 = lds + buf + fb_off[0];
-    const uint8_t* pb1 = lds + buf + fb_off[1];
-    const uint8_t* pa0 = lds + buf + fa_off[0];
-    const uint8_t* pa1 = lds + buf + fa_off[1];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      f.b[q] = *reinterpret_cast<const v4i*>(((q & 1) ? pb1 : pb0) + 1024 * q);
-      f.a[q] = *reinterpret_cast<const v4i*>(((q & 1) ? pa1 : pa0) + 1024 * q);
-    }
-  };
-  auto read_scales = [&](int grp, uint32_t* asc, uint32_t* bsc) {
-    const uint32_t* sc = reinterpret_cast<const uint32_t*>(lds + MX_NBUF * MX_STEP_BYTES + (grp & 1) * MX_SC_BYTES);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      bsc[q] = sc[(128 * wm + 16 * q + l16) * 4 + g];
-      asc[q] = sc[(MX_BM + 128 * wn + 16 * q + l16) * 4 + g];
-    }
+  auto issue_scales = [&](int grp) __attribute__((always_inline)) {
+    dma16(sbase + (size_t)grp * 16, soff, scale_lds + (uint32_t)(grp & 1) * MX_SC_BYTES + (uint32_t)wave * 1024u);
   };
 
-  issue_scales(0);
-  issue_codes(0);
-  if (steps > 1) issue_codes(1);
-  if (steps > 2) issue_codes(2);
-
-  // ---- bias and the low-rank up projection initialise the accumulators
-  // (overlapping the first code loads)
-  v4f acc[8][8];   // [n-tile][m-tile]
+  // fragment addresses (without the step-buffer offset): token fragment q
+  // reads row 128 wm + 16 q + l16 (two parities, 1 KB apart per q), weight
+  // fragment nt reads the permuted row 64 wn + mx_nrow(nt, l16)
+  uint32_t boff[2], aoff[4];
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt) {
-    const int n0 = n_base + 16 * nt + 4 * g;
-    float bv[4] = {0.f, 0.f, 0.f, 0.f};
-    if (bias != nullptr) {
+  for (int par = 0; par < 2; ++par) boff[par] = (uint32_t)swz(128 * wm + 16 * par + l16, g) - 1024u * par;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int n = n0 + i < N ? n0 + i : N - 1;
-        bv[i] = __uint_as_float((uint32_t)bias[n] << 16);
-      }
-    }
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) acc[nt][mt] = (v4f){bv[0], bv[1], bv[2], bv[3]};
-  }
-  if constexpr (NTR > 0) {
-    for (int u = 0; u < NTR; ++u) {
-      v8bf bh[8], bl[8];
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        int m = m_base + 16 * mt + l16;
-        m = m < M ? m : M - 1;
-        float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int p = 0; p < zsplit; ++p) {
-          const float* src = zp + ((size_t)p * M + m) * rpad + 32 * u + 8 * g;
-          const v4f z0 = *reinterpret_cast<const v4f*>(src), z1 = *reinterpret_cast<const v4f*>(src + 4);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) { z[i] += z0[i]; z[4 + i] += z1[i]; }
-        }
-        uint16_t hi[8], lo[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t hb = bf16_rne(z[i]);
-          hi[i] = (uint16_t)hb;
-          lo[i] = (uint16_t)bf16_rne(z[i] - __uint_as_float(hb << 16));
-        }
-        bh[mt] = __builtin_bit_cast(v8bf, *reinterpret_cast<v4i*>(hi));
-        bl[mt] = __builtin_bit_cast(v8bf, *reinterpret_cast<v4i*>(lo));
-      }
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        int n = n_base + 16 * nt + l16;
-        n = n < N ? n : N - 1;
-        const v8bf af = *reinterpret_cast<const v8bf*>(l2k + (size_t)n * rpad + 32 * u + 8 * g);
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-          acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bh[mt], acc[nt][mt], 0, 0, 0);
-          acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bl[mt], acc[nt][mt], 0, 0, 0);
-        }
-      }
-    }
-  }
-
-  // ---- main loop
-  auto mfma_step = [&](const MxFrag& f, const uint32_t* asc, const uint32_t* bsc, int t) {
-    const int sh = 8 * (t & 3);
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const v8i a = (v8i){f.a[nt][0], f.a[nt][1], f.a[nt][2], f.a[nt][3], 0, 0, 0, 0};
-      const int as = (int)(asc[nt] >> sh);
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        const v8i b = (v8i){f.b[mt][0], f.b[mt][1], f.b[mt][2], f.b[mt][3], 0, 0, 0, 0};
-        acc[nt][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[nt][mt], 4, 4, 0, as, 0,
-                                                                      (int)(bsc[mt] >> sh));
-      }
-    }
+  for (int nt = 0; nt < 4; ++nt) aoff[nt] = (uint32_t)(MX_BM * 64 + swz(64 * wn + mx_nrow(nt, l16), g));
+  // bo: byte offset of a step buffer, kept opaque to the optimiser so that
+  // it does not hoist one address register per (buffer, fragment) pair out
+  // of the unrolled loop
+  auto buf_of = [&](int t) __attribute__((always_inline)) -> uint32_t {
+    uint32_t bo = (uint32_t)(t % MX_NBUF) * MX_STEP_BYTES;
+    asm volatile("" : "+s"(bo));
+    return bo;
   };
-  // waits: before reading step s's buffer, every DMA issued before s's own
-  // must be done; the only younger ones are those of step s + 1 (8 per wave)
-  auto wait_for = [&](int s) {
+  auto read_b = [&](uint32_t bo, int q) __attribute__((always_inline)) -> v4i {
+    return *reinterpret_cast<const v4i*>(lds + bo + boff[q & 1] + 1024 * q);
+  };
+  auto read_a = [&](uint32_t bo, int nt) __attribute__((always_inline)) -> v4i {
+    return *reinterpret_cast<const v4i*>(lds + bo + aoff[nt]);
+  };
+  // scale registers hold the E8M0 bytes of a pair of steps (tp, tp+1), tp
+  // even, in their low half: a 16-bit read from the group's dwords
+  uint32_t asc[4], bsc[8];
+  auto read_scales = [&](int tp) __attribute__((always_inline)) {
+    uint32_t so = (uint32_t)(MX_NBUF * MX_STEP_BYTES + ((tp >> 2) & 1) * MX_SC_BYTES + 2 * ((tp >> 1) & 1));
+    asm volatile("" : "+s"(so));
+    const uint8_t* sc = lds + so;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) bsc[q] = *reinterpret_cast<const uint16_t*>(sc + ((128 * wm + 16 * q + l16) * 4 + g) * 4);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+      asc[nt] = *reinterpret_cast<const uint16_t*>(sc + ((MX_BM + 64 * wn + mx_nrow(nt, l16)) * 4 + g) * 4);
+  };
+  // every DMA issued before step s's must be done; only step s + 1's (4 per
+  // wave) may still be in flight
+  auto wait_for = [&](int s) __attribute__((always_inline)) {
     if (s + 1 < steps)
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
 
-  MxFrag f0, f1;
-  uint32_t asc[8], bsc[8];
+  issue_scales(0);
+#pragma unroll
+  for (int s0 = 0; s0 < 3; ++s0)
+    if (s0 < steps) issue_codes(s0);
+
+  v4f acc[4][8];   // [weight tile][token tile]
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) acc[nt][mt] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  v4i wf[2][4];   // weight fragments of the current and the next step
+  v4i tk[4];      // token fragments, three ahead; fragment q sits in slot q & 3
   wait_for(0);
-  read_frags(0, f0);
-  // iteration t: buffer (t+1) becomes readable, step t+3 is fetched into the
-  // buffer step t used (all waves are past their reads of it), the fragments
-  // of t+1 are read while the MFMAs of t run.
-  auto iter = [&](int t, MxFrag& cur, MxFrag& nxt) {
-    if (t + 1 < steps) wait_for(t + 1);
+  read_scales(0);
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) wf[0][nt] = read_a(0, nt);
+#pragma unroll
+  for (int q = 0; q < 3; ++q) tk[q] = read_b(0, q);
+
+  // The lane index is made opaque in these two so that their address
+  // arithmetic is redone where they are called instead of being hoisted out
+  // of the main loop into live registers.
+  auto issue_z = [&](int u, uint32_t zdst) __attribute__((always_inline)) {
+    // Z: 32 units of 8 rows x 128 B; wave w moves units 4w .. 4w+3
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int unit = 4 * wave + j, row = 8 * unit + (ln >> 3);
+      const int m = min(tile_m + row, M - 1);
+      dma16(reinterpret_cast<const uint8_t*>(zp), ((uint32_t)m * (uint32_t)rpad + 32u * u) * 4u + 16u * (ln & 7),
+            zdst + 1024u * unit);
+    }
+  };
+  auto issue_l2 = [&](int u, uint32_t ldst) __attribute__((always_inline)) {
+    // L2'^T: 16 units of 16 rows x 64 B; wave w moves units 2w, 2w+1
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int unit = 2 * wave + j, row = 16 * unit + (ln >> 2);
+      const int n = min(tile_n + row, N - 1);
+      dma16(reinterpret_cast<const uint8_t*>(l2k), ((uint32_t)n * (uint32_t)rpad + 32u * u) * 2u + 16u * (ln & 3),
+            ldst + 1024u * unit);
+    }
+  };
+  // Chunk 0 of Z and L2' is fetched right after the barrier of step
+  // steps-2: by then every wave has left steps-4 and steps-3, whose buffers
+  // take Z and L2' (no code DMA targets them any more).
+  const bool lr_prefetch = NTR > 0 && steps >= 4;
+  const uint32_t zpre = (uint32_t)((steps - 4 + MX_NBUF) % MX_NBUF) * MX_STEP_BYTES;
+  const uint32_t lpre = (uint32_t)((steps - 3 + MX_NBUF) % MX_NBUF) * MX_STEP_BYTES;
+  auto lr_prefetch_issue = [&]() __attribute__((always_inline)) {
+    if (lr_prefetch) {
+      issue_z(0, lds_u32 + zpre);
+      issue_l2(0, lds_u32 + lpre);
+    }
+  };
+  // step t, J = t & 1: the barrier publishes step t+1's buffer; the buffer
+  // of step t-1 (all waves are past it) receives step t+3.  While the MFMAs
+  // of t run, the weight fragments of t+1 and the token fragments three MFMA
+  // groups ahead are read.  The scale registers hold the bytes of steps
+  // (t & ~1, t | 1) in their low half; the MFMA's op_sel picks byte J.  The
+  // last step also reads the next buffer; those reads stay inside LDS and
+  // are never used.
+  auto step = [&](int t, auto jtag, auto hooktag) __attribute__((always_inline)) {
+    constexpr int J = decltype(jtag)::value;
+    constexpr int HOOK = decltype(hooktag)::value;   // 0 none, 1 always, 2 at step steps-2
+    wait_for(t + 1);
     if ((t & 3) == 0 && (t >> 2) + 1 < ks4) issue_scales((t >> 2) + 1);
     if (t + 3 < steps) issue_codes(t + 3);
-    if (t + 1 < steps) read_frags(t + 1, nxt);
-    if ((t & 3) == 0) read_scales(t >> 2, asc, bsc);
-    mfma_step(cur, asc, bsc, t);
+    if constexpr (HOOK == 1) lr_prefetch_issue();
+    if constexpr (HOOK == 2) {
+      if (t == steps - 2) lr_prefetch_issue();
+    }
+    const uint32_t bc = buf_of(t), bn = buf_of(t + 1);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      if (mt < 4) wf[J ^ 1][mt] = read_a(bn, mt);
+      tk[(mt + 3) & 3] = mt + 3 < 8 ? read_b(bc, mt + 3) : read_b(bn, mt - 5);
+      const v4i bq = tk[mt & 3];
+      const v8i b = (v8i){bq[0], bq[1], bq[2], bq[3], 0, 0, 0, 0};
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const v4i aq = wf[J][nt];
+        const v8i a = (v8i){aq[0], aq[1], aq[2], aq[3], 0, 0, 0, 0};
+        acc[nt][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[nt][mt], 4, 4, J, (int)asc[nt], J,
+                                                                      (int)bsc[mt]);
+      }
+      // keep each group's reads next to its MFMAs: hoisting all reads of a
+      // step to its top would need twice the fragment registers
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
-  int t = 0;
-  for (; t + 1 < steps; t += 2) {
-    iter(t, f0, f1);
-    iter(t + 1, f1, f0);
+  using J0 = std::integral_constant<int, 0>;
+  using J1 = std::integral_constant<int, 1>;
+  using H0 = std::integral_constant<int, 0>;
+  using H1 = std::integral_constant<int, 1>;
+  using H2 = std::integral_constant<int, 2>;
+  // Pairs of steps; one loop exit keeps the accumulators in place.  With an
+  // even step count the last pair is peeled and the prefetch sits in it;
+  // with an odd one the prefetch is tested in the loop and one step follows.
+  if constexpr (!ODD) {
+    for (int t0 = 0; t0 < steps - 2; t0 += 2) {
+      step(t0, J0{}, H0{});
+      step(t0 + 1, J1{}, H0{});
+      read_scales(t0 + 2);
+    }
+    step(steps - 2, J0{}, H1{});
+    step(steps - 1, J1{}, H0{});
+  } else {
+    for (int t0 = 0; t0 < steps - 1; t0 += 2) {
+      step(t0, J0{}, H0{});
+      step(t0 + 1, J1{}, H2{});
+      read_scales(t0 + 2);
+    }
+    step(steps - 1, J0{}, H0{});
   }
-  if (t < steps) iter(t, f0, f1);
 
+  // ---- low-rank up projection and bias, then one 16-byte store per pair
+  if constexpr (NTR > 0) {
+    for (int u = 0; u < NTR; ++u) {
+      uint32_t zoff, loff;
+      if (u == 0 && lr_prefetch) {
+        zoff = zpre;
+        loff = lpre;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+      } else {
+        // all ring buffers are idle once every wave has left the main loop
+        // (or finished the previous chunk)
+        __syncthreads();
+        zoff = 0;
+        loff = MX_STEP_BYTES;
+        issue_z(u, lds_u32 + zoff);
+        issue_l2(u, lds_u32 + loff);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+      }
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt) {
-    const int m = m_base + 16 * mt + l16;
-    if (m >= M) continue;
+      for (int mh = 0; mh < 2; ++mh) {
+        v8bf bh[4], bl[4];
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const int n0 = n_base + 16 * nt + 4 * g;
-      if (n0 >= N) continue;
-      const uint32_t lo = bf16_rne(acc[nt][mt][0]) | (bf16_rne(acc[nt][mt][1]) << 16);
-      const uint32_t hi = bf16_rne(acc[nt][mt][2]) | (bf16_rne(acc[nt][mt][3]) << 16);
-      *reinterpret_cast<uint2*>(Y + (size_t)m * N + n0) = make_uint2(lo, hi);
+        for (int k = 0; k < 4; ++k) {
+          const int mt = 4 * mh + k;
+          const float* zr = reinterpret_cast<const float*>(lds + zoff + (128 * wm + 16 * mt + l16) * 128 + 32 * g);
+          uint16_t hi[8], lo[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float z = zr[i];
+            const uint32_t hb = bf16_rne(z);
+            hi[i] = (uint16_t)hb;
+            lo[i] = (uint16_t)bf16_rne(z - __uint_as_float(hb << 16));
+          }
+          bh[k] = __builtin_bit_cast(v8bf, *reinterpret_cast<v4i*>(hi));
+          bl[k] = __builtin_bit_cast(v8bf, *reinterpret_cast<v4i*>(lo));
+        }
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const v8bf af = *reinterpret_cast<const v8bf*>(lds + loff + (64 * wn + mx_nrow(nt, l16)) * 64 + 16 * g);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            acc[nt][4 * mh + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bh[k], acc[nt][4 * mh + k], 0, 0, 0);
+            acc[nt][4 * mh + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bl[k], acc[nt][4 * mh + k], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+  // lane holds out-features n_base + 32 p + 8 g + 0..7 of token m for pair p
+#pragma unroll
+  for (int p2 = 0; p2 < 2; ++p2) {
+    const int n0 = n_base + 32 * p2 + 8 * g;
+    float bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (bias != nullptr && n0 < N) {
+      const v4i braw = *reinterpret_cast<const v4i*>(bias + n0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        bv[2 * i] = bf16_lo((uint32_t)braw[i]);
+        bv[2 * i + 1] = bf16_hi((uint32_t)braw[i]);
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      const int m = m_base + 16 * mt + l16;
+      if (m >= M || n0 >= N) continue;
+      v4i o;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        o[i] = (int)(bf16_rne(acc[2 * p2][mt][2 * i] + bv[2 * i]) |
+                     (bf16_rne(acc[2 * p2][mt][2 * i + 1] + bv[2 * i + 1]) << 16));
+        o[2 + i] = (int)(bf16_rne(acc[2 * p2 + 1][mt][2 * i] + bv[4 + 2 * i]) |
+                         (bf16_rne(acc[2 * p2 + 1][mt][2 * i + 1] + bv[4 + 2 * i + 1]) << 16));
+      }
+      *reinterpret_cast<v4i*>(Y + (size_t)m * N + n0) = o;
     }
   }
 }
@@ -731,9 +826,16 @@ static void launch_kb_mx(const svdq_layer& L, const uint8_t* ws, const svdq_ws_l
                          hipStream_t st) {
   const int rp = rank_pad(L.rank);
   const int tiles = ((M + MX_BM - 1) / MX_BM) * ((L.N + MX_BN - 1) / MX_BN);
-  hipLaunchKernelGGL((kb_mx_kernel<NTR>), dim3(tiles), dim3(MX_THREADS), 0, st, ws + W.xq_off, ws + W.xs_off,
-                     reinterpret_cast<const float*>(ws + W.z_off), W.zsplit, L.wq, L.ws, L.l2k, L.bias, Y, M, L.N,
-                     L.K, rp);
+  // the K loop runs in pairs of 128-wide steps; an odd step count takes the
+  // variant with one trailing step
+  if ((L.K / 128) % 2 == 0)
+    hipLaunchKernelGGL((kb_mx_kernel<NTR, false>), dim3(tiles), dim3(MX_THREADS), 0, st, ws + W.xq_off,
+                       ws + W.xs_off, reinterpret_cast<const float*>(ws + W.z_off), W.zsplit, L.wq, L.ws, L.l2k,
+                       L.bias, Y, M, L.N, L.K, rp);
+  else
+    hipLaunchKernelGGL((kb_mx_kernel<NTR, true>), dim3(tiles), dim3(MX_THREADS), 0, st, ws + W.xq_off,
+                       ws + W.xs_off, reinterpret_cast<const float*>(ws + W.z_off), W.zsplit, L.wq, L.ws, L.l2k,
+                       L.bias, Y, M, L.N, L.K, rp);
 }
 
 template <int FMT>
