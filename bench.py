@@ -9,6 +9,12 @@ check against the oracle on sampled rows, and the oracle timed on the host
 cores as a baseline.
 
   python bench.py [--steps K] [--warmup W] [--config flux_mlp_up] [--gpus 1]
+
+Profiles: run the same command under rocprofv3 (kernel trace + stats, then
+one --pmc pass each for FETCH_SIZE and WRITE_SIZE with --calib-copy, which
+adds a device copy of known size to scale the counters), then
+  python bench.py --summarize-profiles DIR
+writes the text summaries and the per-launch HBM traffic under profiles/.
 """
 
 import argparse
@@ -51,6 +57,40 @@ def measured_traffic(config):
     return e.get("bytes_per_launch")
 
 
+def kb_kernel_names(fmt, K, rank):
+    """Demangled and mangled names of the K-B instantiation a layer launches."""
+    ntr = ((rank + 31) // 32 * 32) // 32
+    if fmt == "mxfp4":
+        odd = (K // 128) % 2
+        return (f"kb_mx_kernel<{ntr}, {'true' if odd else 'false'}>", f"kb_mx_kernelILi{ntr}ELb{odd}E")
+    return (f"kb_kernel<0, {ntr}>", f"kb_kernelILi0ELi{ntr}E")
+
+
+def oracle_sample(F, X, po, bias, seconds):
+    """(rows, passes, seconds) of oracle forward work that takes about
+    `seconds`: the first n token rows, n grown until it does, or whole-layer
+    passes repeated when the whole layer takes less."""
+    M = X.shape[0]
+    n = 16
+    while True:
+        t0 = time.perf_counter()
+        F.forward(X[:n], po, bias)
+        t = time.perf_counter() - t0
+        if t >= 0.5 * seconds:
+            return n, 1, t
+        if n >= M:
+            break
+        n = min(M, int(n * min(8.0, max(2.0, seconds / max(t, 1e-3)))))
+    passes = max(1, int(round(seconds / max(t, 1e-3))))
+    t0 = time.perf_counter()
+    for _ in range(passes):
+        F.forward(X, po, bias)
+    return M, passes, time.perf_counter() - t0
+
+
+CALIB_BYTES = 256 << 20
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -59,10 +99,24 @@ def main():
     ap.add_argument("--config", default="flux_mlp_up")
     ap.add_argument("--fmt", default=None, help="override the workload's format (int4 | mxfp4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--skip-oracle", action="store_true",
                     help="timing only: no oracle parity check and no CPU baseline (profiling runs)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one device-to-device copy of 256 MiB (counter calibration)")
+    ap.add_argument("--print-profile-commands", metavar="DIR", default=None,
+                    help="print the rocprofv3 commands whose output --summarize-profiles reads")
+    ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
+                    help="summarise rocprofv3 output under DIR into profiles/ (no GPU needed)")
     args = ap.parse_args()
+    if args.print_profile_commands:
+        cfg = args.config + (f" --fmt {args.fmt}" if args.fmt else "")
+        for k, c in profile_commands(args.print_profile_commands, cfg).items():
+            print(f"{k}\t{c}")
+        return
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles, args.config, args.fmt)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the layer shards over tokens with no communication; see the design notes)", file=sys.stderr)
@@ -130,6 +184,14 @@ def main():
     log("timing the layer")
     ms, ka, kb, wall = timed(layer, ws, args.steps, args.warmup)
 
+    if args.calib_copy:
+        src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     parity = None
     if not args.skip_oracle:
         # parity on sampled rows against the oracle's own preparation
@@ -168,17 +230,16 @@ def main():
     if not args.no_cpu_baseline and not args.skip_oracle:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-        # bounded sample: as many rows as fit ~cpu_seconds of oracle forward
-        t0 = time.time()
-        F.forward(d["X"][:8], po, d["bias"])
-        t8 = time.time() - t0
-        nrows = int(min(M, max(8, 8 * args.cpu_seconds / max(t8, 1e-3))))
-        t0 = time.time()
-        F.forward(d["X"][:nrows], po, d["bias"])
-        t_cpu = time.time() - t0
-        cpu = {"value": 2.0 * nrows * N * K / t_cpu / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
-               "sample": f"oracle forward (O7-O11, fp64 BLAS) on {nrows} of {M} token rows of the same layer, "
-                         f"{t_cpu:.1f} s; oracle prepare (LAPACK SVD) took {t_oracle_prepare:.1f} s",
+        # bounded sample: the first n token rows of the same layer, n grown
+        # until the oracle forward takes about cpu_seconds
+        nrows, passes, t_cpu = oracle_sample(F, d["X"], po, d["bias"], args.cpu_seconds)
+        what = (f"{passes} passes over all {M} token rows" if nrows == M
+                else f"the first {nrows} of {M} token rows")
+        cpu = {"value": 2.0 * nrows * passes * N * K / t_cpu / 1e12, "unit": "TOPS", "cores": threads,
+               "kind": "oracle",
+               "sample": f"oracle forward (fp64: smoothing, quantisation, decoded GEMM, low-rank branch, bias), "
+                         f"{what} of the same layer, {t_cpu:.1f} s on {threads} BLAS threads; oracle prepare "
+                         f"(LAPACK SVD) took {t_oracle_prepare:.1f} s and is not in the rate",
                "host_cpus": os.cpu_count()}
 
     out = {
@@ -191,7 +252,7 @@ def main():
         "pct_of_peak": 100.0 * tops / PEAK[fmt], "peak_name": PEAK_NAME[fmt],
         "roofline": {"bound": "mfma", "achieved": kb_achieved / 1e12, "peak": PEAK[fmt] / 1e12, "unit": "TFLOP/s",
                      "frac": kb_achieved / PEAK[fmt],
-                     "traffic": traffic, "kernel": "kb_kernel (W4A4 GEMM + lora_up + bias)",
+                     "traffic": traffic, "kernel": kb_kernel_names(fmt, K, r)[0] + " (W4A4 GEMM + lora_up + bias)",
                      "algorithmic_ops_per_launch": main_ops, "algorithmic_bytes_per_launch": kb_bytes},
         "ka": {"us": t_ka * 1e6, "algorithmic_bytes": ka_bytes, "GB_per_s": ka_bytes / t_ka / 1e9,
                "frac_of_hbm": ka_bytes / t_ka / HBM_PEAK},
@@ -203,6 +264,143 @@ def main():
         "wall_s_timed": wall,
     }
     print(json.dumps(out))
+
+
+# ------------------------------------------------------------ profile summaries
+
+PROFILE_STEPS = {
+    "stats": "--kernel-trace --stats --output-format csv -d {dir}/stats -o run -- "
+             "python -u bench.py --config {config} --steps 20 --warmup 5 --skip-oracle",
+    "fetch": "--pmc FETCH_SIZE --output-format csv -d {dir}/fetch -o run -- "
+             "python -u bench.py --config {config} --steps 3 --warmup 1 --skip-oracle --calib-copy",
+    "write": "--pmc WRITE_SIZE --output-format csv -d {dir}/write -o run -- "
+             "python -u bench.py --config {config} --steps 3 --warmup 1 --skip-oracle --calib-copy",
+}
+
+
+def profile_commands(d, config):
+    return {k: "rocprofv3 " + v.format(dir=d, config=config) for k, v in PROFILE_STEPS.items()}
+
+
+def _csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _find(d, suffix):
+    for root, _, files in os.walk(d):
+        for f in sorted(files):
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    raise FileNotFoundError(f"no *{suffix} under {d}")
+
+
+def _matches(name, names):
+    return any(n in name for n in names)
+
+
+def summarize_profiles(d, config, fmt_override=None):
+    """Text summaries of a stats run and the FETCH_SIZE / WRITE_SIZE runs
+    under d (made by the commands of profile_commands) -> profiles/."""
+    sys.path.insert(0, ROOT)
+    from rank_gemm_svdq_amd import synthetic as S
+    from oracle import accounting as A
+    s = S.spec(config, **({"fmt": fmt_override} if fmt_override else {}))
+    M, K, N, fmt = s.M, s.K, s.N, s.fmt
+    r = s.rank + s.lora_rank
+    rp = (r + 31) // 32 * 32 if r else 0
+    kb_names = kb_kernel_names(fmt, K, r)
+    ka_names = ("ka_kernel",)
+    short = "kb_mx" if fmt == "mxfp4" else "kb_int4"
+    key = s.name if not fmt_override else f"{s.name}_{fmt}"
+    cmds = profile_commands("gpurun_out/prof_" + key, config + (f" --fmt {fmt_override}" if fmt_override else ""))
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+
+    # kernel stats
+    rows = _csv(_find(os.path.join(d, "stats"), "kernel_stats.csv"))
+    col = lambda row, *c: next((row[k] for k in row if any(x.lower() == k.lower() for x in c)), None)
+    lines = [f"# Kernel time, {key} (M={M} K={K} N={N} rank={r} {fmt})", "",
+             "Command (from the repository root, TMPDIR=/tmp):", "", "    " + cmds["stats"], "",
+             "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    kb_avg = None
+    for row in rows:
+        name = col(row, "Name", "KernelName")
+        calls = int(float(col(row, "Calls")))
+        avg = float(col(row, "AverageNs")) / 1e3
+        mn, mx = float(col(row, "MinNs")) / 1e3, float(col(row, "MaxNs")) / 1e3
+        pct = float(col(row, "Percentage"))
+        short_name = name.split("(")[0].replace("void ", "")
+        lines.append(f"| {short_name} | {calls} | {avg:.2f} | {mn:.2f} | {mx:.2f} | {pct:.1f} |")
+        if _matches(name, kb_names):
+            kb_avg = avg
+    bench_json = os.path.join(d, "stats.json")
+    if os.path.exists(bench_json):
+        b = json.loads(open(bench_json).read().strip().splitlines()[-1])
+        lines += ["", f"bench.py under the profiler: K-B median {b['kb_us']:.2f} us (HIP events on the launch "
+                      f"stream), K-A median {b['ka']['us']:.2f} us, layer {b['value']:.0f} TOPS."]
+    if kb_avg is not None:
+        ops = A.main_ops(M, N, K)
+        lines += [f"{kb_names[0]}: average {kb_avg:.2f} us -> {ops / (kb_avg * 1e-6) / 1e12:.0f} TOP/s of "
+                  f"2MNK = {ops:.4g} ops per launch."]
+    open(os.path.join(ROOT, "profiles", f"{short}_{key}_kernel_stats.md"), "w").write("\n".join(lines) + "\n")
+
+    # HBM traffic: FETCH_SIZE / WRITE_SIZE (KiB per dispatch), scaled by a
+    # 256 MiB device copy measured in the same run
+    out = {}
+    for which in ("fetch", "write"):
+        cc = _csv(_find(os.path.join(d, which), "counter_collection.csv"))
+        cname = "FETCH_SIZE" if which == "fetch" else "WRITE_SIZE"
+        per = {}
+        for row in cc:
+            if row["Counter_Name"] != cname:
+                continue
+            per.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]) * 1024.0)
+        copy = [v for n, vs in per.items() if "copyBuffer" in n or "copy" in n.lower() for v in vs]
+        big = max(copy) if copy else None           # the 256 MiB calibration copy
+        factor = CALIB_BYTES / big if big else None
+        kb = [v for n, vs in per.items() if _matches(n, kb_names) for v in vs]
+        ka = [v for n, vs in per.items() if _matches(n, ka_names) for v in vs]
+        out[which] = {"copy_counter_bytes": big, "factor": factor,
+                      "kb_counter_bytes": float(np.mean(kb)) if kb else None,
+                      "ka_counter_bytes": float(np.mean(ka)) if ka else None,
+                      "kb_dispatches": len(kb), "ka_dispatches": len(ka)}
+    f_, w_ = out["fetch"], out["write"]
+    kb_alg = A.kb_bytes(M, N, K, r, fmt)
+    ka_alg = A.ka_bytes(M, K, r, fmt)
+    kb_traffic = ka_traffic = None
+    if f_["kb_counter_bytes"] and w_["kb_counter_bytes"] and f_["factor"] and w_["factor"]:
+        kb_traffic = f_["kb_counter_bytes"] * f_["factor"] + w_["kb_counter_bytes"] * w_["factor"]
+    if f_["ka_counter_bytes"] and w_["ka_counter_bytes"] and f_["factor"] and w_["factor"]:
+        ka_traffic = f_["ka_counter_bytes"] * f_["factor"] + w_["ka_counter_bytes"] * w_["factor"]
+    fmtb = lambda v: "n/a" if v is None else f"{v / 1e6:.2f} MB"
+    lines = [f"# HBM traffic per launch, {key} (M={M} K={K} N={N} rank={r} {fmt})", "",
+             "Commands (from the repository root, TMPDIR=/tmp):", "", "    " + cmds["fetch"], "    " + cmds["write"], "",
+             "Counters are KiB per dispatch; each is scaled by (256 MiB / the same counter on the 256 MiB "
+             "device copy of the same run).", "",
+             "| | FETCH_SIZE | WRITE_SIZE |", "|---|---|---|",
+             f"| calibration copy, counter | {fmtb(f_['copy_counter_bytes'])} | {fmtb(w_['copy_counter_bytes'])} |",
+             f"| scale factor | {f_['factor'] or float('nan'):.4f} | {w_['factor'] or float('nan'):.4f} |",
+             f"| {kb_names[0]}, counter (mean of {f_['kb_dispatches']}) | {fmtb(f_['kb_counter_bytes'])} | "
+             f"{fmtb(w_['kb_counter_bytes'])} |",
+             f"| ka_kernel, counter (mean of {f_['ka_dispatches']}) | {fmtb(f_['ka_counter_bytes'])} | "
+             f"{fmtb(w_['ka_counter_bytes'])} |", "",
+             f"K-B scaled traffic {fmtb(kb_traffic)} against {fmtb(kb_alg)} algorithmic "
+             f"({'n/a' if kb_traffic is None else f'{kb_traffic / kb_alg:.2f}x'}).",
+             f"K-A scaled traffic {fmtb(ka_traffic)} against {fmtb(ka_alg)} algorithmic "
+             f"({'n/a' if ka_traffic is None else f'{ka_traffic / ka_alg:.2f}x'})."]
+    open(os.path.join(ROOT, "profiles", f"{short}_{key}_traffic.md"), "w").write("\n".join(lines) + "\n")
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        t = {}
+    t[key] = {"kernel": kb_names[0], "kernel_source_sha256_16": kernel_source_hash(),
+              "bytes_per_launch": kb_traffic, "ka_bytes_per_launch": ka_traffic,
+              "kb_algorithmic_bytes": kb_alg, "ka_algorithmic_bytes": ka_alg,
+              "fetch": f_, "write": w_, "commands": [cmds["fetch"], cmds["write"]]}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(t, fh, indent=1, sort_keys=True)
+    print("\n".join(lines))
 
 
 if __name__ == "__main__":
