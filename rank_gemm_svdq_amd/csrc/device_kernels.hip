@@ -451,11 +451,15 @@ __global__ __launch_bounds__(256) void kb_kernel(const uint8_t* __restrict__ xq,
 // Codes travel global -> LDS by direct-to-LDS loads (no register staging)
 // into a ring of four 32 KB step buffers, three steps ahead of the MFMAs;
 // scale dwords (one per row and 4 steps) travel the same way into a double
-// buffer.  Inside a step, the token fragments of the next step and the next
-// weight fragment are read from LDS while the current MFMAs run, so the
-// barrier at the top of each step does not expose LDS latency.  The low-rank
-// epilogue (Z L2') is applied after the main loop from Z and L2' tiles that
-// were DMA'd into ring buffers freed by the last steps.
+// buffer.  The K loop runs in pairs of steps: the weight fragments of the
+// next step are read into the other half of a two-deep register set while
+// the current MFMAs run, and token fragments stream through four registers
+// three MFMA groups ahead, so the barrier at the top of each step exposes no
+// LDS latency and no fragment is ever copied between registers.  A 16-bit
+// LDS read per pair gives each scale register the E8M0 bytes of both steps;
+// the MFMA's op_sel picks the byte.  The low-rank epilogue (Z L2') is
+// applied after the K loop from Z and L2' tiles DMA'd into ring buffers the
+// last steps no longer use.
 //
 // Weight rows are permuted inside each pair of 16-row MFMA tiles (2p, 2p+1):
 // MFMA row q of tile 2p + h is out-feature 32 p + 8 (q / 4) + 4 h + q % 4, so
