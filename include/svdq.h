@@ -95,8 +95,10 @@ svdq_status svdq_layer_sizes(int32_t K, int32_t N, int32_t rank, int32_t fmt, sv
  *   xq   activation codes [M, K/2], two 4-bit codes per byte (MXFP4:
  *        canonical order; INT4: the bytes of each 128-element step permuted
  *        as for the weight codes)
- *   xs   activation scales (INT4: canonical [M, K/64] fp16 bits; MXFP4:
- *        E8M0 bytes in the permuted per-row layout of the weight scales)
+ *   xs   activation scales, one 16-byte record per row and 4 K steps of
+ *        128 (M * ceil(K/512) * 16 bytes): MXFP4 E8M0 bytes in the permuted
+ *        per-row layout of the weight scales; INT4 the fp16 pair of step t
+ *        (groups 2t, 2t+1) in the dword at byte 16 (t / 4) + 4 (t % 4)
  *   z    down projection Z, fp32 [zsplit][M][rank rounded up to 32]; zsplit
  *        is 1 in this version (partial sums are reduced inside K-A)
  * svdq_unpack_activations() turns a host copy into canonical form. */

@@ -25,8 +25,10 @@
 //     / 16, j = k % 16) sits at byte 16 g + 8 G + j / 2, nibble j % 2, so the
 //     16 bytes of lane group g hold 16 elements of each of the step's two
 //     64-element groups.
-//   INT4 activation scales: canonical [M][K/64] fp16.
-//   INT4 weight scales: [N/4][steps][4 rows][2 groups] fp16.
+//   INT4 activation scales: per row ceil(steps/4) * 16 bytes, the fp16 pair
+//     of step t (groups 2t, 2t+1) in the dword at byte 16 (t / 4) + 4 (t % 4).
+//   INT4 weight scales: [N/4][4 ceil(steps/4)][4 rows][2 groups] fp16, so a
+//     4-row block holds 64 contiguous bytes per 4 steps.
 //   Down factor: bf16 hi/lo split of diag(1/lambda) L1', ordered
 //     [step][hi/lo][s][n-tile][lane][8] with k = 128 step + 32 (lane/16) + 8 s + i.
 //   Up factor: L2'^T, [N][rpad] bf16, rpad = rank rounded up to 32.
@@ -185,7 +187,7 @@ __global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __res
         if (half == 0) {
           uint16_t sb;
           __builtin_memcpy(&sb, &s16, 2);
-          reinterpret_cast<uint16_t*>(xs)[(size_t)row * (K / 64) + 2 * t + G] = sb;
+          *reinterpret_cast<uint16_t*>(xs + (size_t)row * ks4 * 16 + (size_t)(t >> 2) * 16 + (t & 3) * 4 + 2 * G) = sb;
         }
       }
     }
@@ -226,221 +228,12 @@ __global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __res
 
 // ----------------------------------------------------------------- K-B
 
-constexpr int BM = 128, BN = 128;          // tile: tokens x out-features
-constexpr int LDS_TILE = (BM + BN) * 64;   // one step of both operands, bytes
-
 // swizzled byte offset of 16-byte chunk c of row r inside a [rows][64 B] tile.
 // A fragment read has 16 consecutive rows at one chunk; with f(r) =
 // ((r >> 1) ^ (r >> 3)) & 3 any 8 consecutive rows hit 8 distinct 16-byte
 // slots of a 128-byte bank line and any 16 rows 16 slots of 256 bytes.
 __device__ __forceinline__ int swz_f(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 __device__ __forceinline__ int swz(int r, int c) { return r * 64 + 16 * (c ^ swz_f(r)); }
-
-template <int FMT, int NTR>
-__global__ __launch_bounds__(256) void kb_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
-                                                 const float* __restrict__ zp, int zsplit,
-                                                 const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws,
-                                                 const uint16_t* __restrict__ l2k, const uint16_t* __restrict__ bias,
-                                                 uint16_t* __restrict__ Y, int M, int N, int K, int rpad) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * LDS_TILE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int l16 = lane & 15, g = lane >> 4;
-  const int tile_n = blockIdx.x * BN, tile_m = blockIdx.y * BM;
-  const int steps = K / 128;
-  const size_t rowbytes = (size_t)K / 2;
-
-  v4f acc[4][4];   // [n-tile][m-tile]
-
-  // ---- bias and low-rank up projection initialise the accumulators
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int n0 = tile_n + 64 * wn + 16 * nt + 4 * g;   // this lane's 4 output rows n
-    float bv[4] = {0.f, 0.f, 0.f, 0.f};
-    if (bias != nullptr) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int n = n0 + i < N ? n0 + i : N - 1;
-        bv[i] = __uint_as_float((uint32_t)bias[n] << 16);
-      }
-    }
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[nt][mt] = (v4f){bv[0], bv[1], bv[2], bv[3]};
-  }
-  if constexpr (NTR > 0) {
-#pragma unroll
-    for (int u = 0; u < NTR; ++u) {
-      v8bf af[4], bh[4], bl[4];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        int n = tile_n + 64 * wn + 16 * nt + l16;
-        n = n < N ? n : N - 1;
-        af[nt] = *reinterpret_cast<const v8bf*>(l2k + (size_t)n * rpad + 32 * u + 8 * g);
-      }
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        int m = tile_m + 64 * wm + 16 * mt + l16;
-        m = m < M ? m : M - 1;
-        float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int p = 0; p < zsplit; ++p) {
-          const float* src = zp + ((size_t)p * M + m) * rpad + 32 * u + 8 * g;
-          const v4f z0 = *reinterpret_cast<const v4f*>(src), z1 = *reinterpret_cast<const v4f*>(src + 4);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) { z[i] += z0[i]; z[4 + i] += z1[i]; }
-        }
-        uint16_t hi[8], lo[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t hb = bf16_rne(z[i]);
-          hi[i] = (uint16_t)hb;
-          lo[i] = (uint16_t)bf16_rne(z[i] - __uint_as_float(hb << 16));
-        }
-        bh[mt] = __builtin_bit_cast(v8bf, *reinterpret_cast<v4i*>(hi));
-        bl[mt] = __builtin_bit_cast(v8bf, *reinterpret_cast<v4i*>(lo));
-      }
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[nt], bh[mt], acc[nt][mt], 0, 0, 0);
-          acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[nt], bl[mt], acc[nt][mt], 0, 0, 0);
-        }
-    }
-  }
-
-  // ---- global -> LDS staging: thread tid moves 16 B of 2 rows of each operand
-  const int ld_row = tid >> 2, ld_chunk = tid & 3;
-  int xrow[2], wrow[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int m = tile_m + ld_row + 64 * j, n = tile_n + ld_row + 64 * j;
-    xrow[j] = m < M ? m : M - 1;
-    wrow[j] = n < N ? n : N - 1;
-  }
-  v4i stage[4];
-  auto gload = [&](int t) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      stage[j] = *reinterpret_cast<const v4i*>(xq + (size_t)xrow[j] * rowbytes + (size_t)t * 64 + 16 * ld_chunk);
-      stage[2 + j] = *reinterpret_cast<const v4i*>(wq + (size_t)wrow[j] * rowbytes + (size_t)t * 64 + 16 * ld_chunk);
-    }
-  };
-  auto lstore = [&](int buf) {
-    uint8_t* base = lds + buf * LDS_TILE;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      *reinterpret_cast<v4i*>(base + swz(ld_row + 64 * j, ld_chunk)) = stage[j];
-      *reinterpret_cast<v4i*>(base + BM * 64 + swz(ld_row + 64 * j, ld_chunk)) = stage[2 + j];
-    }
-  };
-
-  // per-lane operand rows (for scales)
-  int arow[4], brow[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int n = tile_n + 64 * wn + 16 * q + l16, m = tile_m + 64 * wm + 16 * q + l16;
-    arow[q] = n < N ? n : N - 1;
-    brow[q] = m < M ? m : M - 1;
-  }
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int t = 0; t < steps; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < steps) gload(t + 1);
-    const uint8_t* base = lds + buf * LDS_TILE;
-    v4i af[4], bf[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      af[q] = *reinterpret_cast<const v4i*>(base + BM * 64 + swz(64 * wn + 16 * q + l16, g));
-      bf[q] = *reinterpret_cast<const v4i*>(base + swz(64 * wm + 16 * q + l16, g));
-    }
-    if constexpr (FMT == SVDQ_MXFP4_G32) {
-      const int ks4 = (steps + 3) / 4;
-      const size_t soff = (size_t)(t >> 2) * 16 + 4 * g;
-      const int sh = 8 * (t & 3);
-      int asc[4], bsc[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        asc[q] = (int)((*reinterpret_cast<const uint32_t*>(ws + (size_t)arow[q] * ks4 * 16 + soff)) >> sh);
-        bsc[q] = (int)((*reinterpret_cast<const uint32_t*>(xs + (size_t)brow[q] * ks4 * 16 + soff)) >> sh);
-      }
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const v8i a = (v8i){af[nt][0], af[nt][1], af[nt][2], af[nt][3], 0, 0, 0, 0};
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          const v8i b = (v8i){bf[mt][0], bf[mt][1], bf[mt][2], bf[mt][3], 0, 0, 0, 0};
-          acc[nt][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[nt][mt], 4, 4, 0, asc[nt], 0,
-                                                                        bsc[mt]);
-        }
-      }
-    } else {
-      // INT4 on int8 MFMA: nibble q -> byte 16 q (products carry 2^8, folded
-      // into the scale product); one MFMA per 64-element group, then
-      // acc += float(I) * sw * sx.
-      float sw[4][4][2], sx[4][2];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        int n0 = tile_n + 64 * wn + 16 * nt + 4 * g;
-        n0 = n0 < N ? n0 : N - 4;
-        const v4i v = *reinterpret_cast<const v4i*>(ws + (((size_t)(n0 >> 2)) * steps + t) * 16);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t w = (uint32_t)v[i];
-          sw[nt][i][0] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFF));
-          sw[nt][i][1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-        }
-      }
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(xs + ((size_t)brow[mt] * (K / 64) + 2 * t) * 2);
-        sx[mt][0] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFF)) * (1.0f / 256.0f);
-        sx[mt][1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)) * (1.0f / 256.0f);
-      }
-      const uint32_t MSK = 0xF0F0F0F0u;
-#pragma unroll
-      for (int G = 0; G < 2; ++G) {
-        v4i a8[4], b8[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t a0 = (uint32_t)af[q][2 * G], a1 = (uint32_t)af[q][2 * G + 1];
-          const uint32_t b0 = (uint32_t)bf[q][2 * G], b1 = (uint32_t)bf[q][2 * G + 1];
-          a8[q] = (v4i){(int)((a0 << 4) & MSK), (int)(a0 & MSK), (int)((a1 << 4) & MSK), (int)(a1 & MSK)};
-          b8[q] = (v4i){(int)((b0 << 4) & MSK), (int)(b0 & MSK), (int)((b1 << 4) & MSK), (int)(b1 & MSK)};
-        }
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt) {
-            const v4i I = __builtin_amdgcn_mfma_i32_16x16x64_i8(a8[nt], b8[mt], (v4i){0, 0, 0, 0}, 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              acc[nt][mt][i] = __builtin_fmaf((float)I[i], sw[nt][i][G] * sx[mt][G], acc[nt][mt][i]);
-          }
-      }
-    }
-    if (t + 1 < steps) lstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  // ---- single bf16 store: lane owns Y[m][n0 .. n0 + 3]
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const int m = tile_m + 64 * wm + 16 * mt + l16;
-    if (m >= M) continue;
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int n0 = tile_n + 64 * wn + 16 * nt + 4 * g;
-      if (n0 >= N) continue;
-      const uint32_t lo = bf16_rne(acc[nt][mt][0]) | (bf16_rne(acc[nt][mt][1]) << 16);
-      const uint32_t hi = bf16_rne(acc[nt][mt][2]) | (bf16_rne(acc[nt][mt][3]) << 16);
-      *reinterpret_cast<uint2*>(Y + (size_t)m * N + n0) = make_uint2(lo, hi);
-    }
-  }
-}
 
 // ----------------------------------------------------- K-B, MXFP4, large tile
 //
@@ -803,6 +596,290 @@ __global__ __launch_bounds__(MX_THREADS, 1) void kb_mx_kernel(
   }
 }
 
+// ------------------------------------------------------ K-B, INT4, large tile
+//
+// 256 (tokens) x 128 (out-features) per block of 8 waves, two per SIMD; wave
+// w owns tokens 64 (w & 3) .. +64 and out-features 64 (w >> 2) .. +64, i.e.
+// 4 x 4 MFMA tiles of 16 x 16 (64 fp32 accumulators per lane).  Codes travel
+// global -> LDS by direct-to-LDS loads into a ring of four 24 KB step
+// buffers, three steps ahead; the scale records of 4 steps (token rows: one
+// dword per step; weights: 4 rows x one dword per step, 64 bytes per 4-row
+// block) are double buffered the same way.
+//
+// Each 16-byte fragment holds 16 codes of each of the step's two 64-element
+// groups.  Nibbles become bytes 16 q, the int8 MFMA operand, so one MFMA per
+// group gives 2^8 times the exact integer dot product I; the accumulator
+// takes float(I) * (sx * sw), the fp16 scale product formed exactly in fp32,
+// and the 2^8 is removed once after the K loop.  The weight fragments of the
+// next step are read while the current ones (unpacked at the top of the
+// step) feed the MFMAs; token fragments stream two MFMA groups ahead.
+//
+// Chunk 0 of Z and L2' is fetched into its own LDS region at the start, so
+// the K loop carries no prefetch logic; weight rows are permuted inside tile
+// pairs as in the MXFP4 kernel for 16-byte stores.
+
+constexpr int I4_BM = 256, I4_BN = 128, I4_THREADS = 512;
+constexpr int I4_STEP_BYTES = (I4_BM + I4_BN) * 64;   // codes of one step, both operands
+constexpr int I4_NBUF = 4;
+constexpr int I4_SC_BYTES = (I4_BM + I4_BN) * 16;     // scale records of one 4-step group
+constexpr int I4_SC0 = I4_NBUF * I4_STEP_BYTES;
+constexpr int I4_Z0 = I4_SC0 + 2 * I4_SC_BYTES;       // Z chunk: 256 rows x 32 fp32
+constexpr int I4_L20 = I4_Z0 + I4_BM * 128;           // L2' chunk: 128 rows x 32 bf16
+constexpr int I4_LDS = I4_L20 + I4_BN * 64;
+
+__device__ __forceinline__ float f16_half(uint32_t w, int hi) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(hi ? (w >> 16) : (w & 0xFFFFu)));
+}
+
+// int8 MFMA operand of group G from a 16-byte INT4 fragment: bytes 16 q
+__device__ __forceinline__ v4i i4_unpack(const v4i f, int G) {
+  const uint32_t MSK = 0xF0F0F0F0u;
+  const uint32_t d0 = (uint32_t)f[2 * G], d1 = (uint32_t)f[2 * G + 1];
+  return (v4i){(int)((d0 << 4) & MSK), (int)(d0 & MSK), (int)((d1 << 4) & MSK), (int)(d1 & MSK)};
+}
+
+template <int NTR>
+__global__ __launch_bounds__(I4_THREADS, 1) void kb_i4_kernel(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const float* __restrict__ zp,
+    const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws, const uint16_t* __restrict__ l2k,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int M, int N, int K, int rpad) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[I4_LDS];
+  const uint32_t lds_u32 = (uint32_t)(size_t)(SVDQ_AS3 uint8_t*)lds;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 3, wn = wave >> 2;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int tiles_m = (M + I4_BM - 1) / I4_BM, tiles_n = (N + I4_BN - 1) / I4_BN;
+  int tm, tn;
+  mx_tile_of(blockIdx.x, tiles_m, tiles_n, &tm, &tn);
+  const int tile_m = tm * I4_BM, tile_n = tn * I4_BN;
+  const int steps = K / 128;
+  const int ks4 = (steps + 3) / 4;
+  const uint32_t rowbytes = (uint32_t)K / 2;
+  const int m_base = tile_m + 64 * wm, n_base = tile_n + 64 * wn;
+
+  // ---- DMA plan.  Codes: 24 units of 1 KB per step (units 0-15: 16 token
+  // rows each, 16-23: 16 weight rows each); wave w moves units 3w .. 3w+2,
+  // lane i filling 16-byte slot p = 64 (unit within its operand) + i, i.e.
+  // row p / 4 at swizzled chunk position p mod 4.
+  const uint8_t* cbase[3];
+  uint32_t coff[3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int u = 3 * wave + j;
+    const bool tok = u < 16;
+    const int p = 64 * (tok ? u : u - 16) + lane, r = p >> 2, c = (p & 3) ^ swz_f(r);
+    const int row = tok ? min(tile_m + r, M - 1) : min(tile_n + r, N - 1);
+    cbase[j] = tok ? xq : wq;
+    coff[j] = (uint32_t)row * rowbytes + 16u * c;
+  }
+  // Scales of 4-step group grp: waves 0-3 move token rows 64 w + lane (16
+  // bytes each), waves 4-5 the 128 16-byte pieces of the 32 weight blocks.
+  const uint8_t* sbase = wave < 4 ? xs : ws;
+  uint32_t soff, sstride;
+  if (wave < 4) {
+    soff = (uint32_t)min(tile_m + 64 * wave + lane, M - 1) * (uint32_t)(ks4 * 16);
+    sstride = 16;
+  } else {
+    const int c = 64 * (wave - 4) + lane;
+    const int blk = min(tile_n / 4 + (c >> 2), N / 4 - 1);
+    soff = ((uint32_t)blk * (uint32_t)(4 * ks4) + (uint32_t)(c & 3)) * 16u;
+    sstride = 64;
+  }
+  auto issue_codes = [&](int t) __attribute__((always_inline)) {
+    const uint32_t b = lds_u32 + (uint32_t)(t % I4_NBUF) * I4_STEP_BYTES + (uint32_t)wave * 3072u;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) dma16(cbase[j] + (size_t)t * 64, coff[j], b + 1024u * j);
+  };
+  auto issue_scales = [&](int grp) __attribute__((always_inline)) {
+    if (wave < 6)
+      dma16(sbase + (size_t)grp * sstride, soff,
+            lds_u32 + I4_SC0 + (uint32_t)(grp & 1) * I4_SC_BYTES + (uint32_t)wave * 1024u);
+  };
+  // Z (256 rows x 128 B, 32 units of 8 rows) and L2' (128 rows x 64 B, 8
+  // units of 16 rows) chunk u into their LDS regions
+  auto issue_lowrank = [&](int u) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int unit = 4 * wave + j, row = 8 * unit + (lane >> 3);
+      const int m = min(tile_m + row, M - 1);
+      dma16(reinterpret_cast<const uint8_t*>(zp), ((uint32_t)m * (uint32_t)rpad + 32u * u) * 4u + 16u * (lane & 7),
+            lds_u32 + I4_Z0 + 1024u * unit);
+    }
+    const int row = 16 * wave + (lane >> 2);
+    const int n = min(tile_n + row, N - 1);
+    dma16(reinterpret_cast<const uint8_t*>(l2k), ((uint32_t)n * (uint32_t)rpad + 32u * u) * 2u + 16u * (lane & 3),
+          lds_u32 + I4_L20 + 1024u * wave);
+  };
+
+  // fragment addresses inside a step buffer: token fragment q reads row
+  // 64 wm + 16 q + l16 (the swizzle repeats every 32 rows), weight fragment
+  // nt the permuted row 64 wn + mx_nrow(nt, l16)
+  uint32_t boff[2], aoff[4];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) boff[par] = (uint32_t)swz(64 * wm + 16 * par + l16, g) - 1024u * par;
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) aoff[nt] = (uint32_t)(I4_BM * 64 + swz(64 * wn + mx_nrow(nt, l16), g));
+  auto buf_of = [&](int t) __attribute__((always_inline)) -> uint32_t {
+    uint32_t bo = (uint32_t)(t % I4_NBUF) * I4_STEP_BYTES;
+    asm volatile("" : "+s"(bo));
+    return bo;
+  };
+  auto read_b = [&](uint32_t bo, int q) __attribute__((always_inline)) -> v4i {
+    return *reinterpret_cast<const v4i*>(lds + bo + boff[q & 1] + 1024 * q);
+  };
+  auto read_a = [&](uint32_t bo, int nt) __attribute__((always_inline)) -> v4i {
+    return *reinterpret_cast<const v4i*>(lds + bo + aoff[nt]);
+  };
+  // scales of step t: token row dword (groups 2t, 2t+1) per mt; 4 weight
+  // rows x dword per nt (the lane's 4 consecutive out-features)
+  uint32_t sx[4];
+  v4i sw[4];
+  auto read_scales = [&](int t) __attribute__((always_inline)) {
+    uint32_t so = (uint32_t)(I4_SC0 + ((t >> 2) & 1) * I4_SC_BYTES);
+    asm volatile("" : "+s"(so));
+    const uint8_t* sc = lds + so;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+      sx[mt] = *reinterpret_cast<const uint32_t*>(sc + (64 * wm + 16 * mt + l16) * 16 + 4 * (t & 3));
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int blk = 16 * wn + 8 * (nt >> 1) + 2 * g + (nt & 1);
+      sw[nt] = *reinterpret_cast<const v4i*>(sc + I4_BM * 16 + blk * 64 + 16 * (t & 3));
+    }
+  };
+  auto wait_for = [&](int s) __attribute__((always_inline)) {
+    if (s + 1 < steps)
+      asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  if constexpr (NTR > 0) issue_lowrank(0);
+  issue_scales(0);
+#pragma unroll
+  for (int s0 = 0; s0 < 3; ++s0)
+    if (s0 < steps) issue_codes(s0);
+
+  v4f acc[4][4];   // [weight tile][token tile]
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[nt][mt] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  v4i wp[4];   // packed weight fragments (the next step's, once read)
+  v4i tk[4];   // packed token fragments; fragment q sits in slot q
+  wait_for(0);
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) wp[nt] = read_a(0, nt);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) tk[q] = read_b(0, q);
+
+  for (int t = 0; t < steps; ++t) {
+    // the barrier publishes step t+1's buffer; the buffer of step t-1 (all
+    // waves are past it) receives step t+3.  The last step also reads the
+    // next buffer; those reads stay inside LDS and are never used.
+    wait_for(t + 1);
+    if ((t & 3) == 0 && (t >> 2) + 1 < ks4) issue_scales((t >> 2) + 1);
+    if (t + 3 < steps) issue_codes(t + 3);
+    read_scales(t);
+    const uint32_t bc = buf_of(t), bn = buf_of(t + 1);
+    v4i wu[4][2];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      wu[nt][0] = i4_unpack(wp[nt], 0);
+      wu[nt][1] = i4_unpack(wp[nt], 1);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      wp[mt] = read_a(bn, mt);
+      tk[(mt + 2) & 3] = mt + 2 < 4 ? read_b(bc, mt + 2) : read_b(bn, mt - 2);
+#pragma unroll
+      for (int G = 0; G < 2; ++G) {
+        const v4i b8 = i4_unpack(tk[mt], G);
+        const float sxg = f16_half(sx[mt], G);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const v4i I = __builtin_amdgcn_mfma_i32_16x16x64_i8(wu[nt][G], b8, (v4i){0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[nt][mt][i] = __builtin_fmaf((float)I[i], sxg * f16_half((uint32_t)sw[nt][i], G), acc[nt][mt][i]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[nt][mt][i] *= 1.0f / 256.0f;
+
+  // ---- low-rank up projection and bias, then one 16-byte store per pair
+  if constexpr (NTR > 0) {
+    for (int u = 0; u < NTR; ++u) {
+      if (u > 0) {
+        __syncthreads();   // every wave is done with chunk u-1
+        issue_lowrank(u);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      v8bf bh[4], bl[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const float* zr = reinterpret_cast<const float*>(lds + I4_Z0 + (64 * wm + 16 * mt + l16) * 128 + 32 * g);
+        uint16_t hi[8], lo[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float z = zr[i];
+          const uint32_t hb = bf16_rne(z);
+          hi[i] = (uint16_t)hb;
+          lo[i] = (uint16_t)bf16_rne(z - __uint_as_float(hb << 16));
+        }
+        bh[mt] = __builtin_bit_cast(v8bf, *reinterpret_cast<v4i*>(hi));
+        bl[mt] = __builtin_bit_cast(v8bf, *reinterpret_cast<v4i*>(lo));
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const v8bf af = *reinterpret_cast<const v8bf*>(lds + I4_L20 + (64 * wn + mx_nrow(nt, l16)) * 64 + 16 * g);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bh[mt], acc[nt][mt], 0, 0, 0);
+          acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bl[mt], acc[nt][mt], 0, 0, 0);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int p2 = 0; p2 < 2; ++p2) {
+    const int n0 = n_base + 32 * p2 + 8 * g;
+    float bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (bias != nullptr && n0 < N) {
+      const v4i braw = *reinterpret_cast<const v4i*>(bias + n0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        bv[2 * i] = bf16_lo((uint32_t)braw[i]);
+        bv[2 * i + 1] = bf16_hi((uint32_t)braw[i]);
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int m = m_base + 16 * mt + l16;
+      if (m >= M || n0 >= N) continue;
+      v4i o;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        o[i] = (int)(bf16_rne(acc[2 * p2][mt][2 * i] + bv[2 * i]) |
+                     (bf16_rne(acc[2 * p2][mt][2 * i + 1] + bv[2 * i + 1]) << 16));
+        o[2 + i] = (int)(bf16_rne(acc[2 * p2 + 1][mt][2 * i] + bv[4 + 2 * i]) |
+                         (bf16_rne(acc[2 * p2 + 1][mt][2 * i + 1] + bv[4 + 2 * i + 1]) << 16));
+      }
+      *reinterpret_cast<v4i*>(Y + (size_t)m * N + n0) = o;
+    }
+  }
+}
+
 // ------------------------------------------------------------ dispatch
 
 template <int FMT>
@@ -857,18 +934,22 @@ static hipError_t launch_kb(const svdq_layer& L, const uint8_t* ws, const svdq_w
     }
     return hipGetLastError();
   }
-  dim3 grid((L.N + BN - 1) / BN, (M + BM - 1) / BM), block(256);
+  const int tiles = ((M + I4_BM - 1) / I4_BM) * ((L.N + I4_BN - 1) / I4_BN);
   const uint8_t* xq = ws + W.xq_off;
   const uint8_t* xs = ws + W.xs_off;
   const float* zp = reinterpret_cast<const float*>(ws + W.z_off);
+#define SVDQ_KB_I4(R)                                                                                          \
+  hipLaunchKernelGGL((kb_i4_kernel<R>), dim3(tiles), dim3(I4_THREADS), 0, st, xq, xs, zp, L.wq, L.ws, L.l2k, \
+                     L.bias, Y, M, L.N, L.K, rp)
   switch (rp / 32) {
-    case 0: hipLaunchKernelGGL((kb_kernel<FMT, 0>), grid, block, 0, st, xq, xs, zp, W.zsplit, L.wq, L.ws, L.l2k, L.bias, Y, M, L.N, L.K, rp); break;
-    case 1: hipLaunchKernelGGL((kb_kernel<FMT, 1>), grid, block, 0, st, xq, xs, zp, W.zsplit, L.wq, L.ws, L.l2k, L.bias, Y, M, L.N, L.K, rp); break;
-    case 2: hipLaunchKernelGGL((kb_kernel<FMT, 2>), grid, block, 0, st, xq, xs, zp, W.zsplit, L.wq, L.ws, L.l2k, L.bias, Y, M, L.N, L.K, rp); break;
-    case 3: hipLaunchKernelGGL((kb_kernel<FMT, 3>), grid, block, 0, st, xq, xs, zp, W.zsplit, L.wq, L.ws, L.l2k, L.bias, Y, M, L.N, L.K, rp); break;
-    case 4: hipLaunchKernelGGL((kb_kernel<FMT, 4>), grid, block, 0, st, xq, xs, zp, W.zsplit, L.wq, L.ws, L.l2k, L.bias, Y, M, L.N, L.K, rp); break;
+    case 0: SVDQ_KB_I4(0); break;
+    case 1: SVDQ_KB_I4(1); break;
+    case 2: SVDQ_KB_I4(2); break;
+    case 3: SVDQ_KB_I4(3); break;
+    case 4: SVDQ_KB_I4(4); break;
     default: return hipErrorInvalidValue;
   }
+#undef SVDQ_KB_I4
   return hipGetLastError();
 }
 

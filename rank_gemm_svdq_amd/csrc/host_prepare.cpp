@@ -31,7 +31,7 @@ bool geometry(int32_t K, int32_t N, int32_t rank, int32_t fmt, Geometry* g) {
   g->steps = K / kStep;
   g->ks4 = (g->steps + 3) / 4;
   g->wq_bytes = (size_t)N * K / 2;
-  g->ws_bytes = fmt == SVDQ_INT4_G64 ? (size_t)N * (K / 64) * 2 : (size_t)N * g->ks4 * 16;
+  g->ws_bytes = (size_t)N * g->ks4 * 16;   // INT4: [N/4][4 ks4][4][2] fp16; MXFP4: [N][ks4 * 16] bytes
   g->l1k_bytes = (size_t)K * g->rpad * 2 * 2;
   g->l2k_bytes = (size_t)N * g->rpad * 2;
   return true;
@@ -225,7 +225,7 @@ svdq_status svdq_workspace_layout(int32_t M, int32_t K, int32_t rank, int32_t fm
   out->xq_off = 0;
   out->xq_bytes = (size_t)M * K / 2;
   out->xs_off = align256(out->xq_bytes);
-  out->xs_bytes = fmt == SVDQ_INT4_G64 ? (size_t)M * (K / 64) * 2 : (size_t)M * ks4 * 16;
+  out->xs_bytes = (size_t)M * ks4 * 16;
   out->z_off = align256(out->xs_off + out->xs_bytes);
   out->z_bytes = rank > 0 ? (size_t)out->zsplit * M * rank_pad(rank) * 4 : 0;
   out->total = align256(out->z_off + out->z_bytes);
@@ -415,13 +415,15 @@ svdq_status svdq_kernel_layout(int32_t K, int32_t N, int32_t rank, int32_t fmt, 
       for (int32_t b = 0; b < K / 32; ++b) dst[mx_scale_index(b)] = ws[(size_t)n * (K / 32) + b];
     }
   } else {
-    // [N/4][steps][4 rows][2 groups] fp16
+    // [N/4][4 ks4 steps][4 rows][2 groups] fp16, steps past K zero
     const uint16_t* s = reinterpret_cast<const uint16_t*>(ws);
     uint16_t* d = reinterpret_cast<uint16_t*>(ws_k);
+    const int32_t sp = 4 * g.ks4;
+    std::memset(ws_k, 0, g.ws_bytes);
     for (int32_t n = 0; n < N; ++n)
       for (int32_t t = 0; t < steps; ++t)
         for (int G = 0; G < 2; ++G)
-          d[((size_t)(n / 4) * steps + t) * 8 + (n % 4) * 2 + G] = s[(size_t)n * (K / 64) + 2 * t + G];
+          d[((size_t)(n / 4) * sp + t) * 8 + (n % 4) * 2 + G] = s[(size_t)n * (K / 64) + 2 * t + G];
   }
   if (rank == 0) return SVDQ_OK;
   // down factor: hi/lo bf16 split of diag(smooth_inv) L1', order
@@ -483,7 +485,12 @@ svdq_status svdq_unpack_activations(const void* ws_host, int32_t M, int32_t K, i
     for (int32_t m = 0; m < M; ++m)
       for (int32_t b = 0; b < K / 32; ++b) xs[(size_t)m * (K / 32) + b] = s[(size_t)m * ks4 * 16 + mx_scale_index(b)];
   } else {
-    std::memcpy(xs, s, (size_t)M * (K / 64) * 2);
+    uint16_t* xs16 = reinterpret_cast<uint16_t*>(xs);
+    for (int32_t m = 0; m < M; ++m)
+      for (int32_t t = 0; t < steps; ++t)
+        for (int G = 0; G < 2; ++G)
+          std::memcpy(xs16 + (size_t)m * (K / 64) + 2 * t + G,
+                      s + (size_t)m * ks4 * 16 + (size_t)(t >> 2) * 16 + (t & 3) * 4 + 2 * G, 2);
   }
   if (z && rank > 0) {
     const int32_t rp = rank_pad(rank);

@@ -178,6 +178,7 @@ def test_workspace_layout_regions():
         w = B.workspace_layout(M, K, r, f)
         assert w["xq_off"] % 256 == 0 and w["xs_off"] % 256 == 0 and w["z_off"] % 256 == 0
         assert w["xq_bytes"] == M * K // 2
+        assert w["xs_bytes"] == M * ((K // 128 + 3) // 4) * 16
         assert w["xs_off"] >= w["xq_off"] + w["xq_bytes"] and w["z_off"] >= w["xs_off"] + w["xs_bytes"]
         assert w["total"] >= w["z_off"] + w["z_bytes"]
         if r:
@@ -201,8 +202,10 @@ def test_int4_kernel_layout_positions():
             G, g, j = kk // 64, (kk % 64) // 16, kk % 16
             byte = wk[n, 64 * t + 16 * g + 8 * G + j // 2]
             assert (byte >> (4 * (j % 2))) & 0xF == nib[n, k]
-    ws = kl["ws_k"].view(np.uint16).reshape(N // 4, K // 128, 4, 2)
-    assert np.all(ws == np.float16(1).view(np.uint16))
+    steps = K // 128
+    ws = kl["ws_k"].view(np.uint16).reshape(N // 4, (steps + 3) // 4 * 4, 4, 2)
+    assert np.all(ws[:, :steps] == np.float16(1).view(np.uint16))
+    assert np.all(ws[:, steps:] == 0)
 
 
 def test_mxfp4_scale_layout_positions():
