@@ -86,19 +86,35 @@ typedef struct svdq_sizes {
 } svdq_sizes;
 
 /* Byte sizes of the kernel-layout and canonical buffers of a layer.
- * Errors: SVDQ_ERR_ARG (out NULL), SVDQ_ERR_SHAPE, SVDQ_ERR_UNSUPPORTED (fmt). */
+ * Errors: SVDQ_ERR_ARG (out NULL), SVDQ_ERR_SHAPE, SVDQ_ERR_UNSUPPORTED (fmt).
+ *
+ * Kernel layouts (K in steps of 128 elements = 64 code bytes per row; the
+ * byte order of a row-step is canonical for MXFP4, and for INT4 element k
+ * of the step sits at byte 16 ((k % 64) / 16) + 8 (k / 64) + (k % 16) / 2,
+ * nibble k % 2):
+ *   codes   1 KB units of 16 rows x one step, ordered [row / 16][step];
+ *           16-byte slot 4 (row % 16) + q of a unit holds chunk
+ *           q ^ (((r >> 1) ^ (r >> 3)) & 3) of the row-step, r = row % 32;
+ *           rows are padded to a multiple of 16
+ *   scale records (MXFP4 weights and both formats' activations): 16 bytes
+ *           per row and 4 steps, in 1 KB units of 64 rows ordered
+ *           [row / 64][4-step group], record bytes at (row % 64) * 16;
+ *           MXFP4: block b = 4t + g (32 elements) at record byte 4 g + t % 4;
+ *           INT4: the fp16 scales of step t (groups 2t, 2t+1) at record
+ *           bytes 4 (t % 4) and 4 (t % 4) + 2
+ *   INT4 weight scales: 2 KB units of 128 rows x 4 steps ordered
+ *           [row / 128][4-step group]; inside a unit fp16 index
+ *           32 ((row % 128) / 4) + 8 (t % 4) + 2 (row % 4) + (group of the step)
+ * Padding rows, steps and records hold zero codes, scale 127 (MXFP4) or 0 (INT4). */
 svdq_status svdq_layer_sizes(int32_t K, int32_t N, int32_t rank, int32_t fmt, svdq_sizes* out);
 
 /* --------------------------- workspace ------------------------------- */
 
 /* Per-call device workspace.  Regions, each 256-byte aligned:
- *   xq   activation codes [M, K/2], two 4-bit codes per byte (MXFP4:
- *        canonical order; INT4: the bytes of each 128-element step permuted
- *        as for the weight codes)
- *   xs   activation scales, one 16-byte record per row and 4 K steps of
- *        128 (M * ceil(K/512) * 16 bytes): MXFP4 E8M0 bytes in the permuted
- *        per-row layout of the weight scales; INT4 the fp16 pair of step t
- *        (groups 2t, 2t+1) in the dword at byte 16 (t / 4) + 4 (t % 4)
+ *   xq   activation codes in the codes layout above (rows padded to 16;
+ *        ceil(M/16) * 16 * K/2 bytes; padding rows are not written)
+ *   xs   activation scale records in the scale-record layout above
+ *        (ceil(M/64) * 64 * ceil(K/512) * 16 bytes)
  *   z    down projection Z, fp32 [zsplit][M][rank rounded up to 32]; zsplit
  *        is 1 in this version (partial sums are reduced inside K-A)
  * svdq_unpack_activations() turns a host copy into canonical form. */

@@ -159,9 +159,8 @@ __global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __res
         }
       }
       if (live) {
-        *reinterpret_cast<v4i*>(xq + (size_t)row * (K / 2) + (size_t)t * 64 + 16 * g) = packed;
-        const int b = 4 * t + g;
-        xs[(size_t)row * ks4 * 16 + (size_t)(b >> 4) * 16 + (b & 3) * 4 + ((b >> 2) & 3)] = (uint8_t)(e + 127);
+        *reinterpret_cast<v4i*>(xq + code_offset(row, t, 16 * g, steps)) = packed;
+        xs[scale_record_offset(row, t >> 2, 4 * g + (t & 3), ks4)] = (uint8_t)(e + 127);
       }
     } else {
       // INT4: the 64-element group spans lane groups g and g ^ 1
@@ -180,14 +179,15 @@ __global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __res
         }
       }
       if (live) {
+        // bytes 32 half + 8 G + (0..7) and the same + 16 of the step (the
+        // INT4 step permutation), each inside one 16-byte chunk
         const int G = g >> 1, half = g & 1;
-        uint8_t* base = xq + (size_t)row * (K / 2) + (size_t)t * 64 + 32 * half + 8 * G;
-        *reinterpret_cast<uint2*>(base) = make_uint2(d[0], d[1]);
-        *reinterpret_cast<uint2*>(base + 16) = make_uint2(d[2], d[3]);
+        *reinterpret_cast<uint2*>(xq + code_offset(row, t, 32 * half + 8 * G, steps)) = make_uint2(d[0], d[1]);
+        *reinterpret_cast<uint2*>(xq + code_offset(row, t, 32 * half + 16 + 8 * G, steps)) = make_uint2(d[2], d[3]);
         if (half == 0) {
           uint16_t sb;
           __builtin_memcpy(&sb, &s16, 2);
-          *reinterpret_cast<uint16_t*>(xs + (size_t)row * ks4 * 16 + (size_t)(t >> 2) * 16 + (t & 3) * 4 + 2 * G) = sb;
+          *reinterpret_cast<uint16_t*>(xs + scale_record_offset(row, t >> 2, 4 * (t & 3) + 2 * G, ks4)) = sb;
         }
       }
     }
@@ -259,11 +259,15 @@ __device__ __forceinline__ int swz(int r, int c) { return r * 64 + 16 * (c ^ swz
 // the 4 + 4 accumulators a lane holds for the pair are 8 consecutive
 // out-features of one token: one 16-byte store.
 
-constexpr int MX_BM = 256, MX_BN = 256, MX_THREADS = 512;
+constexpr int MX_BM = 256, MX_BN = 256;
+#ifndef SVDQ_MX_WAVES
+#define SVDQ_MX_WAVES 8
+#endif
 constexpr int MX_STEP_BYTES = (MX_BM + MX_BN) * 64;   // codes of one step, both operands
 constexpr int MX_NBUF = 4;
 constexpr int MX_SC_BYTES = (MX_BM + MX_BN) * 16;     // scale dwords of one 4-step group
-constexpr int MX_LDS = MX_NBUF * MX_STEP_BYTES + 2 * MX_SC_BYTES;
+constexpr int MX_DUMMY = MX_NBUF * MX_STEP_BYTES + 2 * MX_SC_BYTES;   // 1 KB per wave, see below
+constexpr int MX_LDS = MX_DUMMY + 8 * 1024;
 
 #define SVDQ_AS3 __attribute__((address_space(3)))
 
@@ -285,24 +289,43 @@ __device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, uint3
 }
 
 // Blocks are dealt to the 8 XCDs round robin; give each XCD a contiguous run
-// of tile ids, and walk tile ids token-tile fastest so the blocks resident on
-// one XCD share out-feature columns of the weight in its L2.
+// of tile ids (a band of out-feature tiles, all token tiles), and order the
+// run in groups of 8 token tiles, out-feature tile slower, so the ~32 blocks
+// resident on one XCD at a time cover about 8 token x 4 out-feature tiles:
+// 12 operand panels share its L2 instead of 16 + 2.
 __device__ __forceinline__ void mx_tile_of(int b, int tiles_m, int tiles_n, int* tm, int* tn) {
   const int total = tiles_m * tiles_n;
-  const int per = total / 8;
   int id = b;
-  if (per * 8 == total) id = (b & 7) * per + (b >> 3);
-  *tm = id % tiles_m;
-  *tn = id / tiles_m;
+  if (total % 8 == 0) id = (b & 7) * (total / 8) + (b >> 3);
+  const int gm = 8;
+  const int full = tiles_m / gm * gm;             // token tiles in whole groups
+  const int span = gm * tiles_n;                  // ids per whole group
+  if (id < full * tiles_n) {
+    const int grp = id / span, r = id % span;
+    *tm = grp * gm + r % gm;
+    *tn = r / gm;
+  } else {                                        // the last, partial group
+    const int r = id - full * tiles_n, rem = tiles_m - full;
+    *tm = full + r % rem;
+    *tn = r / rem;
+  }
 }
+
+// LDS swizzles of the low-rank tiles read in the epilogues: Z rows are
+// 128 bytes (8 chunks of 16), L2'^T rows 64 bytes (4 chunks); chunk c of row
+// r sits at chunk position c ^ f(r), so the 8 lanes served together by a
+// 16-byte LDS read (consecutive, or pair-permuted, rows) hit 8 distinct
+// 16-byte slots of a 128-byte line.
+__device__ __forceinline__ int zswz(int r) { return r & 7; }
+__device__ __forceinline__ int lswz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 
 // out-feature (relative to the wave's 64) of MFMA row q of weight tile nt
 __device__ __forceinline__ int mx_nrow(int nt, int q) {
   return 32 * (nt >> 1) + 8 * (q >> 2) + 4 * (nt & 1) + (q & 3);
 }
 
-template <int NTR, bool ODD>
-__global__ __launch_bounds__(MX_THREADS, 1) void kb_mx_kernel(
+template <int NTR, bool ODD, int WAVES>
+__global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const float* __restrict__ zp, int zsplit,
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws, const uint16_t* __restrict__ l2k,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int M, int N, int K, int rpad) {
@@ -310,6 +333,10 @@ __global__ __launch_bounds__(MX_THREADS, 1) void kb_mx_kernel(
   const uint32_t lds_u32 = (uint32_t)(size_t)(SVDQ_AS3 uint8_t*)lds;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // WAVES = 8: waves own 128 tokens x 64 out-features; WAVES = 4: 128 x 128
+  constexpr int NTW = 32 / WAVES;        // 16-row weight tiles per wave
+  constexpr int UPW = 32 / WAVES;        // 1 KB code units per wave and step
+  constexpr int RPW = 8 / WAVES;         // 1 KB scale records per wave and 4 steps
   const int wm = wave & 1, wn = wave >> 1;
   const int l16 = lane & 15, g = lane >> 4;
   const int tiles_m = (M + MX_BM - 1) / MX_BM, tiles_n = (N + MX_BN - 1) / MX_BN;
@@ -318,47 +345,56 @@ __global__ __launch_bounds__(MX_THREADS, 1) void kb_mx_kernel(
   const int tile_m = tm * MX_BM, tile_n = tn * MX_BN;
   const int steps = K / 128;
   const int ks4 = (steps + 3) / 4;
-  const uint32_t rowbytes = (uint32_t)K / 2;
-  const int m_base = tile_m + 128 * wm, n_base = tile_n + 64 * wn;
+  const int m_base = tile_m + 128 * wm, n_base = tile_n + 16 * NTW * wn;
 
-  // ---- DMA plan.  Codes: wave w moves the 1 KB units 4w .. 4w+3 of a step
-  // buffer (units 0-15: 16 token rows each, units 16-31: 16 weight rows each);
-  // lane i fills 16-byte slot p = 64 (u mod 16) + i of its operand tile, i.e.
-  // row p / 4 at swizzled chunk position p mod 4.  Waves 0-3 move token rows,
-  // waves 4-7 weight rows; lane offsets are 32-bit (operands below 2 GiB,
-  // checked on the host).
-  const uint8_t* cbase = wave < 4 ? xq : wq;
-  uint32_t coff[4];
+  // ---- DMA plan.  Codes are stored in 1 KB units of 16 rows x one step, in
+  // the order the step buffers hold them (codes layout), so every load is
+  // one contiguous kilobyte: wave w moves units UPW w .. UPW w + UPW - 1 of
+  // a step buffer (units 0-15: token rows, 16-31: weight rows), lane i 16
+  // bytes.  Units past the last row group repeat it (their outputs are
+  // never stored).  Lane offsets are 32-bit (operands below 2 GiB, checked
+  // on the host).
+  const bool tokw = wave < WAVES / 2;
+  const uint8_t* cbase = tokw ? xq : wq;
+  const int gmax = tokw ? (M + 15) / 16 - 1 : N / 16 - 1;
+  const int g0 = (tokw ? tile_m : tile_n) >> 4;
+  uint32_t coff[UPW];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int u = 4 * wave + j;
-    const int p = 64 * (u & 15) + lane, r = p >> 2, c = (p & 3) ^ swz_f(r);
-    const int row = wave < 4 ? min(tile_m + r, M - 1) : min(tile_n + r, N - 1);
-    coff[j] = (uint32_t)row * rowbytes + 16u * c;
+  for (int j = 0; j < UPW; ++j) {
+    const int grp16 = min(g0 + ((UPW * wave + j) & 15), gmax);
+    coff[j] = (uint32_t)grp16 * (uint32_t)steps * 1024u + 16u * lane;
   }
-  // Scales: wave w < 4 moves token rows 64 w + lane, w >= 4 weight rows
-  // 64 (w - 4) + lane; 16 bytes (4 dwords, one per lane group) per row.
-  const uint8_t* sbase = wave < 4 ? xs : ws;
-  const int srow = wave < 4 ? min(tile_m + 64 * wave + lane, M - 1) : min(tile_n + 64 * (wave - 4) + lane, N - 1);
-  const uint32_t soff = (uint32_t)srow * (uint32_t)(ks4 * 16);
+  // Scales: 1 KB records of 64 rows x 4 steps, 8 per 4-step group (records
+  // 0-3 token rows, 4-7 weight rows); wave w moves records RPW w ..
+  const uint8_t* sbase = tokw ? xs : ws;
+  const int smax = tokw ? (M + 63) / 64 - 1 : (N + 63) / 64 - 1;
+  uint32_t soff[RPW];
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) {
+    const int grp64 = min(((tokw ? tile_m : tile_n) >> 6) + ((RPW * wave + j) & 3), smax);
+    soff[j] = (uint32_t)grp64 * (uint32_t)ks4 * 1024u + 16u * lane;
+  }
   const uint32_t scale_lds = lds_u32 + MX_NBUF * MX_STEP_BYTES;
   auto issue_codes = [&](int t) __attribute__((always_inline)) {
-    const uint32_t b = lds_u32 + (uint32_t)(t % MX_NBUF) * MX_STEP_BYTES + (uint32_t)wave * 4096u;
+    const uint32_t b = lds_u32 + (uint32_t)(t % MX_NBUF) * MX_STEP_BYTES + (uint32_t)wave * (1024u * UPW);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(cbase + (size_t)t * 64, coff[j], b + 1024u * j);
+    for (int j = 0; j < UPW; ++j) dma16(cbase + (size_t)t * 1024, coff[j], b + 1024u * j);
   };
   auto issue_scales = [&](int grp) __attribute__((always_inline)) {
-    dma16(sbase + (size_t)grp * 16, soff, scale_lds + (uint32_t)(grp & 1) * MX_SC_BYTES + (uint32_t)wave * 1024u);
+#pragma unroll
+    for (int j = 0; j < RPW; ++j)
+      dma16(sbase + (size_t)grp * 1024, soff[j],
+            scale_lds + (uint32_t)(grp & 1) * MX_SC_BYTES + (uint32_t)(RPW * wave + j) * 1024u);
   };
 
   // fragment addresses (without the step-buffer offset): token fragment q
   // reads row 128 wm + 16 q + l16 (two parities, 1 KB apart per q), weight
-  // fragment nt reads the permuted row 64 wn + mx_nrow(nt, l16)
-  uint32_t boff[2], aoff[4];
+  // fragment nt reads the permuted row 16 NTW wn + mx_nrow(nt, l16)
+  uint32_t boff[2], aoff[NTW];
 #pragma unroll
   for (int par = 0; par < 2; ++par) boff[par] = (uint32_t)swz(128 * wm + 16 * par + l16, g) - 1024u * par;
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) aoff[nt] = (uint32_t)(MX_BM * 64 + swz(64 * wn + mx_nrow(nt, l16), g));
+  for (int nt = 0; nt < NTW; ++nt) aoff[nt] = (uint32_t)(MX_BM * 64 + swz(16 * NTW * wn + mx_nrow(nt, l16), g));
   // bo: byte offset of a step buffer, kept opaque to the optimiser so that
   // it does not hoist one address register per (buffer, fragment) pair out
   // of the unrolled loop
@@ -375,7 +411,7 @@ __global__ __launch_bounds__(MX_THREADS, 1) void kb_mx_kernel(
   };
   // scale registers hold the E8M0 bytes of a pair of steps (tp, tp+1), tp
   // even, in their low half: a 16-bit read from the group's dwords
-  uint32_t asc[4], bsc[8];
+  uint32_t asc[NTW], bsc[8];
   auto read_scales = [&](int tp) __attribute__((always_inline)) {
     uint32_t so = (uint32_t)(MX_NBUF * MX_STEP_BYTES + ((tp >> 2) & 1) * MX_SC_BYTES + 2 * ((tp >> 1) & 1));
     asm volatile("" : "+s"(so));
@@ -383,14 +419,18 @@ __global__ __launch_bounds__(MX_THREADS, 1) void kb_mx_kernel(
 #pragma unroll
     for (int q = 0; q < 8; ++q) bsc[q] = *reinterpret_cast<const uint16_t*>(sc + ((128 * wm + 16 * q + l16) * 4 + g) * 4);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-      asc[nt] = *reinterpret_cast<const uint16_t*>(sc + ((MX_BM + 64 * wn + mx_nrow(nt, l16)) * 4 + g) * 4);
+    for (int nt = 0; nt < NTW; ++nt)
+      asc[nt] = *reinterpret_cast<const uint16_t*>(sc + ((MX_BM + 16 * NTW * wn + mx_nrow(nt, l16)) * 4 + g) * 4);
   };
-  // every DMA issued before step s's must be done; only step s + 1's (4 per
-  // wave) may still be in flight
+  // every DMA issued before step s's must be done; only step s + 1's (UPW
+  // per wave) may still be in flight
   auto wait_for = [&](int s) __attribute__((always_inline)) {
-    if (s + 1 < steps)
-      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    if (s + 1 < steps) {
+      if constexpr (UPW == 4)
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    }
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -401,18 +441,18 @@ __global__ __launch_bounds__(MX_THREADS, 1) void kb_mx_kernel(
   for (int s0 = 0; s0 < 3; ++s0)
     if (s0 < steps) issue_codes(s0);
 
-  v4f acc[4][8];   // [weight tile][token tile]
+  v4f acc[NTW][8];   // [weight tile][token tile]
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
+  for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) acc[nt][mt] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  v4i wf[2][4];   // weight fragments of the current and the next step
+  v4i wf[2][NTW];   // weight fragments of the current and the next step
   v4i tk[4];      // token fragments, three ahead; fragment q sits in slot q & 3
   wait_for(0);
   read_scales(0);
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) wf[0][nt] = read_a(0, nt);
+  for (int nt = 0; nt < NTW; ++nt) wf[0][nt] = read_a(0, nt);
 #pragma unroll
   for (int q = 0; q < 3; ++q) tk[q] = read_b(0, q);
 
@@ -420,27 +460,27 @@ __global__ __launch_bounds__(MX_THREADS, 1) void kb_mx_kernel(
   // arithmetic is redone where they are called instead of being hoisted out
   // of the main loop into live registers.
   auto issue_z = [&](int u, uint32_t zdst) __attribute__((always_inline)) {
-    // Z: 32 units of 8 rows x 128 B; wave w moves units 4w .. 4w+3
+    // Z: 32 units of 8 rows x 128 B; wave w moves units 32/WAVES each
     int ln = lane;
     asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int unit = 4 * wave + j, row = 8 * unit + (ln >> 3);
+    for (int j = 0; j < 32 / WAVES; ++j) {
+      const int unit = (32 / WAVES) * wave + j, row = 8 * unit + (ln >> 3);
       const int m = min(tile_m + row, M - 1);
-      dma16(reinterpret_cast<const uint8_t*>(zp), ((uint32_t)m * (uint32_t)rpad + 32u * u) * 4u + 16u * (ln & 7),
-            zdst + 1024u * unit);
+      dma16(reinterpret_cast<const uint8_t*>(zp),
+            ((uint32_t)m * (uint32_t)rpad + 32u * u) * 4u + 16u * ((ln & 7) ^ zswz(row)), zdst + 1024u * unit);
     }
   };
   auto issue_l2 = [&](int u, uint32_t ldst) __attribute__((always_inline)) {
-    // L2'^T: 16 units of 16 rows x 64 B; wave w moves units 2w, 2w+1
+    // L2'^T: 16 units of 16 rows x 64 B; wave w moves units 16/WAVES each
     int ln = lane;
     asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int unit = 2 * wave + j, row = 16 * unit + (ln >> 2);
+    for (int j = 0; j < 16 / WAVES; ++j) {
+      const int unit = (16 / WAVES) * wave + j, row = 16 * unit + (ln >> 2);
       const int n = min(tile_n + row, N - 1);
-      dma16(reinterpret_cast<const uint8_t*>(l2k), ((uint32_t)n * (uint32_t)rpad + 32u * u) * 2u + 16u * (ln & 3),
-            ldst + 1024u * unit);
+      dma16(reinterpret_cast<const uint8_t*>(l2k),
+            ((uint32_t)n * (uint32_t)rpad + 32u * u) * 2u + 16u * ((ln & 3) ^ lswz(row)), ldst + 1024u * unit);
     }
   };
   // Chunk 0 of Z and L2' is fetched right after the barrier of step
@@ -467,20 +507,35 @@ __global__ __launch_bounds__(MX_THREADS, 1) void kb_mx_kernel(
     constexpr int HOOK = decltype(hooktag)::value;   // 0 none, 1 always, 2 at step steps-2
     wait_for(t + 1);
     if ((t & 3) == 0 && (t >> 2) + 1 < ks4) issue_scales((t >> 2) + 1);
-    if (t + 3 < steps) issue_codes(t + 3);
     if constexpr (HOOK == 1) lr_prefetch_issue();
     if constexpr (HOOK == 2) {
       if (t == steps - 2) lr_prefetch_issue();
     }
     const uint32_t bc = buf_of(t), bn = buf_of(t + 1);
+    // The code loads of step t+3 go out one per odd MFMA group, so no wave
+    // stalls its MFMAs behind a burst of vector-memory issues.  In the last
+    // three steps there is no step t+3: the loads then re-read the last step
+    // (in bounds) into this wave's 1 KB dummy region, which keeps the loop
+    // free of branches and every step's load count (the vmcnt arithmetic)
+    // the same.
+    const bool more = t + 3 < steps;
+    const uint8_t* csrc = cbase + (size_t)(more ? t + 3 : steps - 1) * 1024;
+    const uint32_t cdst = more ? lds_u32 + (uint32_t)((t + 3) % MX_NBUF) * MX_STEP_BYTES + (uint32_t)wave * (1024u * UPW)
+                               : lds_u32 + MX_DUMMY + (uint32_t)wave * 1024u;
+    const uint32_t cinc = more ? 1024u : 0u;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
-      if (mt < 4) wf[J ^ 1][mt] = read_a(bn, mt);
+      if constexpr (UPW == 8) {
+        dma16(csrc, coff[mt], cdst + cinc * mt);
+      } else {
+        if (mt & 1) dma16(csrc, coff[mt >> 1], cdst + cinc * (mt >> 1));
+      }
+      if (mt < NTW) wf[J ^ 1][mt] = read_a(bn, mt);
       tk[(mt + 3) & 3] = mt + 3 < 8 ? read_b(bc, mt + 3) : read_b(bn, mt - 5);
       const v4i bq = tk[mt & 3];
       const v8i b = (v8i){bq[0], bq[1], bq[2], bq[3], 0, 0, 0, 0};
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < NTW; ++nt) {
         const v4i aq = wf[J][nt];
         const v8i a = (v8i){aq[0], aq[1], aq[2], aq[3], 0, 0, 0, 0};
         acc[nt][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[nt][mt], 4, 4, J, (int)asc[nt], J,
@@ -542,11 +597,13 @@ __global__ __launch_bounds__(MX_THREADS, 1) void kb_mx_kernel(
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int mt = 4 * mh + k;
-          const float* zr = reinterpret_cast<const float*>(lds + zoff + (128 * wm + 16 * mt + l16) * 128 + 32 * g);
+          const int zrow = 128 * wm + 16 * mt + l16;
+          const v4f z0 = *reinterpret_cast<const v4f*>(lds + zoff + zrow * 128 + 16 * ((2 * g) ^ zswz(zrow)));
+          const v4f z1 = *reinterpret_cast<const v4f*>(lds + zoff + zrow * 128 + 16 * ((2 * g + 1) ^ zswz(zrow)));
           uint16_t hi[8], lo[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
-            const float z = zr[i];
+            const float z = i < 4 ? z0[i] : z1[i - 4];
             const uint32_t hb = bf16_rne(z);
             hi[i] = (uint16_t)hb;
             lo[i] = (uint16_t)bf16_rne(z - __uint_as_float(hb << 16));
@@ -555,8 +612,9 @@ __global__ __launch_bounds__(MX_THREADS, 1) void kb_mx_kernel(
           bl[k] = __builtin_bit_cast(v8bf, *reinterpret_cast<v4i*>(lo));
         }
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const v8bf af = *reinterpret_cast<const v8bf*>(lds + loff + (64 * wn + mx_nrow(nt, l16)) * 64 + 16 * g);
+        for (int nt = 0; nt < NTW; ++nt) {
+          const int lrow = 16 * NTW * wn + mx_nrow(nt, l16);
+          const v8bf af = *reinterpret_cast<const v8bf*>(lds + loff + lrow * 64 + 16 * (g ^ lswz(lrow)));
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             acc[nt][4 * mh + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bh[k], acc[nt][4 * mh + k], 0, 0, 0);
@@ -568,7 +626,7 @@ __global__ __launch_bounds__(MX_THREADS, 1) void kb_mx_kernel(
   }
   // lane holds out-features n_base + 32 p + 8 g + 0..7 of token m for pair p
 #pragma unroll
-  for (int p2 = 0; p2 < 2; ++p2) {
+  for (int p2 = 0; p2 < NTW / 2; ++p2) {
     const int n0 = n_base + 32 * p2 + 8 * g;
     float bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (bias != nullptr && n0 < N) {
@@ -655,41 +713,38 @@ __global__ __launch_bounds__(I4_THREADS, 1) void kb_i4_kernel(
   const int tile_m = tm * I4_BM, tile_n = tn * I4_BN;
   const int steps = K / 128;
   const int ks4 = (steps + 3) / 4;
-  const uint32_t rowbytes = (uint32_t)K / 2;
   const int m_base = tile_m + 64 * wm, n_base = tile_n + 64 * wn;
 
-  // ---- DMA plan.  Codes: 24 units of 1 KB per step (units 0-15: 16 token
-  // rows each, 16-23: 16 weight rows each); wave w moves units 3w .. 3w+2,
-  // lane i filling 16-byte slot p = 64 (unit within its operand) + i, i.e.
-  // row p / 4 at swizzled chunk position p mod 4.
+  // ---- DMA plan.  Codes: 24 contiguous 1 KB units per step (codes layout;
+  // units 0-15: token row groups, 16-23: weight row groups); wave w moves
+  // units 3w .. 3w+2, lane i 16 bytes.  Units past the last row group
+  // repeat it (their outputs are never stored).
   const uint8_t* cbase[3];
   uint32_t coff[3];
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
     const int u = 3 * wave + j;
     const bool tok = u < 16;
-    const int p = 64 * (tok ? u : u - 16) + lane, r = p >> 2, c = (p & 3) ^ swz_f(r);
-    const int row = tok ? min(tile_m + r, M - 1) : min(tile_n + r, N - 1);
+    const int grp16 = tok ? min((tile_m >> 4) + u, (M + 15) / 16 - 1) : min((tile_n >> 4) + u - 16, N / 16 - 1);
     cbase[j] = tok ? xq : wq;
-    coff[j] = (uint32_t)row * rowbytes + 16u * c;
+    coff[j] = (uint32_t)grp16 * (uint32_t)steps * 1024u + 16u * lane;
   }
-  // Scales of 4-step group grp: waves 0-3 move token rows 64 w + lane (16
-  // bytes each), waves 4-5 the 128 16-byte pieces of the 32 weight blocks.
+  // Scales of 4-step group grp: waves 0-3 move the 1 KB records of token
+  // rows 64 w .. (64 rows x 16 bytes), waves 4-5 the 2 KB weight-scale unit
+  // of the block's 128 out-features (32 blocks of 4 rows x 4 steps).
   const uint8_t* sbase = wave < 4 ? xs : ws;
   uint32_t soff, sstride;
   if (wave < 4) {
-    soff = (uint32_t)min(tile_m + 64 * wave + lane, M - 1) * (uint32_t)(ks4 * 16);
-    sstride = 16;
+    soff = (uint32_t)min((tile_m >> 6) + wave, (M + 63) / 64 - 1) * (uint32_t)ks4 * 1024u + 16u * lane;
+    sstride = 1024;
   } else {
-    const int c = 64 * (wave - 4) + lane;
-    const int blk = min(tile_n / 4 + (c >> 2), N / 4 - 1);
-    soff = ((uint32_t)blk * (uint32_t)(4 * ks4) + (uint32_t)(c & 3)) * 16u;
-    sstride = 64;
+    soff = (uint32_t)(tile_n >> 7) * (uint32_t)ks4 * 2048u + 1024u * (uint32_t)(wave & 1) + 16u * lane;
+    sstride = 2048;
   }
   auto issue_codes = [&](int t) __attribute__((always_inline)) {
     const uint32_t b = lds_u32 + (uint32_t)(t % I4_NBUF) * I4_STEP_BYTES + (uint32_t)wave * 3072u;
 #pragma unroll
-    for (int j = 0; j < 3; ++j) dma16(cbase[j] + (size_t)t * 64, coff[j], b + 1024u * j);
+    for (int j = 0; j < 3; ++j) dma16(cbase[j] + (size_t)t * 1024, coff[j], b + 1024u * j);
   };
   auto issue_scales = [&](int grp) __attribute__((always_inline)) {
     if (wave < 6)
@@ -703,12 +758,14 @@ __global__ __launch_bounds__(I4_THREADS, 1) void kb_i4_kernel(
     for (int j = 0; j < 4; ++j) {
       const int unit = 4 * wave + j, row = 8 * unit + (lane >> 3);
       const int m = min(tile_m + row, M - 1);
-      dma16(reinterpret_cast<const uint8_t*>(zp), ((uint32_t)m * (uint32_t)rpad + 32u * u) * 4u + 16u * (lane & 7),
+      dma16(reinterpret_cast<const uint8_t*>(zp),
+            ((uint32_t)m * (uint32_t)rpad + 32u * u) * 4u + 16u * ((lane & 7) ^ zswz(row)),
             lds_u32 + I4_Z0 + 1024u * unit);
     }
     const int row = 16 * wave + (lane >> 2);
     const int n = min(tile_n + row, N - 1);
-    dma16(reinterpret_cast<const uint8_t*>(l2k), ((uint32_t)n * (uint32_t)rpad + 32u * u) * 2u + 16u * (lane & 3),
+    dma16(reinterpret_cast<const uint8_t*>(l2k),
+          ((uint32_t)n * (uint32_t)rpad + 32u * u) * 2u + 16u * ((lane & 3) ^ lswz(row)),
           lds_u32 + I4_L20 + 1024u * wave);
   };
 
@@ -828,11 +885,13 @@ __global__ __launch_bounds__(I4_THREADS, 1) void kb_i4_kernel(
       v8bf bh[4], bl[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const float* zr = reinterpret_cast<const float*>(lds + I4_Z0 + (64 * wm + 16 * mt + l16) * 128 + 32 * g);
+        const int zrow = 64 * wm + 16 * mt + l16;
+        const v4f z0 = *reinterpret_cast<const v4f*>(lds + I4_Z0 + zrow * 128 + 16 * ((2 * g) ^ zswz(zrow)));
+        const v4f z1 = *reinterpret_cast<const v4f*>(lds + I4_Z0 + zrow * 128 + 16 * ((2 * g + 1) ^ zswz(zrow)));
         uint16_t hi[8], lo[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float z = zr[i];
+          const float z = i < 4 ? z0[i] : z1[i - 4];
           const uint32_t hb = bf16_rne(z);
           hi[i] = (uint16_t)hb;
           lo[i] = (uint16_t)bf16_rne(z - __uint_as_float(hb << 16));
@@ -842,7 +901,8 @@ __global__ __launch_bounds__(I4_THREADS, 1) void kb_i4_kernel(
       }
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const v8bf af = *reinterpret_cast<const v8bf*>(lds + I4_L20 + (64 * wn + mx_nrow(nt, l16)) * 64 + 16 * g);
+        const int lrow = 64 * wn + mx_nrow(nt, l16);
+        const v8bf af = *reinterpret_cast<const v8bf*>(lds + I4_L20 + lrow * 64 + 16 * (g ^ lswz(lrow)));
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bh[mt], acc[nt][mt], 0, 0, 0);
@@ -909,12 +969,13 @@ static void launch_kb_mx(const svdq_layer& L, const uint8_t* ws, const svdq_ws_l
   const int tiles = ((M + MX_BM - 1) / MX_BM) * ((L.N + MX_BN - 1) / MX_BN);
   // the K loop runs in pairs of 128-wide steps; an odd step count takes the
   // variant with one trailing step
+  constexpr int WV = SVDQ_MX_WAVES;
   if ((L.K / 128) % 2 == 0)
-    hipLaunchKernelGGL((kb_mx_kernel<NTR, false>), dim3(tiles), dim3(MX_THREADS), 0, st, ws + W.xq_off,
+    hipLaunchKernelGGL((kb_mx_kernel<NTR, false, WV>), dim3(tiles), dim3(WV * 64), 0, st, ws + W.xq_off,
                        ws + W.xs_off, reinterpret_cast<const float*>(ws + W.z_off), W.zsplit, L.wq, L.ws, L.l2k,
                        L.bias, Y, M, L.N, L.K, rp);
   else
-    hipLaunchKernelGGL((kb_mx_kernel<NTR, true>), dim3(tiles), dim3(MX_THREADS), 0, st, ws + W.xq_off,
+    hipLaunchKernelGGL((kb_mx_kernel<NTR, true, WV>), dim3(tiles), dim3(WV * 64), 0, st, ws + W.xq_off,
                        ws + W.xs_off, reinterpret_cast<const float*>(ws + W.z_off), W.zsplit, L.wq, L.ws, L.l2k,
                        L.bias, Y, M, L.N, L.K, rp);
 }

@@ -8,6 +8,7 @@
 #include <vector>
 
 #include "../../include/svdq.h"
+#include "layout.h"
 
 namespace svdq {
 
@@ -32,11 +33,6 @@ int32_t choose_zsplit(int32_t M, int32_t K);
 inline int int4_step_byte(int k) {
   const int G = k >> 6, r = k & 63, g = r >> 4, j = r & 15;
   return 16 * g + 8 * G + (j >> 1);
-}
-// Byte index of MXFP4 scale block b in a permuted scale row.
-inline size_t mx_scale_index(int32_t b) {
-  const int32_t t = b >> 2, g = b & 3;
-  return (size_t)(t >> 2) * 16 + g * 4 + (t & 3);
 }
 
 // Scalar conversions (round to nearest even).

@@ -30,8 +30,8 @@ bool geometry(int32_t K, int32_t N, int32_t rank, int32_t fmt, Geometry* g) {
   g->K = K; g->N = N; g->rank = rank; g->rpad = rank_pad(rank); g->fmt = fmt;
   g->steps = K / kStep;
   g->ks4 = (g->steps + 3) / 4;
-  g->wq_bytes = (size_t)N * K / 2;
-  g->ws_bytes = (size_t)N * g->ks4 * 16;   // INT4: [N/4][4 ks4][4][2] fp16; MXFP4: [N][ks4 * 16] bytes
+  g->wq_bytes = code_bytes(N, g->steps);   // N % 16 == 0: exactly N K / 2
+  g->ws_bytes = fmt == SVDQ_INT4_G64 ? int4_wscale_bytes(N, g->ks4) : scale_record_bytes(N, g->ks4);
   g->l1k_bytes = (size_t)K * g->rpad * 2 * 2;
   g->l2k_bytes = (size_t)N * g->rpad * 2;
   return true;
@@ -223,9 +223,9 @@ svdq_status svdq_workspace_layout(int32_t M, int32_t K, int32_t rank, int32_t fm
   const int32_t steps = K / kStep, ks4 = (steps + 3) / 4;
   out->zsplit = rank > 0 ? choose_zsplit(M, K) : 0;
   out->xq_off = 0;
-  out->xq_bytes = (size_t)M * K / 2;
+  out->xq_bytes = code_bytes(M, steps);
   out->xs_off = align256(out->xq_bytes);
-  out->xs_bytes = (size_t)M * ks4 * 16;
+  out->xs_bytes = scale_record_bytes(M, ks4);
   out->z_off = align256(out->xs_off + out->xs_bytes);
   out->z_bytes = rank > 0 ? (size_t)out->zsplit * M * rank_pad(rank) * 4 : 0;
   out->total = align256(out->z_off + out->z_bytes);
@@ -389,41 +389,40 @@ svdq_status svdq_kernel_layout(int32_t K, int32_t N, int32_t rank, int32_t fmt, 
   if (!geometry(K, N, rank, fmt, &g)) return SVDQ_ERR_SHAPE;
   if (rank > 0 && (!l1 || !l2 || !l1k || !l2k)) return SVDQ_ERR_ARG;
   const int32_t steps = g.steps, rp = g.rpad;
-  // codes
-  if (fmt == SVDQ_MXFP4_G32) {
-    std::memcpy(wq_k, wq, g.wq_bytes);
-  } else {
-    parallel_for(N, default_threads(0), [&](int64_t lo, int64_t hi) {
-      for (int64_t n = lo; n < hi; ++n)
-        for (int32_t t = 0; t < steps; ++t) {
-          const uint8_t* src = wq + (size_t)n * (K / 2) + (size_t)t * 64;
-          uint8_t* dst = wq_k + (size_t)n * (K / 2) + (size_t)t * 64;
-          std::memset(dst, 0, 64);
+  // codes: tiled 1 KB units (INT4 bytes first permuted inside each step)
+  parallel_for(N, default_threads(0), [&](int64_t lo, int64_t hi) {
+    for (int64_t n = lo; n < hi; ++n)
+      for (int32_t t = 0; t < steps; ++t) {
+        const uint8_t* src = wq + (size_t)n * (K / 2) + (size_t)t * 64;
+        if (fmt == SVDQ_MXFP4_G32) {
+          for (int b = 0; b < 64; ++b) wq_k[code_offset((int)n, t, b, steps)] = src[b];
+        } else {
+          uint8_t step[64];
+          std::memset(step, 0, 64);
           for (int k = 0; k < kStep; ++k) {
             const uint8_t v = (src[k >> 1] >> ((k & 1) * 4)) & 0xF;
             const int j = (k & 63) & 15;
-            dst[int4_step_byte(k)] |= (uint8_t)(v << ((j & 1) * 4));
+            step[int4_step_byte(k)] |= (uint8_t)(v << ((j & 1) * 4));
           }
+          for (int b = 0; b < 64; ++b) wq_k[code_offset((int)n, t, b, steps)] = step[b];
         }
-    });
-  }
+      }
+  });
   // scales
   if (fmt == SVDQ_MXFP4_G32) {
-    for (int32_t n = 0; n < N; ++n) {
-      uint8_t* dst = ws_k + (size_t)n * g.ks4 * 16;
-      std::memset(dst, 127, (size_t)g.ks4 * 16);
-      for (int32_t b = 0; b < K / 32; ++b) dst[mx_scale_index(b)] = ws[(size_t)n * (K / 32) + b];
-    }
+    std::memset(ws_k, 127, g.ws_bytes);
+    for (int32_t n = 0; n < N; ++n)
+      for (int32_t b = 0; b < K / 32; ++b) {
+        const int32_t t = b / 4, gq = b % 4;
+        ws_k[scale_record_offset(n, t / 4, 4 * gq + t % 4, g.ks4)] = ws[(size_t)n * (K / 32) + b];
+      }
   } else {
-    // [N/4][4 ks4 steps][4 rows][2 groups] fp16, steps past K zero
     const uint16_t* s = reinterpret_cast<const uint16_t*>(ws);
     uint16_t* d = reinterpret_cast<uint16_t*>(ws_k);
-    const int32_t sp = 4 * g.ks4;
     std::memset(ws_k, 0, g.ws_bytes);
     for (int32_t n = 0; n < N; ++n)
       for (int32_t t = 0; t < steps; ++t)
-        for (int G = 0; G < 2; ++G)
-          d[((size_t)(n / 4) * sp + t) * 8 + (n % 4) * 2 + G] = s[(size_t)n * (K / 64) + 2 * t + G];
+        for (int G = 0; G < 2; ++G) d[int4_wscale_index(n, t, G, g.ks4)] = s[(size_t)n * (K / 64) + 2 * t + G];
   }
   if (rank == 0) return SVDQ_OK;
   // down factor: hi/lo bf16 split of diag(smooth_inv) L1', order
@@ -466,7 +465,8 @@ svdq_status svdq_unpack_activations(const void* ws_host, int32_t M, int32_t K, i
   const int32_t steps = K / kStep, ks4 = (steps + 3) / 4;
   for (int32_t m = 0; m < M; ++m) {
     for (int32_t t = 0; t < steps; ++t) {
-      const uint8_t* src = q + (size_t)m * (K / 2) + (size_t)t * 64;
+      uint8_t src[64];
+      for (int b = 0; b < 64; ++b) src[b] = q[code_offset(m, t, b, steps)];
       uint8_t* dst = xq + (size_t)m * (K / 2) + (size_t)t * 64;
       if (fmt == SVDQ_MXFP4_G32) {
         std::memcpy(dst, src, 64);
@@ -483,14 +483,16 @@ svdq_status svdq_unpack_activations(const void* ws_host, int32_t M, int32_t K, i
   const uint8_t* s = base + L.xs_off;
   if (fmt == SVDQ_MXFP4_G32) {
     for (int32_t m = 0; m < M; ++m)
-      for (int32_t b = 0; b < K / 32; ++b) xs[(size_t)m * (K / 32) + b] = s[(size_t)m * ks4 * 16 + mx_scale_index(b)];
+      for (int32_t b = 0; b < K / 32; ++b) {
+        const int32_t t = b / 4, gq = b % 4;
+        xs[(size_t)m * (K / 32) + b] = s[scale_record_offset(m, t / 4, 4 * gq + t % 4, ks4)];
+      }
   } else {
     uint16_t* xs16 = reinterpret_cast<uint16_t*>(xs);
     for (int32_t m = 0; m < M; ++m)
       for (int32_t t = 0; t < steps; ++t)
         for (int G = 0; G < 2; ++G)
-          std::memcpy(xs16 + (size_t)m * (K / 64) + 2 * t + G,
-                      s + (size_t)m * ks4 * 16 + (size_t)(t >> 2) * 16 + (t & 3) * 4 + 2 * G, 2);
+          std::memcpy(xs16 + (size_t)m * (K / 64) + 2 * t + G, s + scale_record_offset(m, t / 4, 4 * (t % 4) + 2 * G, ks4), 2);
   }
   if (z && rank > 0) {
     const int32_t rp = rank_pad(rank);

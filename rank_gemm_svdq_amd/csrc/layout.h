@@ -1,0 +1,51 @@
+// Device-friendly layouts of the 4-bit operands and their scales.
+//
+// K is cut into steps of 128 elements (64 bytes of codes per row).  Codes
+// are stored in 1 KB units of 16 rows x one step, units ordered [row / 16]
+// [step], so every direct-to-LDS load moves one contiguous kilobyte.  Inside
+// a unit, 16-byte slot p = 4 (row % 16) + q holds chunk q ^ chunk_swz(row %
+// 32) of that row's 64 bytes: the XOR swizzle the GEMM kernels read LDS with
+// (rows modulo 32 because their tiles start at multiples of 32 rows).
+//
+// Scale records (16 bytes per row and 4 steps) are stored in 1 KB units of
+// 64 rows, ordered [row / 64][4-step group].  INT4 weight scales are stored
+// in 2 KB units of 128 rows x 4 steps, ordered [row / 128][4-step group];
+// inside a unit [4-row block][step % 4][row % 4][group of 64] fp16.
+#ifndef SVDQ_LAYOUT_H
+#define SVDQ_LAYOUT_H
+
+#include <cstddef>
+#include <cstdint>
+
+#if defined(__HIPCC__)
+#define SVDQ_HD __host__ __device__
+#else
+#define SVDQ_HD
+#endif
+
+namespace svdq {
+
+SVDQ_HD inline int chunk_swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+// byte b (0..63) of step t of row `row`
+SVDQ_HD inline size_t code_offset(int row, int t, int b, int steps) {
+  return ((size_t)(row >> 4) * steps + t) * 1024 +
+         (size_t)(4 * (row & 15) + ((b >> 4) ^ chunk_swz(row & 31))) * 16 + (b & 15);
+}
+SVDQ_HD inline size_t code_bytes(int rows, int steps) { return (size_t)((rows + 15) / 16) * steps * 1024; }
+
+// byte j (0..15) of the scale record of row `row` for 4-step group q
+SVDQ_HD inline size_t scale_record_offset(int row, int q, int j, int ks4) {
+  return ((size_t)(row >> 6) * ks4 + q) * 1024 + (size_t)(row & 63) * 16 + j;
+}
+SVDQ_HD inline size_t scale_record_bytes(int rows, int ks4) { return (size_t)((rows + 63) / 64) * ks4 * 1024; }
+
+// fp16 index of the INT4 weight scale of row n, step t, 64-group G (0, 1) of the step
+SVDQ_HD inline size_t int4_wscale_index(int n, int t, int G, int ks4) {
+  return ((size_t)(n >> 7) * ks4 + (t >> 2)) * 1024 + (size_t)((n & 127) >> 2) * 32 + (t & 3) * 8 + (n & 3) * 2 + G;
+}
+SVDQ_HD inline size_t int4_wscale_bytes(int rows, int ks4) { return (size_t)((rows + 127) / 128) * ks4 * 2048; }
+
+}  // namespace svdq
+
+#endif

@@ -173,12 +173,26 @@ def test_error_codes_device_entry_points_validate_before_hip():
     assert lib.svdq_gemm_lora_up(C.byref(mis), 0x3000, ws, 64, 0x2000, None) == 3
 
 
+def _code_off(row, t, b, steps):
+    """Codes layout as documented in svdq.h: 1 KB units of 16 rows x one
+    step ordered [row / 16][step]; slot 4 (row % 16) + q holds chunk
+    q ^ swz(row % 32) of the row-step."""
+    r = row % 32
+    swz = ((r >> 1) ^ (r >> 3)) & 3
+    return ((row // 16) * steps + t) * 1024 + (4 * (row % 16) + ((b // 16) ^ swz)) * 16 + b % 16
+
+
+def _rec_off(row, q, j, ks4):
+    return ((row // 64) * ks4 + q) * 1024 + (row % 64) * 16 + j
+
+
 def test_workspace_layout_regions():
     for M, K, r, f in [(1, 128, 0, 0), (4096, 3072, 32, 1), (8192, 3072, 48, 0), (17, 512, 16, 1)]:
         w = B.workspace_layout(M, K, r, f)
+        ks4 = (K // 128 + 3) // 4
         assert w["xq_off"] % 256 == 0 and w["xs_off"] % 256 == 0 and w["z_off"] % 256 == 0
-        assert w["xq_bytes"] == M * K // 2
-        assert w["xs_bytes"] == M * ((K // 128 + 3) // 4) * 16
+        assert w["xq_bytes"] == (M + 15) // 16 * 16 * K // 2
+        assert w["xs_bytes"] == (M + 63) // 64 * 64 * ks4 * 16
         assert w["xs_off"] >= w["xq_off"] + w["xq_bytes"] and w["z_off"] >= w["xs_off"] + w["xs_bytes"]
         assert w["total"] >= w["z_off"] + w["z_bytes"]
         if r:
@@ -187,37 +201,66 @@ def test_workspace_layout_regions():
 
 
 def test_int4_kernel_layout_positions():
-    """Element k of a 128-element step sits at byte 16 g + 8 G + j/2 (nibble
-    j % 2) with G = k // 64, g = (k % 64) // 16, j = k % 16."""
-    K, N = 256, 16
+    """INT4 element k of a step sits at step byte 16 g + 8 G + j/2 (nibble
+    j % 2), G = k // 64, g = (k % 64) // 16, j = k % 16, and the step bytes
+    are tiled as documented; weight scales in 2 KB units of 128 rows."""
+    K, N = 640, 144
+    steps, ks4 = K // 128, (K // 128 + 3) // 4
     rng = np.random.default_rng(0)
     nib = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    sc = rng.integers(1, 30000, (N, K // 64)).astype(np.uint16)
     prep = {"K": K, "N": N, "rank": 0, "fmt": 0, "smooth_inv": np.ones(K, np.float32),
-            "wq": Q.pack_nibbles(nib), "ws": np.ones((N, K // 64), np.float16).view(np.uint16)}
+            "wq": Q.pack_nibbles(nib), "ws": sc}
     kl = B.kernel_layout(prep)
-    wk = kl["wq_k"].reshape(N, K // 2)
-    for n in range(N):
+    wk = kl["wq_k"].reshape(-1)
+    for n in range(0, N, 7):
         for k in range(K):
             t, kk = divmod(k, 128)
             G, g, j = kk // 64, (kk % 64) // 16, kk % 16
-            byte = wk[n, 64 * t + 16 * g + 8 * G + j // 2]
+            byte = wk[_code_off(n, t, 16 * g + 8 * G + j // 2, steps)]
             assert (byte >> (4 * (j % 2))) & 0xF == nib[n, k]
+    ws = kl["ws_k"].view(np.uint16).reshape(-1)
+    assert ws.size == (N + 127) // 128 * ks4 * 1024
+    seen = np.zeros(ws.size, bool)
+    for n in range(N):
+        for t in range(steps):
+            for G in range(2):
+                i = ((n // 128) * ks4 + t // 4) * 1024 + ((n % 128) // 4) * 32 + (t % 4) * 8 + (n % 4) * 2 + G
+                assert ws[i] == sc[n, 2 * t + G]
+                seen[i] = True
+    assert np.all(ws[~seen] == 0)
+
+
+def test_mxfp4_code_layout_positions():
+    K, N = 384, 48
     steps = K // 128
-    ws = kl["ws_k"].view(np.uint16).reshape(N // 4, (steps + 3) // 4 * 4, 4, 2)
-    assert np.all(ws[:, :steps] == np.float16(1).view(np.uint16))
-    assert np.all(ws[:, steps:] == 0)
+    rng = np.random.default_rng(2)
+    codes = rng.integers(0, 256, (N, K // 2)).astype(np.uint8)
+    prep = {"K": K, "N": N, "rank": 0, "fmt": 1, "smooth_inv": np.ones(K, np.float32),
+            "wq": codes, "ws": np.full((N, K // 32), 127, np.uint8)}
+    wk = B.kernel_layout(prep)["wq_k"].reshape(-1)
+    assert wk.size == N * K // 2
+    for n in range(N):
+        for t in range(steps):
+            for b in range(64):
+                assert wk[_code_off(n, t, b, steps)] == codes[n, 64 * t + b]
 
 
 def test_mxfp4_scale_layout_positions():
-    K, N = 1024, 16
+    K, N = 1024, 80
     rng = np.random.default_rng(1)
     sc = rng.integers(100, 150, (N, K // 32)).astype(np.uint8)
     prep = {"K": K, "N": N, "rank": 0, "fmt": 1, "smooth_inv": np.ones(K, np.float32),
             "wq": np.zeros((N, K // 2), np.uint8), "ws": sc}
     kl = B.kernel_layout(prep)
-    steps = K // 128
-    row = kl["ws_k"].reshape(N, -1)
-    assert row.shape[1] == (steps + 3) // 4 * 16
-    for b in range(K // 32):
-        t, g = divmod(b, 4)
-        assert np.array_equal(row[:, 16 * (t // 4) + 4 * g + t % 4], sc[:, b])
+    ks4 = (K // 128 + 3) // 4
+    row = kl["ws_k"].reshape(-1)
+    assert row.size == (N + 63) // 64 * 64 * ks4 * 16
+    seen = np.zeros(row.size, bool)
+    for n in range(N):
+        for b in range(K // 32):
+            t, g = divmod(b, 4)
+            i = _rec_off(n, t // 4, 4 * g + t % 4, ks4)
+            assert row[i] == sc[n, b]
+            seen[i] = True
+    assert np.all(row[~seen] == 127)
