@@ -187,8 +187,11 @@ svdq_status svdq_attach_lora(const float* lambda, const uint16_t* l1, const uint
                              int32_t k, float strength, uint16_t* l1_out, uint16_t* l2_out);
 
 /* Canonical host buffers -> kernel-layout host buffers (sizes from
- * svdq_layer_sizes).  l1 may be NULL when rank == 0.  The down factor is
- * stored pre-multiplied by diag(smooth_inv), split into a bf16 hi/lo pair. */
+ * svdq_layer_sizes).  l1 may be NULL when rank == 0.  The down factor L1'
+ * (bf16) is stored in the order of the quantize kernel's MFMA operand,
+ * [step][s 0..3][16-column tile][lane 0..63][i 0..7] holding
+ * L1'[128 step + 32 (lane / 16) + 8 s + i][16 tile + lane % 16] (0 past rank);
+ * the up factor as L2'^T [N][rank rounded up to 32] (0 past rank). */
 svdq_status svdq_kernel_layout(int32_t K, int32_t N, int32_t rank, int32_t fmt,
                                const float* smooth_inv, const uint8_t* wq, const uint8_t* ws,
                                const uint16_t* l1, const uint16_t* l2,

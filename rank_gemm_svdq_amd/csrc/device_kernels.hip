@@ -29,8 +29,8 @@
 //     of step t (groups 2t, 2t+1) in the dword at byte 16 (t / 4) + 4 (t % 4).
 //   INT4 weight scales: [N/4][4 ceil(steps/4)][4 rows][2 groups] fp16, so a
 //     4-row block holds 64 contiguous bytes per 4 steps.
-//   Down factor: bf16 hi/lo split of diag(1/lambda) L1', ordered
-//     [step][hi/lo][s][n-tile][lane][8] with k = 128 step + 32 (lane/16) + 8 s + i.
+//   Down factor: L1' (bf16), ordered [step][s][n-tile][lane][8] with
+//     k = 128 step + 32 (lane/16) + 8 s + i, n = 16 n-tile + lane % 16.
 //   Up factor: L2'^T, [N][rpad] bf16, rpad = rank rounded up to 32.
 //   Z (down projection): fp32 [M][rpad].
 
@@ -63,20 +63,28 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 // ----------------------------------------------------------------- K-A
 
 constexpr int KA_WAVES = 8;
+constexpr int KA_SL_MAX_K = 16384;   // 1/lambda is staged in LDS up to this K
 
 // One block handles 16 rows; its 8 waves split the K steps evenly and the
 // down-projection partial sums are reduced in LDS, so Z leaves the kernel
 // once.  Lane l owns row l % 16 and the 32 consecutive elements
-// 32 (l / 16) .. +32 of each 128-element step; the next step's X is loaded
-// while the current one is processed.
-template <int FMT, int NT>
+// 32 (l / 16) .. +32 of each 128-element step.  Each wave keeps the next
+// two steps' X (and, for ranks up to 64, their down-factor fragments) in
+// flight in a register ring while it processes the current one; 1/lambda
+// comes from LDS when K allows.  The down projection multiplies the
+// smoothed x^ = x / lambda, split into bf16 hi + lo, by the bf16 factor
+// L1', so it runs on bf16 MFMA with fp32 accumulation.
+template <int FMT, int NT, bool SL>
 __global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __restrict__ X, int M, int K,
                                                           const float* __restrict__ sinv,
                                                           const v8bf* __restrict__ l1k,
                                                           uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
                                                           float* __restrict__ zout, int rpad) {
   constexpr int NTZ = NT > 0 ? NT : 1;
+  constexpr bool WRING = NT > 0 && NT <= (SL ? 4 : 2);   // down-factor fragments in the ring
+  constexpr int NW = WRING ? 4 * NT : 1;
   __shared__ float zred[NT > 0 ? KA_WAVES * 16 * NT * 16 : 1];
+  extern __shared__ __attribute__((aligned(16))) float svl[];   // K floats when SL
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int row0 = blockIdx.x * 16;
@@ -90,29 +98,44 @@ __global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __res
   const int t0 = wave * spw;
   const int t1 = min(steps, t0 + spw);
   const uint16_t* xrow = X + (size_t)rowc * K + 32 * g;
+
+  struct Slot {
+    v4i x[4];
+    v4f s[SL ? 1 : 8];
+    v8bf w[NW];
+  };
+  auto load = [&](int t, Slot& sl) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sl.x[c] = *reinterpret_cast<const v4i*>(xrow + (size_t)t * 128 + 8 * c);
+    if constexpr (!SL) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) sl.s[c] = *reinterpret_cast<const v4f*>(sinv + t * 128 + 32 * g + 4 * c);
+    }
+    if constexpr (WRING) {
+#pragma unroll
+      for (int i = 0; i < 4 * NT; ++i) sl.w[i] = l1k[((size_t)t * 4 * NT + i) * 64 + lane];
+    }
+  };
+  if constexpr (SL) {
+    for (int i = 4 * (int)threadIdx.x; i < K; i += 4 * 64 * KA_WAVES)
+      *reinterpret_cast<v4f*>(svl + i) = *reinterpret_cast<const v4f*>(sinv + i);
+  }
+  Slot ring[2];
+  if (t0 < t1) load(t0, ring[0]);
+  if (t0 + 1 < t1) load(t0 + 1, ring[1]);
+  if constexpr (SL) __syncthreads();
+
   v4f acc[NTZ];
 #pragma unroll
   for (int nt = 0; nt < NTZ; ++nt) acc[nt] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  v4i nxt[4];
-  if (t0 < t1) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) nxt[c] = *reinterpret_cast<const v4i*>(xrow + (size_t)t0 * 128 + 8 * c);
-  }
-  for (int t = t0; t < t1; ++t) {
-    v4i raw[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) raw[c] = nxt[c];
-    if (t + 1 < t1) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) nxt[c] = *reinterpret_cast<const v4i*>(xrow + (size_t)(t + 1) * 128 + 8 * c);
-    }
+  auto process = [&](int t, const Slot& sl) __attribute__((always_inline)) {
     const int k0 = t * 128 + 32 * g;
     float xh[32];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const v4f iv = *reinterpret_cast<const v4f*>(sinv + k0 + 4 * c);
-      const uint32_t w0 = (uint32_t)raw[c >> 1][(c & 1) * 2], w1 = (uint32_t)raw[c >> 1][(c & 1) * 2 + 1];
+      const v4f iv = SL ? *reinterpret_cast<const v4f*>(svl + k0 + 4 * c) : sl.s[SL ? 0 : c];
+      const uint32_t w0 = (uint32_t)sl.x[c >> 1][(c & 1) * 2], w1 = (uint32_t)sl.x[c >> 1][(c & 1) * 2 + 1];
       xh[4 * c + 0] = bf16_lo(w0) * iv[0];
       xh[4 * c + 1] = bf16_hi(w0) * iv[1];
       xh[4 * c + 2] = bf16_lo(w1) * iv[2];
@@ -193,19 +216,33 @@ __global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __res
     }
 
     if constexpr (NT > 0) {
-      // Z += X diag(1/lambda) L1' with the scaling folded into the factor;
-      // the raw bf16 X words are the A operand.
+      // Z += (x^hi + x^lo) L1': MFMA s covers elements 32 g + 8 s .. + 8 of
+      // every lane group, i.e. k = 128 t + 32 (lane / 16) + 8 s + i
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const v8bf a = __builtin_bit_cast(v8bf, raw[s]);
+      for (int s4 = 0; s4 < 4; ++s4) {
+        v8bf hi, lo;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int i = 0; i < 8; ++i) {
+          const __bf16 h = (__bf16)xh[8 * s4 + i];
+          hi[i] = h;
+          lo[i] = (__bf16)(xh[8 * s4 + i] - (float)h);
+        }
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            const v8bf b = l1k[((((size_t)t * 2 + h) * 4 + s) * NT + nt) * 64 + lane];
-            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[nt], 0, 0, 0);
-          }
+        for (int nt = 0; nt < NT; ++nt) {
+          const v8bf b = WRING ? sl.w[WRING ? s4 * NT + nt : 0] : l1k[(((size_t)t * 4 + s4) * NT + nt) * 64 + lane];
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, b, acc[nt], 0, 0, 0);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, b, acc[nt], 0, 0, 0);
+        }
       }
+    }
+  };
+
+  for (int t = t0; t < t1; t += 2) {
+    process(t, ring[0]);
+    if (t + 2 < t1) load(t + 2, ring[0]);
+    if (t + 1 < t1) {
+      process(t + 1, ring[1]);
+      if (t + 3 < t1) load(t + 3, ring[1]);
     }
   }
   if constexpr (NT > 0) {
@@ -951,14 +988,24 @@ static hipError_t launch_ka(const svdq_layer& L, const uint16_t* X, int M, uint8
   uint8_t* xs = ws + W.xs_off;
   float* z = reinterpret_cast<float*>(ws + W.z_off);
   const v8bf* l1 = reinterpret_cast<const v8bf*>(L.l1k);
+#define SVDQ_KA(NTV)                                                                                        \
+  do {                                                                                                      \
+    if (L.K <= KA_SL_MAX_K)                                                                                 \
+      hipLaunchKernelGGL((ka_kernel<FMT, NTV, true>), grid, block, (size_t)L.K * 4, st, X, M, L.K, L.smooth_inv, \
+                         l1, xq, xs, z, rp);                                                                \
+    else                                                                                                    \
+      hipLaunchKernelGGL((ka_kernel<FMT, NTV, false>), grid, block, 0, st, X, M, L.K, L.smooth_inv, l1, xq, xs, \
+                         z, rp);                                                                            \
+  } while (0)
   switch (rp / 16) {
-    case 0: hipLaunchKernelGGL((ka_kernel<FMT, 0>), grid, block, 0, st, X, M, L.K, L.smooth_inv, l1, xq, xs, z, rp); break;
-    case 2: hipLaunchKernelGGL((ka_kernel<FMT, 2>), grid, block, 0, st, X, M, L.K, L.smooth_inv, l1, xq, xs, z, rp); break;
-    case 4: hipLaunchKernelGGL((ka_kernel<FMT, 4>), grid, block, 0, st, X, M, L.K, L.smooth_inv, l1, xq, xs, z, rp); break;
-    case 6: hipLaunchKernelGGL((ka_kernel<FMT, 6>), grid, block, 0, st, X, M, L.K, L.smooth_inv, l1, xq, xs, z, rp); break;
-    case 8: hipLaunchKernelGGL((ka_kernel<FMT, 8>), grid, block, 0, st, X, M, L.K, L.smooth_inv, l1, xq, xs, z, rp); break;
+    case 0: SVDQ_KA(0); break;
+    case 2: SVDQ_KA(2); break;
+    case 4: SVDQ_KA(4); break;
+    case 6: SVDQ_KA(6); break;
+    case 8: SVDQ_KA(8); break;
     default: return hipErrorInvalidValue;
   }
+#undef SVDQ_KA
   return hipGetLastError();
 }
 

@@ -32,7 +32,7 @@ bool geometry(int32_t K, int32_t N, int32_t rank, int32_t fmt, Geometry* g) {
   g->ks4 = (g->steps + 3) / 4;
   g->wq_bytes = code_bytes(N, g->steps);   // N % 16 == 0: exactly N K / 2
   g->ws_bytes = fmt == SVDQ_INT4_G64 ? int4_wscale_bytes(N, g->ks4) : scale_record_bytes(N, g->ks4);
-  g->l1k_bytes = (size_t)K * g->rpad * 2 * 2;
+  g->l1k_bytes = (size_t)K * g->rpad * 2;
   g->l2k_bytes = (size_t)N * g->rpad * 2;
   return true;
 }
@@ -425,28 +425,21 @@ svdq_status svdq_kernel_layout(int32_t K, int32_t N, int32_t rank, int32_t fmt, 
         for (int G = 0; G < 2; ++G) d[int4_wscale_index(n, t, G, g.ks4)] = s[(size_t)n * (K / 64) + 2 * t + G];
   }
   if (rank == 0) return SVDQ_OK;
-  // down factor: hi/lo bf16 split of diag(smooth_inv) L1', order
-  // [step][hi/lo][s 0..3][n-tile][lane 0..63][i 0..7] with
+  // down factor: L1' (bf16) in the order of K-A's MFMA B operand,
+  // [step][s 0..3][n-tile][lane 0..63][i 0..7] with
   // k = 128 step + 32 (lane / 16) + 8 s + i and n = 16 tile + lane % 16
   const int32_t ntile = rp / 16;
   parallel_for(steps, default_threads(0), [&](int64_t lo, int64_t hi) {
     for (int64_t t = lo; t < hi; ++t)
-      for (int h = 0; h < 2; ++h)
-        for (int s = 0; s < 4; ++s)
-          for (int32_t nt = 0; nt < ntile; ++nt)
-            for (int lane = 0; lane < 64; ++lane)
-              for (int i = 0; i < 8; ++i) {
-                const int32_t k = (int32_t)t * kStep + 32 * (lane / 16) + 8 * s + i;
-                const int32_t n = 16 * nt + lane % 16;
-                uint16_t out = 0;
-                if (n < rank) {
-                  const double v = (double)smooth_inv[k] * double_from_bf16(l1[(size_t)k * rank + n]);
-                  const uint16_t hb = bf16_from_double(v);
-                  out = h == 0 ? hb : bf16_from_double(v - double_from_bf16(hb));
-                }
-                const size_t idx = ((((((size_t)t * 2 + h) * 4 + s) * ntile + nt) * 64 + lane) * 8) + i;
-                l1k[idx] = out;
-              }
+      for (int s = 0; s < 4; ++s)
+        for (int32_t nt = 0; nt < ntile; ++nt)
+          for (int lane = 0; lane < 64; ++lane)
+            for (int i = 0; i < 8; ++i) {
+              const int32_t k = (int32_t)t * kStep + 32 * (lane / 16) + 8 * s + i;
+              const int32_t n = 16 * nt + lane % 16;
+              const size_t idx = (((((size_t)t * 4 + s) * ntile + nt) * 64 + lane) * 8) + i;
+              l1k[idx] = n < rank ? l1[(size_t)k * rank + n] : (uint16_t)0;
+            }
   });
   // up factor: L2'^T padded to rpad columns
   for (int32_t n = 0; n < N; ++n)
