@@ -62,8 +62,8 @@ def kb_kernel_names(fmt, K, rank):
     ntr = ((rank + 31) // 32 * 32) // 32
     if fmt == "mxfp4":
         odd = (K // 128) % 2
-        return (f"kb_mx_kernel<{ntr}, {'true' if odd else 'false'}>", f"kb_mx_kernelILi{ntr}ELb{odd}E")
-    return (f"kb_kernel<0, {ntr}>", f"kb_kernelILi0ELi{ntr}E")
+        return (f"kb_mx_kernel<{ntr}, {'true' if odd else 'false'}, 8>", f"kb_mx_kernelILi{ntr}ELb{odd}ELi8E")
+    return (f"kb_i4_kernel<{ntr}>", f"kb_i4_kernelILi{ntr}E")
 
 
 def oracle_sample(F, X, po, bias, seconds):

@@ -115,8 +115,9 @@ svdq_status svdq_layer_sizes(int32_t K, int32_t N, int32_t rank, int32_t fmt, sv
  *        ceil(M/16) * 16 * K/2 bytes; padding rows are not written)
  *   xs   activation scale records in the scale-record layout above
  *        (ceil(M/64) * 64 * ceil(K/512) * 16 bytes)
- *   z    down projection Z, fp32 [zsplit][M][rank rounded up to 32]; zsplit
- *        is 1 in this version (partial sums are reduced inside K-A)
+ *   z    down projection Z: per row and 32-column chunk of the rank
+ *        (rounded up to 32), 32 bf16 values hi then 32 bf16 values lo with
+ *        hi + lo = Z to about 2^-17 relative (M * rank_pad * 4 bytes)
  * svdq_unpack_activations() turns a host copy into canonical form. */
 typedef struct svdq_ws_layout {
   size_t xq_off, xq_bytes, xs_off, xs_bytes, z_off, z_bytes, total;

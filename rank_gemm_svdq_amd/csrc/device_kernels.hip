@@ -32,7 +32,8 @@
 //   Down factor: L1' (bf16), ordered [step][s][n-tile][lane][8] with
 //     k = 128 step + 32 (lane/16) + 8 s + i, n = 16 n-tile + lane % 16.
 //   Up factor: L2'^T, [N][rpad] bf16, rpad = rank rounded up to 32.
-//   Z (down projection): fp32 [M][rpad].
+//   Z (down projection): per row and 32-column chunk, 32 bf16 hi values then
+//     32 bf16 lo values (hi + lo = Z to about 2^-17), rpad * 4 bytes per row.
 
 #include <hip/hip_runtime.h>
 
@@ -258,7 +259,15 @@ __global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __res
       float sum = 0.f;
 #pragma unroll
       for (int w = 0; w < KA_WAVES; ++w) sum += zred[(w * 16 + rr) * W + cc];
-      if (row0 + rr < M) zout[(size_t)(row0 + rr) * rpad + cc] = sum;
+      // Z leaves as the bf16 pair hi + lo the up projection multiplies with:
+      // per row and 32-column chunk, 32 hi values then 32 lo values
+      if (row0 + rr < M) {
+        const __bf16 hi = (__bf16)sum;
+        const __bf16 lo = (__bf16)(sum - (float)hi);
+        uint16_t* zr = reinterpret_cast<uint16_t*>(zout) + (size_t)(row0 + rr) * 2 * rpad + 64 * (cc >> 5) + (cc & 31);
+        zr[0] = __builtin_bit_cast(uint16_t, hi);
+        zr[32] = __builtin_bit_cast(uint16_t, lo);
+      }
     }
   }
 }
@@ -635,18 +644,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
         for (int k = 0; k < 4; ++k) {
           const int mt = 4 * mh + k;
           const int zrow = 128 * wm + 16 * mt + l16;
-          const v4f z0 = *reinterpret_cast<const v4f*>(lds + zoff + zrow * 128 + 16 * ((2 * g) ^ zswz(zrow)));
-          const v4f z1 = *reinterpret_cast<const v4f*>(lds + zoff + zrow * 128 + 16 * ((2 * g + 1) ^ zswz(zrow)));
-          uint16_t hi[8], lo[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float z = i < 4 ? z0[i] : z1[i - 4];
-            const uint32_t hb = bf16_rne(z);
-            hi[i] = (uint16_t)hb;
-            lo[i] = (uint16_t)bf16_rne(z - __uint_as_float(hb << 16));
-          }
-          bh[k] = __builtin_bit_cast(v8bf, *reinterpret_cast<v4i*>(hi));
-          bl[k] = __builtin_bit_cast(v8bf, *reinterpret_cast<v4i*>(lo));
+          bh[k] = *reinterpret_cast<const v8bf*>(lds + zoff + zrow * 128 + 16 * (g ^ zswz(zrow)));
+          bl[k] = *reinterpret_cast<const v8bf*>(lds + zoff + zrow * 128 + 16 * ((4 + g) ^ zswz(zrow)));
         }
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
@@ -923,18 +922,8 @@ __global__ __launch_bounds__(I4_THREADS, 1) void kb_i4_kernel(
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const int zrow = 64 * wm + 16 * mt + l16;
-        const v4f z0 = *reinterpret_cast<const v4f*>(lds + I4_Z0 + zrow * 128 + 16 * ((2 * g) ^ zswz(zrow)));
-        const v4f z1 = *reinterpret_cast<const v4f*>(lds + I4_Z0 + zrow * 128 + 16 * ((2 * g + 1) ^ zswz(zrow)));
-        uint16_t hi[8], lo[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float z = i < 4 ? z0[i] : z1[i - 4];
-          const uint32_t hb = bf16_rne(z);
-          hi[i] = (uint16_t)hb;
-          lo[i] = (uint16_t)bf16_rne(z - __uint_as_float(hb << 16));
-        }
-        bh[mt] = __builtin_bit_cast(v8bf, *reinterpret_cast<v4i*>(hi));
-        bl[mt] = __builtin_bit_cast(v8bf, *reinterpret_cast<v4i*>(lo));
+        bh[mt] = *reinterpret_cast<const v8bf*>(lds + I4_Z0 + zrow * 128 + 16 * (g ^ zswz(zrow)));
+        bl[mt] = *reinterpret_cast<const v8bf*>(lds + I4_Z0 + zrow * 128 + 16 * ((4 + g) ^ zswz(zrow)));
       }
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {

@@ -489,12 +489,11 @@ svdq_status svdq_unpack_activations(const void* ws_host, int32_t M, int32_t K, i
   }
   if (z && rank > 0) {
     const int32_t rp = rank_pad(rank);
-    const float* zp = reinterpret_cast<const float*>(base + L.z_off);
+    const uint16_t* zp = reinterpret_cast<const uint16_t*>(base + L.z_off);
     for (int32_t m = 0; m < M; ++m)
       for (int32_t j = 0; j < rank; ++j) {
-        float acc = 0.0f;
-        for (int32_t p = 0; p < L.zsplit; ++p) acc += zp[((size_t)p * M + m) * rp + j];
-        z[(size_t)m * rank + j] = acc;
+        const uint16_t* c = zp + (size_t)m * 2 * rp + 64 * (j / 32) + (j % 32);
+        z[(size_t)m * rank + j] = (float)(double_from_bf16(c[0]) + double_from_bf16(c[32]));
       }
   }
   return SVDQ_OK;
