@@ -169,29 +169,33 @@ def main():
         torch.cuda.synchronize()
         return (np.array([a.elapsed_time(b) for a, b, _ in ev]), np.array([b.elapsed_time(c) for _, b, c in ev]))
 
-    def chunk(lay, wsb, steps):
-        """Back-to-back svdq_linear_forward calls between one pair of events."""
+    def chunk(lay, wsb, steps, fwd=None):
+        """Back-to-back forward calls between one pair of events."""
+        fwd = fwd or B.linear_forward
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         start.record(stream)
         for _ in range(steps):
-            B.linear_forward(lay, X, Y, wsb)
+            fwd(lay, X, Y, wsb)
         end.record(stream)
         return start, end
 
     for _ in range(args.warmup):
         B.linear_forward(layer0, X, Y, ws0)
         B.linear_forward(layer, X, Y, ws)
+        B.linear_forward_unfused(layer, X, Y, ws)
     torch.cuda.synchronize()
     # rank-0 (plain W4A4) chunks interleaved with the layer's, so both see the
     # same clocks; then the timed region proper: exactly `steps` forwards
     log("timing rank-0 (plain W4A4) and the layer, interleaved")
-    pairs = []
+    trip = []
     for _ in range(5):
-        pairs.append((chunk(layer0, ws0, 10), chunk(layer, ws, 10)))
+        trip.append((chunk(layer0, ws0, 10), chunk(layer, ws, 10),
+                     chunk(layer, ws, 10, B.linear_forward_unfused)))
     torch.cuda.synchronize()
-    ms0_chunks = np.array([a[0].elapsed_time(a[1]) / 10 for a, _ in pairs])
-    msr_chunks = np.array([b[0].elapsed_time(b[1]) / 10 for _, b in pairs])
+    ms0_chunks = np.array([a[0].elapsed_time(a[1]) / 10 for a, _, _ in trip])
+    msr_chunks = np.array([b[0].elapsed_time(b[1]) / 10 for _, b, _ in trip])
+    msu_chunks = np.array([c[0].elapsed_time(c[1]) / 10 for _, _, c in trip])
     log("timing the layer")
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -244,6 +248,7 @@ def main():
     traffic = measured_traffic(s.name if not args.fmt else f"{s.name}_{fmt}")
     t_step0 = float(np.median(ms0_chunks)) * 1e-3
     t_stepr = float(np.median(msr_chunks)) * 1e-3
+    t_stepu = float(np.median(msu_chunks)) * 1e-3
 
     cpu = None
     if not args.no_cpu_baseline and not args.skip_oracle:
@@ -278,6 +283,8 @@ def main():
         "kb_us": t_kb * 1e6,
         "lowrank_overhead": t_stepr / t_step0 - 1.0, "rank0_layer_us": t_step0 * 1e6,
         "layer_us_interleaved": t_stepr * 1e6,
+        "unfused": {"layer_us": t_stepu * 1e6, "lowrank_overhead": t_stepu / t_step0 - 1.0,
+                    "kernels": "quantize; down projection (second pass over X); W4A4 GEMM + bias; Y += Z L2'"},
         "rank0_ka_us": float(np.median(ka0)) * 1e3, "rank0_kb_us": float(np.median(kb0)) * 1e3,
         "parity": parity,
         "cpu_baseline": cpu,

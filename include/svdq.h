@@ -223,6 +223,17 @@ svdq_status svdq_gemm_lora_up(const svdq_layer* layer, const void* ws, size_t ws
 svdq_status svdq_linear_forward(const svdq_layer* layer, const uint16_t* X, int32_t M, uint16_t* Y,
                                 void* ws, size_t ws_bytes, void* stream);
 
+/* The same layer computed by four separate kernels, the arrangement whose
+ * cost the notes weigh against the fused kernels (Zhou notes, sec. 6.1: run
+ * unfused, the low-rank branch adds a large share of the 4-bit layer's time,
+ * mostly memory traffic): quantize only; the down projection as a second
+ * pass over X; the W4A4 GEMM with bias storing Y; then Y += Z L2' as a
+ * read-modify-write of Y.  Same layer, workspace, arguments and errors as
+ * svdq_linear_forward; Y is rounded to bf16 twice (after the GEMM and after
+ * the add), so it matches the fused result to bf16 rounding, not bitwise. */
+svdq_status svdq_linear_forward_unfused(const svdq_layer* layer, const uint16_t* X, int32_t M, uint16_t* Y,
+                                        void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------ misc ---------------------------------- */
 
 const char* svdq_status_str(svdq_status s);

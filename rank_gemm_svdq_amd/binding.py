@@ -16,7 +16,7 @@ __all__ = [
     "INT4", "MXFP4", "SvdqError", "lib", "status_str", "abi_version", "device_check",
     "layer_sizes", "workspace_layout", "workspace_bytes", "calib_absmax", "pack_host",
     "prepare", "attach_lora", "kernel_layout", "unpack_activations", "DeviceLayer",
-    "quantize_lora_down", "gemm_lora_up", "linear_forward", "fmt_code", "LIB_PATH",
+    "quantize_lora_down", "gemm_lora_up", "linear_forward", "linear_forward_unfused", "fmt_code", "LIB_PATH",
 ]
 
 INT4 = 0
@@ -94,10 +94,11 @@ def lib():
     L.svdq_quantize_lora_down.argtypes = [C.POINTER(Layer), vp, i32, vp, sz, vp]
     L.svdq_gemm_lora_up.argtypes = [C.POINTER(Layer), vp, sz, i32, vp, vp]
     L.svdq_linear_forward.argtypes = [C.POINTER(Layer), vp, i32, vp, vp, sz, vp]
+    L.svdq_linear_forward_unfused.argtypes = [C.POINTER(Layer), vp, i32, vp, vp, sz, vp]
     for name in ("svdq_device_check", "svdq_layer_sizes", "svdq_workspace_layout", "svdq_calib_absmax",
                  "svdq_pack_host", "svdq_prepare", "svdq_attach_lora", "svdq_kernel_layout",
                  "svdq_unpack_activations", "svdq_quantize_lora_down", "svdq_gemm_lora_up",
-                 "svdq_linear_forward"):
+                 "svdq_linear_forward", "svdq_linear_forward_unfused"):
         getattr(L, name).restype = C.c_int
     _lib = L
     return L
@@ -295,3 +296,10 @@ def linear_forward(layer, X, Y, ws, stream=None):
     M = X.shape[0]
     _check(lib().svdq_linear_forward(C.byref(layer.struct), X.data_ptr(), M, Y.data_ptr(), ws.data_ptr(),
                                      ws.numel(), _stream(stream)), "svdq_linear_forward")
+
+
+def linear_forward_unfused(layer, X, Y, ws, stream=None):
+    """The same layer as four separate kernels (svdq_linear_forward_unfused)."""
+    M = X.shape[0]
+    _check(lib().svdq_linear_forward_unfused(C.byref(layer.struct), X.data_ptr(), M, Y.data_ptr(), ws.data_ptr(),
+                                             ws.numel(), _stream(stream)), "svdq_linear_forward_unfused")

@@ -74,8 +74,9 @@ constexpr int KA_SL_MAX_K = 16384;   // 1/lambda is staged in LDS up to this K
 // flight in a register ring while it processes the current one; 1/lambda
 // comes from LDS when K allows.  The down projection multiplies the
 // smoothed x^ = x / lambda, split into bf16 hi + lo, by the bf16 factor
-// L1', so it runs on bf16 MFMA with fp32 accumulation.
-template <int FMT, int NT, bool SL>
+// L1', so it runs on bf16 MFMA with fp32 accumulation.  ZONLY drops the
+// quantisation (the unfused baseline's separate down-projection pass).
+template <int FMT, int NT, bool SL, bool ZONLY = false>
 __global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __restrict__ X, int M, int K,
                                                           const float* __restrict__ sinv,
                                                           const v8bf* __restrict__ l1k,
@@ -146,7 +147,9 @@ __global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __res
 #pragma unroll
     for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(xh[i]));
 
-    if constexpr (FMT == SVDQ_MXFP4_G32) {
+    if constexpr (ZONLY) {
+      // down projection only (the unfused baseline's separate pass over X)
+    } else if constexpr (FMT == SVDQ_MXFP4_G32) {
       // smallest e with amax <= 6 * 2^e, clamped to [-127, 127]
       const uint32_t ab = __float_as_uint(amax);
       const int ex = (int)(ab >> 23);
@@ -966,9 +969,56 @@ __global__ __launch_bounds__(I4_THREADS, 1) void kb_i4_kernel(
   }
 }
 
+
+// ------------------------------------------------- unfused baseline: up + add
+//
+// Y += Z L2' as its own pass over Y, for measuring what fusing the branch
+// into the GEMM epilogue saves.  One wave per 16 tokens x 64 out-features;
+// bf16 MFMA on the Z hi/lo halves and L2'^T rows, then a read-modify-write
+// of the bf16 output.
+template <int NTR>
+__global__ __launch_bounds__(256) void kup_kernel(const uint16_t* __restrict__ zp, const uint16_t* __restrict__ l2k,
+                                                  uint16_t* __restrict__ Y, int M, int N, int rpad) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int tiles_n = (N + 63) / 64, tiles = ((M + 15) / 16) * tiles_n;
+  const int tile = blockIdx.x * 4 + wave;
+  if (tile >= tiles) return;   // whole wave; no barriers in this kernel
+  const int m0 = (tile / tiles_n) * 16, n0 = (tile % tiles_n) * 64;
+  const int m = min(m0 + l16, M - 1);
+  v4f acc[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) acc[nt] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < NTR; ++u) {
+    const uint16_t* zr = zp + (size_t)m * 2 * rpad + 64 * u + 8 * g;
+    const v8bf bh = *reinterpret_cast<const v8bf*>(zr);
+    const v8bf bl = *reinterpret_cast<const v8bf*>(zr + 32);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int n = min(n0 + 16 * nt + l16, N - 1);
+      const v8bf af = *reinterpret_cast<const v8bf*>(l2k + (size_t)n * rpad + 32 * u + 8 * g);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bh, acc[nt], 0, 0, 0);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bl, acc[nt], 0, 0, 0);
+    }
+  }
+  // lane holds out-features n0 + 16 nt + 4 g + 0..3 of token m0 + l16
+  if (m0 + l16 >= M) return;
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int nn = n0 + 16 * nt + 4 * g;
+    if (nn >= N) continue;
+    uint2* yp = reinterpret_cast<uint2*>(Y + (size_t)(m0 + l16) * N + nn);
+    const uint2 y = *yp;
+    const uint32_t lo = bf16_rne(bf16_lo(y.x) + acc[nt][0]) | (bf16_rne(bf16_hi(y.x) + acc[nt][1]) << 16);
+    const uint32_t hi = bf16_rne(bf16_lo(y.y) + acc[nt][2]) | (bf16_rne(bf16_hi(y.y) + acc[nt][3]) << 16);
+    *yp = make_uint2(lo, hi);
+  }
+}
+
 // ------------------------------------------------------------ dispatch
 
-template <int FMT>
+template <int FMT, bool ZONLY = false>
 static hipError_t launch_ka(const svdq_layer& L, const uint16_t* X, int M, uint8_t* ws, const svdq_ws_layout& W,
                             hipStream_t st) {
   const int rp = rank_pad(L.rank);
@@ -980,10 +1030,10 @@ static hipError_t launch_ka(const svdq_layer& L, const uint16_t* X, int M, uint8
 #define SVDQ_KA(NTV)                                                                                        \
   do {                                                                                                      \
     if (L.K <= KA_SL_MAX_K)                                                                                 \
-      hipLaunchKernelGGL((ka_kernel<FMT, NTV, true>), grid, block, (size_t)L.K * 4, st, X, M, L.K, L.smooth_inv, \
+      hipLaunchKernelGGL((ka_kernel<FMT, NTV, true, ZONLY>), grid, block, (size_t)L.K * 4, st, X, M, L.K, L.smooth_inv, \
                          l1, xq, xs, z, rp);                                                                \
     else                                                                                                    \
-      hipLaunchKernelGGL((ka_kernel<FMT, NTV, false>), grid, block, 0, st, X, M, L.K, L.smooth_inv, l1, xq, xs, \
+      hipLaunchKernelGGL((ka_kernel<FMT, NTV, false, ZONLY>), grid, block, 0, st, X, M, L.K, L.smooth_inv, l1, xq, xs, \
                          z, rp);                                                                            \
   } while (0)
   switch (rp / 16) {
@@ -1141,6 +1191,43 @@ svdq_status svdq_linear_forward(const svdq_layer* layer, const uint16_t* X, int3
   if (!aligned16(X) || !aligned16(Y) || !aligned16(ws)) return SVDQ_ERR_ALIGN;
   if ((s = svdq_quantize_lora_down(layer, X, M, ws, ws_bytes, stream)) != SVDQ_OK) return s;
   return svdq_gemm_lora_up(layer, ws, ws_bytes, M, Y, stream);
+}
+
+svdq_status svdq_linear_forward_unfused(const svdq_layer* layer, const uint16_t* X, int32_t M, uint16_t* Y,
+                                        void* ws, size_t ws_bytes, void* stream) {
+  svdq_status s = check_layer(layer, M);
+  if (s != SVDQ_OK) return s;
+  if (!X || !Y || !ws) return SVDQ_ERR_ARG;
+  if (!aligned16(X) || !aligned16(Y) || !aligned16(ws)) return SVDQ_ERR_ALIGN;
+  svdq_ws_layout W;
+  if ((s = svdq_workspace_layout(M, layer->K, layer->rank, layer->fmt, &W)) != SVDQ_OK) return s;
+  if (ws_bytes < W.total) return SVDQ_ERR_WORKSPACE;
+  if ((s = device_ok()) != SVDQ_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* w8 = static_cast<uint8_t*>(ws);
+  svdq_layer plain = *layer;   // the same kernels with the low-rank branch left out
+  plain.rank = 0;
+  const bool mx = layer->fmt == SVDQ_MXFP4_G32;
+  hipError_t e = mx ? launch_ka<SVDQ_MXFP4_G32>(plain, X, M, w8, W, st) : launch_ka<SVDQ_INT4_G64>(plain, X, M, w8, W, st);
+  if (e == hipSuccess && layer->rank > 0)
+    e = mx ? launch_ka<SVDQ_MXFP4_G32, true>(*layer, X, M, w8, W, st)
+           : launch_ka<SVDQ_INT4_G64, true>(*layer, X, M, w8, W, st);
+  if (e == hipSuccess)
+    e = mx ? launch_kb<SVDQ_MXFP4_G32>(plain, w8, W, M, Y, st) : launch_kb<SVDQ_INT4_G64>(plain, w8, W, M, Y, st);
+  if (e == hipSuccess && layer->rank > 0) {
+    const int rp = rank_pad(layer->rank);
+    const int tiles = ((M + 15) / 16) * ((layer->N + 63) / 64);
+    const uint16_t* zp = reinterpret_cast<const uint16_t*>(w8 + W.z_off);
+    switch (rp / 32) {
+      case 1: hipLaunchKernelGGL(kup_kernel<1>, dim3((tiles + 3) / 4), dim3(256), 0, st, zp, layer->l2k, Y, M, layer->N, rp); break;
+      case 2: hipLaunchKernelGGL(kup_kernel<2>, dim3((tiles + 3) / 4), dim3(256), 0, st, zp, layer->l2k, Y, M, layer->N, rp); break;
+      case 3: hipLaunchKernelGGL(kup_kernel<3>, dim3((tiles + 3) / 4), dim3(256), 0, st, zp, layer->l2k, Y, M, layer->N, rp); break;
+      case 4: hipLaunchKernelGGL(kup_kernel<4>, dim3((tiles + 3) / 4), dim3(256), 0, st, zp, layer->l2k, Y, M, layer->N, rp); break;
+      default: return SVDQ_ERR_SHAPE;
+    }
+    e = hipGetLastError();
+  }
+  return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_DEVICE;
 }
 
 }  // extern "C"

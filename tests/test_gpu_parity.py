@@ -98,3 +98,25 @@ def test_workspace_reuse_and_determinism():
     run.ws.fill_(0x5A)
     run.forward()
     assert bool((run.Y == y1).all())
+
+
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+@pytest.mark.parametrize("M,K,N,rank", [(300, 1024, 400, 32), (17, 512, 272, 48), (130, 640, 144, 0)])
+def test_unfused_baseline(fmt, M, K, N, rank):
+    """The four-kernel baseline computes the same layer: within the
+    tolerance of the oracle, and close to the fused output (it rounds Y to
+    bf16 once more, before the low-rank add)."""
+    import torch
+    s = S.spec("tiny", M=M, K=K, N=N, rank=rank, fmt=fmt)
+    d = S.make_layer(s)
+    run = GpuRun(d, fmt, rank, s.alpha).forward()
+    y_fused = run.y()
+    B.linear_forward_unfused(run.layer, run.X, run.Y, run.ws)
+    torch.cuda.synchronize()
+    y_unf = run.y()
+    po = oracle_layer(d, fmt, rank, s.alpha)
+    of = F.forward(d["X"], po, d["bias"])
+    assert rel_fro(y_unf, of["y"]) <= Y_TOL
+    assert rel_fro(y_unf, y_fused) <= 4e-3
+    xq, xs, _ = run.activations()
+    assert np.array_equal(xq, of["xq"])

@@ -165,6 +165,10 @@ def test_error_codes_device_entry_points_validate_before_hip():
     assert lib.svdq_linear_forward(C.byref(L), 0x1008, 64, 0x2000, 0x3000, ws, None) == 3
     assert lib.svdq_linear_forward(C.byref(L), 0x1000, 64, 0x2000, 0x3000, ws - 1, None) == 5
     assert lib.svdq_linear_forward(C.byref(L), 0x1000, 0, 0x2000, 0x3000, ws, None) == 2
+    uf = lib.svdq_linear_forward_unfused
+    assert uf(None, 0x1000, 64, 0x2000, 0x3000, ws, None) == 1
+    assert uf(C.byref(L), 0x1000, 64, 0x2008, 0x3000, ws, None) == 3
+    assert uf(C.byref(L), 0x1000, 64, 0x2000, 0x3000, ws - 1, None) == 5
     bad = B.binding.Layer(256, 256, 40, 1, 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, None)
     assert lib.svdq_quantize_lora_down(C.byref(bad), 0x1000, 64, 0x3000, ws, None) == 2
     badf = B.binding.Layer(256, 256, 32, 3, 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, None)
