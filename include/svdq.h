@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define SVDQ_ABI_VERSION 1
+#define SVDQ_ABI_VERSION 2
 #define SVDQ_MAX_RANK 128   /* msModelSlim doc, svd_res: rank not above 128 recommended */
 
 typedef enum svdq_status {
@@ -144,7 +144,13 @@ typedef struct svdq_prepare_opts {
   int32_t        threads;         /* host threads; 0 = all available */
   int32_t        max_iters;       /* eigen solver iteration cap per value; 0 = default, < 0 forces
                                      SVDQ_ERR_NUMERIC (test hook) */
+  int32_t        residual_iters;  /* 0 or 1: one SVD; T > 1: residual iteration (below); <= SVDQ_MAX_RESIDUAL_ITERS */
+  int32_t        residual_early_stop; /* nonzero: stop at the first iteration worse than the best */
+  int32_t        has_beta;        /* nonzero: lambda uses the weight exponent `beta` below */
+  double         beta;            /* in [0, 1]; when has_beta == 0 the exponent is 1 - alpha */
 } svdq_prepare_opts;
+
+#define SVDQ_MAX_RESIDUAL_ITERS 64
 
 /* Canonical host outputs of svdq_prepare (caller-allocated). */
 typedef struct svdq_prepared {
@@ -156,15 +162,25 @@ typedef struct svdq_prepared {
   double*   sigma;        /* [rank] leading singular values of diag(lambda) W (optional) */
   uint8_t*  wq;           /* [N, K/2] canonical codes of R^T (required) */
   uint8_t*  ws;           /* [N, K/G] canonical scales: fp16 bits (INT4) or E8M0 bytes (MXFP4) (required) */
+  double*   iter_errors;  /* [max(1, residual_iters)] ||W~ - L1b L2b - Q(R)||_F of every iteration run,
+                             NaN for those not run (optional) */
+  int32_t*  best_iter;    /* index of the kept iteration (optional) */
 } svdq_prepared;
 
 /* Offline preparation of one layer (notes, Algorithm 1; AutoRound doc,
- * "Residual iteration" with residual_iters = 1):
- *   lambda_i = amaxX_i^alpha / amaxW_i^(1-alpha)  (Eq. (4); 1 when either is 0)
+ * "Residual iteration" and "Smooth search"):
+ *   lambda_i = amaxX_i^alpha / amaxW_i^beta        (Eq. (4), beta = 1 - alpha unless
+ *                                                   opts->has_beta; 1 when either is 0)
  *   W~ = diag(lambda) W                            (Eq. (3))
  *   L1 = U_r S_r, L2 = V_r^T of W~                 (Eq. (10), exact top-r)
  *   L1b, L2b = bf16(L1), bf16(L2); R = W~ - L1b L2b (fp64, stored fp32)
  *   codes/scales = RTN of R^T grouped along K in `fmt`.
+ * With residual_iters = T > 1, iteration t >= 2 takes the top-r split of
+ * W~ - Q(R_{t-1}) instead of W~ (Q = the RTN quantize-dequantize above) and
+ * forms R_t = W~ - L1b L2b again.  Every iteration is scored by the weight
+ * reconstruction error ||W~ - L1b L2b - Q(R_t)||_F and the best one is
+ * returned; with residual_early_stop the loop ends at the first iteration
+ * that scores worse than the best so far.
  * W: host [K, N] fp32; act_amax: host [K] fp32 (svdq_calib_absmax);
  * alpha in [0, 1].  A grouped projection (e.g. Q|K|V) is passed as the
  * column concatenation of its weights: one lambda, one shared L1, and the

@@ -28,6 +28,10 @@ O5 LoRA attach (Zhou notes sec. 7, Eq. (13)): L1' = [L1b | bf16(D A)],
 O6 weight packing: the quantizer of the chosen format applied to R32^T
    ([N, K], grouped along K).
 
+O-RI residual iterations (AutoRound doc, "Residual iteration"): refit the
+   branch to W~ - Q(R_prev), keep the candidate with the smallest
+   ||W~ - L1b L2b - Q(R)||_F, optionally stop at the first worse one.
+
 Pins (tests/test_oracle_prepare.py): Eq. (3) smoothing invariance (bit
 identical for power-of-two lambda), Eckart-Young tail energy, R = 0 at full
 rank, optimality against random rank-r competitors, a hand-computed lambda,
@@ -48,12 +52,15 @@ def calib_amax(x_cal):
     return np.max(np.abs(np.asarray(x_cal, dtype=np.float64)), axis=0).astype(np.float32)
 
 
-def smoothing_factors(act_amax, w, alpha):
-    """O1: lambda32 and inv_lambda (both fp32 [K])."""
+def smoothing_factors(act_amax, w, alpha, beta=None):
+    """O1: lambda32 and inv_lambda (both fp32 [K]).  The weight exponent is
+    beta (AutoRound doc, "Smooth search": lambda = x_span^alpha /
+    w_span^beta); None means 1 - alpha, Eq. (4) of the notes."""
     ax = np.asarray(act_amax, dtype=np.float64)
     aw = np.max(np.abs(np.asarray(w, dtype=np.float64)), axis=1)
+    b = 1.0 - alpha if beta is None else beta
     with np.errstate(divide="ignore", invalid="ignore"):
-        lam = ax ** alpha / aw ** (1.0 - alpha)
+        lam = ax ** alpha / aw ** b
     lam = np.where((ax == 0) | (aw == 0), 1.0, lam)
     lam32 = to_f32(lam)
     inv = (np.float32(1.0) / lam32).astype(np.float32)
@@ -73,23 +80,68 @@ def truncated_svd(wt, rank):
     return l1, l2, s
 
 
-def prepare(w, act_amax, alpha, rank, fmt, lora=None):
+def _candidate(wt, target, rank, fmt):
+    """One low-rank fit of `target` and the residual of wt it leaves (steps
+    O3-O6 with the fit taken on `target`)."""
+    l1, l2, sig = truncated_svd(target, rank)
+    l1b = round_bf16(l1)
+    l2b = round_bf16(l2)
+    r = wt - l1b @ l2b
+    r32 = to_f32(r)
+    q = quantize(r32.T.copy(), fmt)
+    err = float(np.linalg.norm(wt - l1b @ l2b - q["deq"].T))
+    return {"l1": l1, "l2": l2, "sigma": sig, "l1b": l1b, "l2b": l2b, "r": r, "r32": r32, "q": q, "err": err}
+
+
+def residual_iterations(wt, rank, fmt, iters=1, early_stop=False, keep_all=False):
+    """Residual iteration (AutoRound doc, "Residual iteration"; Zhou notes
+    sec. 5, the alternating update of the protected branch).
+
+    Iteration 1 fits the rank-r branch to W~ itself.  Every further
+    iteration fits it to W~ - Q(R_prev), Q the deployment RTN
+    quantize-dequantize of the previous residual, then takes the new
+    residual R = W~ - L1b L2b.  A candidate's error is the weight
+    reconstruction error ||W~ - L1b L2b - Q(R)||_F (smoothed coordinates;
+    the pages use it when no calibration output is scored).  The candidate
+    with the smallest error is kept; with early_stop the loop ends at the
+    first iteration whose error is larger than the best so far.
+    Returns (best candidate, list of errors per iteration run, all
+    candidates if keep_all).
+    """
+    cands, errors = [], []
+    best = None
+    target = wt
+    for it in range(max(1, int(iters))):
+        c = _candidate(wt, target, rank, fmt)
+        c["iteration"] = it
+        errors.append(c["err"])
+        if keep_all:
+            cands.append(c)
+        if best is None or c["err"] < best["err"]:
+            best = c
+        elif early_stop and c["err"] > best["err"]:
+            break
+        target = wt - c["q"]["deq"].T
+    return best, errors, cands
+
+
+def prepare(w, act_amax, alpha, rank, fmt, lora=None, residual_iters=1, early_stop=False, beta=None):
     """Prepare one layer.
 
     w: [K, N] weight values, act_amax: [K], alpha in [0, 1], rank r >= 0,
-    fmt 'int4' | 'mxfp4', lora: optional dict(A=[K, k], B=[k, N], strength=s).
+    fmt 'int4' | 'mxfp4', lora: optional dict(A=[K, k], B=[k, N], strength=s),
+    residual_iters / early_stop: see residual_iterations (1 = one SVD),
+    beta: weight exponent of lambda (None: 1 - alpha).
     Returns a dict of every intermediate the pins and the forward need.
     """
     w = np.asarray(w, dtype=np.float64)
-    lam32, inv = smoothing_factors(act_amax, w, alpha)
+    lam32, inv = smoothing_factors(act_amax, w, alpha, beta)
     wt = smooth_weight(w, lam32)
-    l1, l2, sig = truncated_svd(wt, rank)
-    l1b = round_bf16(l1)
-    l2b = round_bf16(l2)
+    c, errors, _ = residual_iterations(wt, rank, fmt, residual_iters, early_stop)
+    l1, l2, sig = c["l1"], c["l2"], c["sigma"]
+    l1b, l2b = c["l1b"], c["l2b"]
     r_exact = wt - l1 @ l2
-    r = wt - l1b @ l2b
-    r32 = to_f32(r)
-    wq = quantize(r32.T.copy(), fmt)
+    wq = c["q"]
     l1p, l2p = l1b, l2b
     if lora is not None:
         l1p, l2p = attach_lora(l1b, l2b, lam32, lora["A"], lora["B"], lora.get("strength", 1.0))
@@ -97,9 +149,10 @@ def prepare(w, act_amax, alpha, rank, fmt, lora=None):
         "lam32": lam32, "inv_lambda": inv, "w_tilde": wt, "sigma": sig,
         "l1": l1, "l2": l2, "l1b": l1b, "l2b": l2b,
         "l1p": l1p, "l2p": l2p,
-        "r_exact": r_exact, "r": r, "r32": r32,
+        "r_exact": r_exact, "r": c["r"], "r32": c["r32"],
         "wq_packed": wq["packed"], "ws": wq["scales"], "wq_codes": wq["codes"],
         "w_deq": wq["deq"], "fmt": fmt, "rank": rank,
+        "iter_errors": errors, "best_iter": c["iteration"],
     }
 
 

@@ -17,6 +17,7 @@ __all__ = [
     "layer_sizes", "workspace_layout", "workspace_bytes", "calib_absmax", "pack_host",
     "prepare", "attach_lora", "kernel_layout", "unpack_activations", "DeviceLayer",
     "quantize_lora_down", "gemm_lora_up", "linear_forward", "linear_forward_unfused", "fmt_code", "LIB_PATH",
+    "ABI_VERSION",
 ]
 
 INT4 = 0
@@ -56,16 +57,20 @@ class WsLayout(C.Structure):
 
 class PrepareOpts(C.Structure):
     _fields_ = [("lora_rank", C.c_int32), ("lora_a", C.c_void_p), ("lora_b", C.c_void_p),
-                ("lora_strength", C.c_float), ("threads", C.c_int32), ("max_iters", C.c_int32)]
+                ("lora_strength", C.c_float), ("threads", C.c_int32), ("max_iters", C.c_int32),
+                ("residual_iters", C.c_int32), ("residual_early_stop", C.c_int32),
+                ("has_beta", C.c_int32), ("beta", C.c_double)]
 
 
 class Prepared(C.Structure):
     _fields_ = [("lambda_", C.c_void_p), ("smooth_inv", C.c_void_p), ("l1", C.c_void_p),
                 ("l2", C.c_void_p), ("residual", C.c_void_p), ("sigma", C.c_void_p),
-                ("wq", C.c_void_p), ("ws", C.c_void_p)]
+                ("wq", C.c_void_p), ("ws", C.c_void_p), ("iter_errors", C.c_void_p),
+                ("best_iter", C.c_void_p)]
 
 
 _lib = None
+ABI_VERSION = 2   # SVDQ_ABI_VERSION of include/svdq.h that these structures mirror
 
 
 def lib():
@@ -80,6 +85,8 @@ def lib():
     L.svdq_status_str.restype = C.c_char_p
     L.svdq_status_str.argtypes = [C.c_int]
     L.svdq_abi_version.restype = i32
+    if L.svdq_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"libsvdq.so ABI {L.svdq_abi_version()} != {ABI_VERSION}: rebuild the library")
     L.svdq_device_check.argtypes = [i32]
     L.svdq_layer_sizes.argtypes = [i32, i32, i32, i32, C.POINTER(Sizes)]
     L.svdq_workspace_layout.argtypes = [i32, i32, i32, i32, C.POINTER(WsLayout)]
@@ -161,23 +168,28 @@ def pack_host(x, fmt):
     return codes, (scales.view(np.uint16) if f == INT4 else scales)
 
 
-def prepare(W, act_amax, alpha, rank, fmt, lora=None, threads=0, want_residual=False, max_iters=0):
-    """Offline prepare (svdq_prepare).  Returns canonical host arrays."""
+def prepare(W, act_amax, alpha, rank, fmt, lora=None, threads=0, want_residual=False, max_iters=0,
+            residual_iters=1, early_stop=False, beta=None):
+    """Offline prepare (svdq_prepare).  Returns canonical host arrays, the
+    per-iteration reconstruction errors and the index of the kept one."""
     W = np.ascontiguousarray(W, dtype=np.float32)
     act_amax = np.ascontiguousarray(act_amax, dtype=np.float32)
     K, N = W.shape
     f = fmt_code(fmt)
     k = 0 if lora is None else lora["A"].shape[1]
     rt = rank + k
+    T = max(1, int(residual_iters))
     out = {
         "lambda": np.empty(K, np.float32), "smooth_inv": np.empty(K, np.float32),
         "l1": np.empty((K, rt), np.uint16), "l2": np.empty((rt, N), np.uint16),
         "sigma": np.empty(max(rank, 1), np.float64), "wq": np.empty((N, K // 2), np.uint8),
         "ws": np.empty((N, (K // 64) * 2 if f == INT4 else K // 32), np.uint8),
+        "iter_errors": np.empty(T, np.float64), "best_iter": np.zeros(1, np.int32),
     }
     if want_residual:
         out["residual"] = np.empty((K, N), np.float32)
-    opts = PrepareOpts(0, None, None, 1.0, threads, max_iters)
+    opts = PrepareOpts(0, None, None, 1.0, threads, max_iters, int(residual_iters), int(bool(early_stop)),
+                       0 if beta is None else 1, 0.0 if beta is None else float(beta))
     keep = []
     if lora is not None:
         a = np.ascontiguousarray(lora["A"], np.float32)
@@ -188,12 +200,14 @@ def prepare(W, act_amax, alpha, rank, fmt, lora=None, threads=0, want_residual=F
     pr = Prepared(_p(out["lambda"]).value, _p(out["smooth_inv"]).value,
                   _p(out["l1"]).value if rt else None, _p(out["l2"]).value if rt else None,
                   _p(out["residual"]).value if want_residual else None, _p(out["sigma"]).value,
-                  _p(out["wq"]).value, _p(out["ws"]).value)
+                  _p(out["wq"]).value, _p(out["ws"]).value, _p(out["iter_errors"]).value,
+                  _p(out["best_iter"]).value)
     _check(lib().svdq_prepare(_p(W), _p(act_amax), K, N, float(alpha), rank, f, C.byref(opts), C.byref(pr)),
            "svdq_prepare")
     if f == INT4:
         out["ws"] = out["ws"].view(np.uint16)
     out["sigma"] = out["sigma"][:rank]
+    out["best_iter"] = int(out["best_iter"][0])
     out.update(K=K, N=N, rank=rt, fmt=f)
     return out
 

@@ -295,53 +295,71 @@ svdq_status svdq_attach_lora(const float* lambda, const uint16_t* l1, const uint
   return SVDQ_OK;
 }
 
-svdq_status svdq_prepare(const float* W, const float* act_amax, int32_t K, int32_t N, double alpha, int32_t rank,
-                         int32_t fmt, const svdq_prepare_opts* opts, svdq_prepared* out) {
-  if (!W || !act_amax || !out || !out->smooth_inv || !out->wq || !out->ws) return SVDQ_ERR_ARG;
-  if (!valid_fmt(fmt)) return SVDQ_ERR_UNSUPPORTED;
-  if (!valid_kn(K, N) || !valid_rank(rank) || rank > std::min(K, N)) return SVDQ_ERR_SHAPE;
-  if (!(alpha >= 0.0 && alpha <= 1.0)) return SVDQ_ERR_ARG;
-  const int32_t lk = opts ? opts->lora_rank : 0;
-  if (lk < 0 || lk % 16 || rank + lk > SVDQ_MAX_RANK) return SVDQ_ERR_SHAPE;
-  if (lk > 0 && (!opts->lora_a || !opts->lora_b)) return SVDQ_ERR_ARG;
-  if (rank + lk > 0 && (!out->l1 || !out->l2)) return SVDQ_ERR_ARG;
-  if (rank > 0 && std::min(K, N) > 16384) return SVDQ_ERR_SHAPE;
-  const int threads = default_threads(opts ? opts->threads : 0);
-  const int max_iters = opts ? opts->max_iters : 0;
-  if (!all_finite(W, (size_t)K * N) || !all_finite(act_amax, K)) return SVDQ_ERR_NUMERIC;
-  for (int32_t i = 0; i < K; ++i)
-    if (act_amax[i] < 0.0f) return SVDQ_ERR_ARG;
-  if (lk > 0 && (!all_finite(opts->lora_a, (size_t)K * lk) || !all_finite(opts->lora_b, (size_t)lk * N) ||
-                 !std::isfinite(opts->lora_strength)))
-    return SVDQ_ERR_NUMERIC;
+// Value of canonical code `nib` under its group's scale (exact in fp64).
+static double decode_int4(uint8_t nib, uint16_t s16) {
+  const int q = (nib & 8) ? (int)nib - 16 : (int)nib;
+  return (double)q * (double)float_from_half(s16);
+}
+static double decode_mxfp4(uint8_t nib, uint8_t e8m0) {
+  static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  const double v = std::ldexp(mag[nib & 7], (int)e8m0 - 127);
+  return (nib & 8) ? -v : v;
+}
 
-  // lambda (Eq. (4)); a zero statistic leaves the channel unscaled
-  std::vector<float> lam(K), inv(K);
-  for (int32_t i = 0; i < K; ++i) {
-    float aw = 0.0f;
-    const float* row = W + (size_t)i * N;
-    for (int32_t j = 0; j < N; ++j) aw = std::max(aw, std::fabs(row[j]));
-    const double ax = act_amax[i];
-    double l = 1.0;
-    if (ax > 0.0 && aw > 0.0f) l = std::pow(ax, alpha) / std::pow((double)aw, 1.0 - alpha);
-    lam[i] = (float)l;
-    if (!std::isfinite(lam[i]) || lam[i] == 0.0f) return SVDQ_ERR_NUMERIC;
-    inv[i] = 1.0f / lam[i];
-  }
-  // W~ = diag(lambda) W (exact in fp64)
-  std::vector<double> wt((size_t)K * N);
-  parallel_for(K, threads, [&](int64_t lo, int64_t hi) {
-    for (int64_t i = lo; i < hi; ++i)
-      for (int32_t j = 0; j < N; ++j) wt[(size_t)i * N + j] = (double)lam[i] * (double)W[(size_t)i * N + j];
+// Canonical codes [N, K/2] + scales -> decoded values transposed to [K, N].
+static void decode_transposed(const uint8_t* wq, const uint8_t* ws, int32_t N, int32_t K, int32_t fmt, int threads,
+                              double* out) {
+  constexpr int32_t NB = 32;
+  const int32_t G = group_size(fmt);
+  parallel_for((N + NB - 1) / NB, threads, [&](int64_t lo, int64_t hi) {
+    std::vector<double> blk((size_t)NB * K);
+    for (int64_t b = lo; b < hi; ++b) {
+      const int32_t n0 = (int32_t)b * NB, nn = std::min(NB, N - n0);
+      for (int32_t i = 0; i < nn; ++i) {
+        const int32_t n = n0 + i;
+        const uint8_t* codes = wq + (size_t)n * (K / 2);
+        for (int32_t k = 0; k < K; ++k) {
+          const uint8_t nib = (codes[k >> 1] >> ((k & 1) * 4)) & 0xF;
+          const size_t g = (size_t)n * (K / G) + k / G;
+          double v;
+          if (fmt == SVDQ_INT4_G64) {
+            uint16_t s16;
+            std::memcpy(&s16, ws + 2 * g, 2);
+            v = decode_int4(nib, s16);
+          } else {
+            v = decode_mxfp4(nib, ws[g]);
+          }
+          blk[(size_t)i * K + k] = v;
+        }
+      }
+      for (int32_t k = 0; k < K; ++k)
+        for (int32_t i = 0; i < nn; ++i) out[(size_t)k * N + n0 + i] = blk[(size_t)i * K + k];
+    }
   });
-  // top-r split and bf16 factors
-  std::vector<double> L1, L2, sig;
-  if (!truncated_svd(wt.data(), K, N, rank, threads, max_iters, L1, L2, sig)) return SVDQ_ERR_NUMERIC;
-  std::vector<uint16_t> l1b((size_t)K * rank), l2b((size_t)rank * N);
-  std::vector<double> l1d((size_t)K * rank), l2d((size_t)rank * N);
-  for (size_t i = 0; i < l1b.size(); ++i) { l1b[i] = bf16_from_double(L1[i]); l1d[i] = double_from_bf16(l1b[i]); }
-  for (size_t i = 0; i < l2b.size(); ++i) { l2b[i] = bf16_from_double(L2[i]); l2d[i] = double_from_bf16(l2b[i]); }
-  // R = W~ - L1b L2b in fp64, stored fp32; R^T feeds the packer
+}
+
+// One candidate of the residual iteration: bf16 factors of the top-r split
+// of `target`, R = W~ - L1b L2b (fp64, kept), its RTN codes and the error
+// ||W~ - L1b L2b - Q(R)||_F.
+struct Candidate {
+  std::vector<uint16_t> l1b, l2b;
+  std::vector<double> sig, r64, qr;  // qr: Q(R) in [K, N]
+  std::vector<uint8_t> wq, ws;
+  double err = 0.0;
+  int32_t iter = 0;
+};
+
+static svdq_status fit_candidate(const std::vector<double>& wt, const double* target, int32_t K, int32_t N,
+                                 int32_t rank, int32_t fmt, int threads, int max_iters, Candidate& c) {
+  std::vector<double> L1, L2;
+  if (!truncated_svd(target, K, N, rank, threads, max_iters, L1, L2, c.sig)) return SVDQ_ERR_NUMERIC;
+  c.l1b.resize((size_t)K * rank);
+  c.l2b.resize((size_t)rank * N);
+  std::vector<double> l1d(c.l1b.size()), l2d(c.l2b.size());
+  for (size_t i = 0; i < l1d.size(); ++i) { c.l1b[i] = bf16_from_double(L1[i]); l1d[i] = double_from_bf16(c.l1b[i]); }
+  for (size_t i = 0; i < l2d.size(); ++i) { c.l2b[i] = bf16_from_double(L2[i]); l2d[i] = double_from_bf16(c.l2b[i]); }
+  // R = W~ - L1b L2b in fp64; its fp32 transpose feeds the packer
+  c.r64.resize((size_t)K * N);
   std::vector<float> rt((size_t)N * K);
   parallel_for(K, threads, [&](int64_t lo, int64_t hi) {
     std::vector<double> acc(N);
@@ -353,28 +371,123 @@ svdq_status svdq_prepare(const float* W, const float* act_amax, int32_t K, int32
         for (int32_t j = 0; j < N; ++j) acc[j] += a * b[j];
       }
       for (int32_t j = 0; j < N; ++j) {
-        const float r = (float)(wt[(size_t)i * N + j] - acc[j]);
-        rt[(size_t)j * K + i] = r;
-        if (out->residual) out->residual[(size_t)i * N + j] = r;
+        const double r = wt[(size_t)i * N + j] - acc[j];
+        c.r64[(size_t)i * N + j] = r;
+        rt[(size_t)j * K + i] = (float)r;
       }
     }
   });
-  svdq_status st = svdq_pack_host(rt.data(), N, K, fmt, out->wq, out->ws);
+  const int G = group_size(fmt);
+  c.wq.resize((size_t)N * (K / 2));
+  c.ws.resize((size_t)N * (K / G) * (fmt == SVDQ_INT4_G64 ? 2 : 1));
+  const svdq_status st = svdq_pack_host(rt.data(), N, K, fmt, c.wq.data(), c.ws.data());
   if (st != SVDQ_OK) return st;
+  // Q(R) = decoded codes, transposed back to [K, N]; error = ||R - Q(R)||_F
+  c.qr.resize((size_t)K * N);
+  decode_transposed(c.wq.data(), c.ws.data(), N, K, fmt, threads, c.qr.data());
+  std::vector<double> rowerr(K);
+  parallel_for(K, threads, [&](int64_t lo, int64_t hi) {
+    for (int64_t k = lo; k < hi; ++k) {
+      double e = 0.0;
+      for (int32_t n = 0; n < N; ++n) {
+        const double d = c.r64[(size_t)k * N + n] - c.qr[(size_t)k * N + n];
+        e += d * d;
+      }
+      rowerr[k] = e;
+    }
+  });
+  double e = 0.0;
+  for (double v : rowerr) e += v;
+  c.err = std::sqrt(e);
+  return SVDQ_OK;
+}
+
+svdq_status svdq_prepare(const float* W, const float* act_amax, int32_t K, int32_t N, double alpha, int32_t rank,
+                         int32_t fmt, const svdq_prepare_opts* opts, svdq_prepared* out) {
+  if (!W || !act_amax || !out || !out->smooth_inv || !out->wq || !out->ws) return SVDQ_ERR_ARG;
+  if (!valid_fmt(fmt)) return SVDQ_ERR_UNSUPPORTED;
+  if (!valid_kn(K, N) || !valid_rank(rank) || rank > std::min(K, N)) return SVDQ_ERR_SHAPE;
+  if (!(alpha >= 0.0 && alpha <= 1.0)) return SVDQ_ERR_ARG;
+  const int32_t lk = opts ? opts->lora_rank : 0;
+  if (lk < 0 || lk % 16 || rank + lk > SVDQ_MAX_RANK) return SVDQ_ERR_SHAPE;
+  if (lk > 0 && (!opts->lora_a || !opts->lora_b)) return SVDQ_ERR_ARG;
+  if (rank + lk > 0 && (!out->l1 || !out->l2)) return SVDQ_ERR_ARG;
+  if (rank > 0 && std::min(K, N) > 16384) return SVDQ_ERR_SHAPE;
+  const int32_t iters = opts ? std::max(1, opts->residual_iters) : 1;
+  if (iters > SVDQ_MAX_RESIDUAL_ITERS) return SVDQ_ERR_ARG;
+  const bool early_stop = opts && opts->residual_early_stop;
+  const double beta = (opts && opts->has_beta) ? opts->beta : 1.0 - alpha;
+  if (!(beta >= 0.0 && beta <= 1.0)) return SVDQ_ERR_ARG;
+  const int threads = default_threads(opts ? opts->threads : 0);
+  const int max_iters = opts ? opts->max_iters : 0;
+  if (!all_finite(W, (size_t)K * N) || !all_finite(act_amax, K)) return SVDQ_ERR_NUMERIC;
+  for (int32_t i = 0; i < K; ++i)
+    if (act_amax[i] < 0.0f) return SVDQ_ERR_ARG;
+  if (lk > 0 && (!all_finite(opts->lora_a, (size_t)K * lk) || !all_finite(opts->lora_b, (size_t)lk * N) ||
+                 !std::isfinite(opts->lora_strength)))
+    return SVDQ_ERR_NUMERIC;
+
+  // lambda (Eq. (4), weight exponent beta); a zero statistic leaves the channel unscaled
+  std::vector<float> lam(K), inv(K);
+  for (int32_t i = 0; i < K; ++i) {
+    float aw = 0.0f;
+    const float* row = W + (size_t)i * N;
+    for (int32_t j = 0; j < N; ++j) aw = std::max(aw, std::fabs(row[j]));
+    const double ax = act_amax[i];
+    double l = 1.0;
+    if (ax > 0.0 && aw > 0.0f) l = std::pow(ax, alpha) / std::pow((double)aw, beta);
+    lam[i] = (float)l;
+    if (!std::isfinite(lam[i]) || lam[i] == 0.0f) return SVDQ_ERR_NUMERIC;
+    inv[i] = 1.0f / lam[i];
+  }
+  // W~ = diag(lambda) W (exact in fp64)
+  std::vector<double> wt((size_t)K * N);
+  parallel_for(K, threads, [&](int64_t lo, int64_t hi) {
+    for (int64_t i = lo; i < hi; ++i)
+      for (int32_t j = 0; j < N; ++j) wt[(size_t)i * N + j] = (double)lam[i] * (double)W[(size_t)i * N + j];
+  });
+  // residual iteration: candidate t fits W~ (t = 0) or W~ - Q(R_{t-1})
+  Candidate best, cur;
+  std::vector<double> target;
+  if (out->iter_errors)
+    for (int32_t t = 0; t < iters; ++t) out->iter_errors[t] = std::nan("");
+  for (int32_t t = 0; t < iters; ++t) {
+    const svdq_status st = fit_candidate(wt, t == 0 ? wt.data() : target.data(), K, N, rank, fmt, threads,
+                                         max_iters, cur);
+    if (st != SVDQ_OK) return st;
+    cur.iter = t;
+    if (out->iter_errors) out->iter_errors[t] = cur.err;
+    if (t + 1 < iters) {
+      target.resize((size_t)K * N);
+      parallel_for(K, threads, [&](int64_t lo, int64_t hi) {
+        for (size_t i = (size_t)lo * N; i < (size_t)hi * N; ++i) target[i] = wt[i] - cur.qr[i];
+      });
+    }
+    if (t == 0 || cur.err < best.err) {
+      std::swap(best, cur);
+    } else if (early_stop && cur.err > best.err) {
+      break;
+    }
+  }
+  std::memcpy(out->wq, best.wq.data(), best.wq.size());
+  std::memcpy(out->ws, best.ws.data(), best.ws.size());
+  if (out->residual)
+    for (size_t i = 0; i < best.r64.size(); ++i) out->residual[i] = (float)best.r64[i];
+  if (out->best_iter) *out->best_iter = best.iter;
   for (int32_t i = 0; i < K; ++i) {
     out->smooth_inv[i] = inv[i];
     if (out->lambda) out->lambda[i] = lam[i];
   }
   if (out->sigma)
-    for (int32_t j = 0; j < rank; ++j) out->sigma[j] = sig[j];
+    for (int32_t j = 0; j < rank; ++j) out->sigma[j] = best.sig[j];
   if (rank + lk > 0) {
     if (lk > 0) {
-      st = svdq_attach_lora(lam.data(), l1b.data(), l2b.data(), K, N, rank, opts->lora_a, opts->lora_b, lk,
-                            opts->lora_strength, out->l1, out->l2);
+      const svdq_status st = svdq_attach_lora(lam.data(), best.l1b.data(), best.l2b.data(), K, N, rank,
+                                              opts->lora_a, opts->lora_b, lk, opts->lora_strength, out->l1, out->l2);
       if (st != SVDQ_OK) return st;
     } else {
-      std::memcpy(out->l1, l1b.data(), l1b.size() * 2);
-      std::memcpy(out->l2, l2b.data(), l2b.size() * 2);
+      std::memcpy(out->l1, best.l1b.data(), best.l1b.size() * 2);
+      std::memcpy(out->l2, best.l2b.data(), best.l2b.size() * 2);
     }
   }
   return SVDQ_OK;

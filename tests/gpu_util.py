@@ -19,7 +19,7 @@ def bf16_to_f64(bits):
 class GpuRun:
     """Prepare a layer with the library, run the device path, read back."""
 
-    def __init__(self, d, fmt, rank, alpha, lora=None, use_bias=True, x=None):
+    def __init__(self, d, fmt, rank, alpha, lora=None, use_bias=True, x=None, **prep_kw):
         import torch
         self.torch = torch
         s = d["spec"]
@@ -28,7 +28,7 @@ class GpuRun:
         self.N = d["W"].shape[1]
         self.fmt = fmt
         amax = B.calib_absmax(S.bf16_bits_of(d["X_cal"]))
-        self.prep = B.prepare(d["W"], amax, alpha, rank, fmt, lora=lora)
+        self.prep = B.prepare(d["W"], amax, alpha, rank, fmt, lora=lora, **prep_kw)
         self.rank = self.prep["rank"]
         self.bias = d["bias"] if use_bias else None
         bias_bits = S.bf16_bits_of(self.bias) if use_bias else None
@@ -51,8 +51,8 @@ class GpuRun:
         return B.unpack_activations(ws_host, self.M, self.K, self.rank, self.fmt)
 
 
-def oracle_layer(d, fmt, rank, alpha, lora=None):
-    return P.prepare(d["W"], P.calib_amax(d["X_cal"]), alpha, rank, fmt, lora=lora)
+def oracle_layer(d, fmt, rank, alpha, lora=None, **prep_kw):
+    return P.prepare(d["W"], P.calib_amax(d["X_cal"]), alpha, rank, fmt, lora=lora, **prep_kw)
 
 
 def oracle_scales_bits(xs, fmt):

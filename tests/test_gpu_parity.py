@@ -120,3 +120,17 @@ def test_unfused_baseline(fmt, M, K, N, rank):
     assert rel_fro(y_unf, y_fused) <= 4e-3
     xq, xs, _ = run.activations()
     assert np.array_equal(xq, of["xq"])
+
+
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+def test_residual_iterated_layer(fmt):
+    """A layer prepared with residual iteration (refits to W~ - Q(R_prev),
+    the best of 6 kept) runs through the same device path: codes bit-exact,
+    Y within tolerance of the oracle's forward of its own iterated layer."""
+    s = S.spec("tiny", M=200, K=512, N=384, rank=32, fmt=fmt)
+    d = S.make_layer(s)
+    run = GpuRun(d, fmt, s.rank, s.alpha, residual_iters=6).forward()
+    po = oracle_layer(d, fmt, s.rank, s.alpha, residual_iters=6)
+    assert run.prep["best_iter"] == po["best_iter"]
+    np.testing.assert_allclose(run.prep["iter_errors"], po["iter_errors"], rtol=1e-9)
+    _check_full(run, po, d["X"], d["bias"])

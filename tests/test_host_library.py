@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     lib = B.lib()
     for n in sorted(names):
         assert hasattr(lib, n), n
-    assert B.abi_version() == 1
+    assert B.abi_version() == B.ABI_VERSION == 2
     assert B.status_str(0) == "ok"
 
 
@@ -62,9 +62,9 @@ def test_calib_absmax_matches_and_rejects_nan():
     assert e.value.status == 6
 
 
-def _compare_prepare(W, amax, alpha, rank, fmt, lora=None):
-    pc = B.prepare(W, amax, alpha, rank, fmt, lora=lora, want_residual=True)
-    po = P.prepare(W, amax, alpha, rank, fmt, lora=lora)
+def _compare_prepare(W, amax, alpha, rank, fmt, lora=None, **kw):
+    pc = B.prepare(W, amax, alpha, rank, fmt, lora=lora, want_residual=True, **kw)
+    po = P.prepare(W, amax, alpha, rank, fmt, lora=lora, **kw)
     assert np.array_equal(pc["lambda"], po["lam32"])
     assert np.array_equal(pc["smooth_inv"], po["inv_lambda"])
     l1, l2 = bf16_from_bits(pc["l1"]), bf16_from_bits(pc["l2"])
@@ -124,6 +124,36 @@ def test_prepare_lora_matches_oracle():
     assert np.array_equal(bf16_from_bits(pc["l2"])[32:], po["l2p"][32:])
 
 
+@pytest.mark.parametrize("fmt,rank,early", [("int4", 16, False), ("mxfp4", 48, False), ("mxfp4", 48, True)])
+def test_residual_iterations_match_oracle(fmt, rank, early):
+    # AutoRound doc, "Residual iteration": same error sequence, same kept
+    # iteration and the same codes as the oracle's loop
+    rng = np.random.default_rng(0)
+    W = rng.standard_normal((128, 64)).astype(np.float32)
+    amax = (np.abs(rng.standard_normal(128)) + 0.1).astype(np.float32)
+    pc, po = _compare_prepare(W, amax, 0.5, rank, fmt, residual_iters=10, early_stop=early)
+    n = len(po["iter_errors"])
+    np.testing.assert_allclose(pc["iter_errors"][:n], po["iter_errors"], rtol=1e-9)
+    assert np.isnan(pc["iter_errors"][n:]).all()
+    assert pc["best_iter"] == po["best_iter"]
+    assert (n < 10) == early
+
+
+def test_residual_iterations_one_is_default_and_beta_explicit():
+    s = S.spec("tiny")
+    d = S.make_layer(s, with_x=False)
+    amax = P.calib_amax(d["X_cal"])
+    a = B.prepare(d["W"], amax, 0.4, 16, "int4")
+    b = B.prepare(d["W"], amax, 0.4, 16, "int4", residual_iters=1, beta=0.6)
+    for k in ("lambda", "l1", "l2", "wq", "ws", "iter_errors"):
+        assert np.array_equal(a[k], b[k]), k
+    assert a["best_iter"] == 0
+    c = B.prepare(d["W"], amax, 0.4, 16, "int4", beta=0.0)
+    po = P.prepare(d["W"], amax, 0.4, 16, "int4", beta=0.0)
+    assert np.array_equal(c["lambda"], po["lam32"])
+    assert not np.array_equal(c["lambda"], a["lambda"])
+
+
 def test_error_codes_host():
     lib = B.lib()
     W = np.zeros((128, 64), np.float32)
@@ -138,6 +168,12 @@ def test_error_codes_host():
     with pytest.raises(B.SvdqError) as e:
         B.prepare(W, amax, 0.5, 24, "int4")
     assert e.value.status == 2
+    with pytest.raises(B.SvdqError) as e:
+        B.prepare(W, amax, 0.5, 16, "int4", residual_iters=65)
+    assert e.value.status == 1
+    with pytest.raises(B.SvdqError) as e:
+        B.prepare(W, amax, 0.5, 16, "int4", beta=1.5)
+    assert e.value.status == 1
     Wn = W.copy()
     Wn[3, 3] = np.nan
     with pytest.raises(B.SvdqError) as e:

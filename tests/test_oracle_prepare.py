@@ -1,12 +1,16 @@
 """Pins of the oracle's offline preparation: Eq. (4) special cases, Eq. (3)
 invariance, Eckart-Young (Eq. (10)), full-rank exactness, optimality, QKV
-grouping and the Eq. (13) LoRA identity (Zhou notes sec. 3, 5, 7; AutoRound
-doc processing flow)."""
+grouping, the Eq. (13) LoRA identity (Zhou notes sec. 3, 5, 7; AutoRound
+doc processing flow), and residual iteration (AutoRound doc, "Residual
+iteration": each refit is the top-r part of W~ - Q(R_prev), checked through
+an eigen-decomposition; rank 0 reduces to plain RTN; early stop cuts the full
+sequence at its first rise)."""
 import numpy as np
 import pytest
 
 from oracle import prepare as P
 from oracle import forward as F
+from oracle import quantizers as Q
 from oracle.rounding import round_bf16
 from rank_gemm_svdq_amd import synthetic as S
 
@@ -143,3 +147,95 @@ def test_lora_attach_eq13():
 def test_calib_amax():
     x = np.array([[1.0, -3.0], [-2.0, 0.5]])
     assert list(P.calib_amax(x)) == [2.0, 3.0]
+
+
+# ---------------------------------------------------------------- residual iteration
+# AutoRound doc, "Residual iteration": every outer iteration after the first
+# refits the rank-r branch to W~ - Q(R_prev) and re-quantizes the new
+# residual; the best candidate by weight reconstruction error is kept.
+
+def _ri_layer(seed, K=128, N=64, scale=1.0):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((K, N)) * scale).astype(np.float32)
+    ax = (np.abs(rng.standard_normal(K)) + 0.1).astype(np.float32)
+    return w, ax
+
+
+def _top_r_projection(a, r):
+    """Best rank-r approximation of a through the eigenvectors of a^T a
+    (a different route from the SVD the oracle takes)."""
+    ev, vec = np.linalg.eigh(a.T @ a)
+    v = vec[:, np.argsort(ev)[::-1][:r]]
+    return a @ v @ v.T
+
+
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+def test_residual_iteration_targets_and_errors(fmt):
+    w, ax = _ri_layer(11)
+    lam, _ = P.smoothing_factors(ax, w, 0.5)
+    wt = P.smooth_weight(w, lam)
+    best, errors, cands = P.residual_iterations(wt, 16, fmt, iters=4, keep_all=True)
+    assert len(errors) == len(cands) == 4
+    prev_deq = None
+    for t, c in enumerate(cands):
+        # the fit of iteration t is the top-r part of W~ (t = 0) or of W~ - Q(R_{t-1})
+        target = wt if t == 0 else wt - prev_deq
+        ref = _top_r_projection(target, 16)
+        assert np.linalg.norm(c["l1"] @ c["l2"] - ref) <= 1e-9 * np.linalg.norm(ref)
+        # residual and its quantization, decoded from the packed codes
+        np.testing.assert_array_equal(c["r"], wt - c["l1b"] @ c["l2b"])
+        sc = c["q"]["scales"]
+        deq_t = Q.dequantize_packed(c["q"]["packed"], sc, fmt).T
+        # error: explicit sum of squares over the columns
+        e2 = sum(float(np.dot(col, col)) for col in (wt - c["l1b"] @ c["l2b"] - deq_t).T)
+        assert abs(errors[t] - np.sqrt(e2)) <= 1e-12 * errors[t]
+        prev_deq = deq_t
+    assert best["err"] == min(errors) and best["iteration"] == int(np.argmin(errors))
+
+
+def test_residual_iteration_rank0_is_plain_rtn():
+    # with no branch every iteration leaves R = W~, so all errors are ||W~ - Q(W~)||
+    w, ax = _ri_layer(3)
+    lam, _ = P.smoothing_factors(ax, w, 0.5)
+    wt = P.smooth_weight(w, lam)
+    best, errors, _ = P.residual_iterations(wt, 0, "int4", iters=3, early_stop=True)
+    rtn = np.linalg.norm(wt - Q.quantize(P.to_f32(wt).T.copy(), "int4")["deq"].T)
+    assert errors == [errors[0]] * 3 and abs(errors[0] - rtn) <= 1e-12 * rtn
+    assert best["iteration"] == 0
+
+
+def test_residual_iteration_early_stop_is_prefix_of_full_run():
+    # a layer whose error sequence rises at iteration 5 and later falls below
+    # its earlier best: early stop must cut the full sequence right there
+    w, ax = _ri_layer(0)
+    lam, _ = P.smoothing_factors(ax, w, 0.5)
+    wt = P.smooth_weight(w, lam)
+    _, full, _ = P.residual_iterations(wt, 48, "mxfp4", iters=10)
+    best_es, es, _ = P.residual_iterations(wt, 48, "mxfp4", iters=10, early_stop=True)
+    rise = next(t for t in range(1, len(full)) if full[t] > min(full[:t]))
+    assert es == full[:rise + 1]
+    assert best_es["err"] == min(full[:rise + 1]) > min(full)
+
+
+def test_residual_iteration_reduces_error_on_outlier_layer():
+    # the point of iterating: the kept error is below the one-shot split
+    w, ax, L1 = _layer(2, 256, 192, 16)
+    L = P.prepare(w, ax, 0.5, 16, "int4", residual_iters=6)
+    assert L["iter_errors"][0] == pytest.approx(np.linalg.norm(L1["r"] - L1["w_deq"].T), rel=1e-12)
+    assert min(L["iter_errors"]) < 0.97 * L["iter_errors"][0]
+    assert L["best_iter"] > 0
+
+
+def test_beta_weight_exponent():
+    # Smooth search candidates: (alpha, 0) gives lambda = amaxX^alpha, and
+    # beta = 1 - alpha is Eq. (4)
+    rng = np.random.default_rng(0)
+    w = rng.standard_normal((8, 5))
+    ax = np.abs(rng.standard_normal(8)) + 0.5
+    lam0, _ = P.smoothing_factors(ax, w, 0.3, beta=0.0)
+    np.testing.assert_array_equal(lam0, np.float32(ax ** 0.3))
+    a, _ = P.smoothing_factors(ax, w, 0.3, beta=0.7)
+    b, _ = P.smoothing_factors(ax, w, 0.3)
+    np.testing.assert_array_equal(a, b)
+    lam00, _ = P.smoothing_factors(ax, w, 0.0, beta=0.0)
+    np.testing.assert_array_equal(lam00, np.ones(8, np.float32))
