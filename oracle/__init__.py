@@ -22,4 +22,4 @@ Parity status of every function is listed in the module headers; a function
 without an independent pin says "parity unpinned" there.
 """
 
-from . import rounding, quantizers, prepare, forward, accounting  # noqa: F401
+from . import rounding, quantizers, prepare, forward, accounting, search  # noqa: F401

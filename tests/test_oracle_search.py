@@ -1,0 +1,64 @@
+"""Pins of the oracle's smooth-factor grid search (AutoRound doc, "Smooth
+search"): the candidate set the section describes, the finite-minimum
+selection, and two layers whose winner is fixed by the mathematics."""
+import numpy as np
+import pytest
+
+from oracle import search as SR
+from oracle import prepare as P
+from rank_gemm_svdq_amd import synthetic as S
+
+
+def test_candidate_set_default_grid():
+    c = SR.candidates(20)
+    assert len(c) == 39                                    # the count the section states for G = 20
+    assert c[0] == (0.0, 0.0)
+    assert len(set(c)) == 39
+    beta0 = [a for a, b in c[1:] if b == 0.0]
+    paired = [(a, b) for a, b in c[1:] if b != 0.0]
+    assert beta0 == [k / 20 for k in range(1, 20)]
+    assert [a for a, _ in paired] == beta0
+    assert all(abs(a + b - 1.0) < 1e-15 for a, b in paired)
+    assert len(SR.candidates(2)) == 3
+    with pytest.raises(ValueError):
+        SR.candidates(1)
+
+
+def test_select_finite_minimum():
+    assert SR.select([0.3, 0.1, 0.2]) == 1
+    assert SR.select([np.nan, 0.5, np.inf, 0.5, 0.4]) == 4
+    assert SR.select([0.2, 0.2]) == 0                      # ties keep the earlier candidate
+    assert SR.select([np.nan, np.inf]) is None
+
+
+def test_exactly_representable_layer_selects_no_smoothing():
+    # X and W hold exact INT4 grid values with a full-scale element in every
+    # group of 64, so with lambda = 1 and no branch both quantize without
+    # loss and only the bf16 rounding of Y remains.  Channel ranges differ,
+    # so every other candidate has a non-uniform lambda and moves values off
+    # the grid.
+    rng = np.random.default_rng(3)
+    M, K, N = 64, 256, 128
+    cx = rng.integers(1, 8, K)                              # per-channel code range
+    cw = rng.integers(1, 8, K)
+    x = np.round(rng.uniform(-1, 1, (M, K)) * cx).astype(np.float64)
+    x[:, ::64] = 7.0
+    w = np.round(rng.uniform(-1, 1, (K, N)) * cw[:, None]) / 64.0
+    w[::64, :] = 7.0 / 64.0
+    best, pairs, errs = SR.smooth_search(w, x, 0, "int4", grids=4)
+    y_ref = x @ w
+    bf16_only = np.linalg.norm(P.round_bf16(y_ref) - y_ref) / np.linalg.norm(y_ref)
+    assert best == 0 and pairs[best] == (0.0, 0.0)
+    assert errs[0] == pytest.approx(bf16_only, rel=1e-12)
+    assert min(errs[1:]) > 2 * errs[0]
+
+
+def test_outlier_activations_select_smoothing():
+    # a few activation channels 40x larger than the rest: lambda = 1 leaves
+    # them to crush every other channel's 4-bit grid, so some alpha > 0 wins
+    s = S.spec("tiny", M=128, K=512, N=256, rank=16)
+    d = S.make_layer(s)
+    best, pairs, errs = SR.smooth_search(d["W"], d["X"], 16, "int4", grids=4)
+    assert pairs[best][0] > 0.0
+    assert errs[best] < 0.8 * errs[0]
+    assert all(np.isfinite(errs))
