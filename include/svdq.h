@@ -189,6 +189,52 @@ typedef struct svdq_prepared {
 svdq_status svdq_prepare(const float* W, const float* act_amax, int32_t K, int32_t N, double alpha,
                          int32_t rank, int32_t fmt, const svdq_prepare_opts* opts, svdq_prepared* out);
 
+/* ---------------------------- smooth search --------------------------- */
+
+/* Candidate exponent pairs of the smooth search (AutoRound doc, "Smooth
+ * search"): (0, 0), then (a/G, 0) for a = 1 .. G-1, then (a/G, 1 - a/G) for
+ * the same a, in that order.  Returns the count 2G - 1 (39 for G = 20), or 0
+ * if G is outside [2, 1000]; fills alpha[] and beta[] (host) when both are
+ * non-NULL. */
+int32_t svdq_smooth_candidates(int32_t grids, double* alpha, double* beta);
+
+typedef struct svdq_search_opts {
+  int32_t grids;                  /* G; 0 = 20 */
+  int32_t residual_iters;         /* per candidate, as in svdq_prepare_opts */
+  int32_t residual_early_stop;
+  int32_t threads;                /* host threads of each candidate's preparation; 0 = all */
+} svdq_search_opts;
+
+typedef struct svdq_search_result {
+  int32_t count;                  /* number of candidates scored (2G - 1) */
+  int32_t best;                   /* index of the winner in candidate order, -1 if none is finite */
+  double  alpha, beta;            /* the winner's exponents */
+  double* errors;                 /* host [count] scores, NaN where a candidate could not be
+                                     prepared (optional, caller-allocated) */
+} svdq_search_result;
+
+/* Device workspace bytes of svdq_smooth_search (0 on an invalid shape). */
+size_t svdq_search_workspace_bytes(int32_t M, int32_t K, int32_t N, int32_t rank, int32_t fmt);
+
+/* Smooth-factor grid search of one layer (AutoRound doc, "Smooth search").
+ * lambda_i = x_span_i^alpha / w_span_i^beta with x_span the per-channel
+ * absolute maximum of the calibration rows x_cal and w_span that of the
+ * weight rows.  Every candidate is prepared as svdq_prepare does (with
+ * opts' residual iteration), run through svdq_linear_forward on x_cal
+ * (no bias) and scored by ||Y - x_cal W||_F / ||x_cal W||_F, with the
+ * reference x_cal W computed on the device in fp32.  The finite smallest
+ * score wins (the earlier candidate on ties).
+ * W: host [K, N] fp32.  x_cal: device [M, K] bf16, 16-byte aligned.
+ * ws: device workspace of svdq_search_workspace_bytes(), 256-byte aligned.
+ * best (optional): receives the winner's lambda, smooth_inv, l1, l2, wq and
+ * ws as svdq_prepare would write them (other fields are ignored).
+ * Blocks the calling thread: it synchronizes `stream` once per candidate.
+ * Errors: ARG, SHAPE, ALIGN, WORKSPACE, UNSUPPORTED, NUMERIC (non-finite W
+ * or x_cal, an all-zero reference, or no finite score), DEVICE. */
+svdq_status svdq_smooth_search(const float* W, int32_t K, int32_t N, int32_t rank, int32_t fmt,
+                               const uint16_t* x_cal, int32_t M, const svdq_search_opts* opts, void* ws,
+                               size_t ws_bytes, void* stream, svdq_search_result* res, svdq_prepared* best);
+
 /* RTN quantization of a host [rows, K] fp32 matrix, grouped along K, into
  * canonical codes [rows, K/2] (element 2j in the low nibble of byte j) and
  * canonical scales [rows, K/G] (fp16 bits or E8M0 bytes).  Errors: ARG, SHAPE. */

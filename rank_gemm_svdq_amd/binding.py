@@ -17,7 +17,7 @@ __all__ = [
     "layer_sizes", "workspace_layout", "workspace_bytes", "calib_absmax", "pack_host",
     "prepare", "attach_lora", "kernel_layout", "unpack_activations", "DeviceLayer",
     "quantize_lora_down", "gemm_lora_up", "linear_forward", "linear_forward_unfused", "fmt_code", "LIB_PATH",
-    "ABI_VERSION",
+    "ABI_VERSION", "smooth_candidates", "search_workspace_bytes", "smooth_search", "SearchOpts", "SearchResult",
 ]
 
 INT4 = 0
@@ -69,6 +69,16 @@ class Prepared(C.Structure):
                 ("best_iter", C.c_void_p)]
 
 
+class SearchOpts(C.Structure):
+    _fields_ = [("grids", C.c_int32), ("residual_iters", C.c_int32), ("residual_early_stop", C.c_int32),
+                ("threads", C.c_int32)]
+
+
+class SearchResult(C.Structure):
+    _fields_ = [("count", C.c_int32), ("best", C.c_int32), ("alpha", C.c_double), ("beta", C.c_double),
+                ("errors", C.c_void_p)]
+
+
 _lib = None
 ABI_VERSION = 2   # SVDQ_ABI_VERSION of include/svdq.h that these structures mirror
 
@@ -102,10 +112,16 @@ def lib():
     L.svdq_gemm_lora_up.argtypes = [C.POINTER(Layer), vp, sz, i32, vp, vp]
     L.svdq_linear_forward.argtypes = [C.POINTER(Layer), vp, i32, vp, vp, sz, vp]
     L.svdq_linear_forward_unfused.argtypes = [C.POINTER(Layer), vp, i32, vp, vp, sz, vp]
+    L.svdq_smooth_candidates.restype = i32
+    L.svdq_smooth_candidates.argtypes = [i32, vp, vp]
+    L.svdq_search_workspace_bytes.restype = sz
+    L.svdq_search_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.svdq_smooth_search.argtypes = [vp, i32, i32, i32, i32, vp, i32, C.POINTER(SearchOpts), vp, sz, vp,
+                                     C.POINTER(SearchResult), C.POINTER(Prepared)]
     for name in ("svdq_device_check", "svdq_layer_sizes", "svdq_workspace_layout", "svdq_calib_absmax",
                  "svdq_pack_host", "svdq_prepare", "svdq_attach_lora", "svdq_kernel_layout",
                  "svdq_unpack_activations", "svdq_quantize_lora_down", "svdq_gemm_lora_up",
-                 "svdq_linear_forward", "svdq_linear_forward_unfused"):
+                 "svdq_linear_forward", "svdq_linear_forward_unfused", "svdq_smooth_search"):
         getattr(L, name).restype = C.c_int
     _lib = L
     return L
@@ -317,3 +333,53 @@ def linear_forward_unfused(layer, X, Y, ws, stream=None):
     M = X.shape[0]
     _check(lib().svdq_linear_forward_unfused(C.byref(layer.struct), X.data_ptr(), M, Y.data_ptr(), ws.data_ptr(),
                                              ws.numel(), _stream(stream)), "svdq_linear_forward_unfused")
+
+
+def smooth_candidates(grids=20):
+    """(alpha, beta) pairs of the smooth search, in scoring order."""
+    n = lib().svdq_smooth_candidates(int(grids), None, None)
+    if n == 0:
+        raise SvdqError(1, "svdq_smooth_candidates")
+    a, b = np.empty(n, np.float64), np.empty(n, np.float64)
+    lib().svdq_smooth_candidates(int(grids), _p(a), _p(b))
+    return list(zip(a.tolist(), b.tolist()))
+
+
+def search_workspace_bytes(M, K, N, rank, fmt):
+    return lib().svdq_search_workspace_bytes(M, K, N, rank, fmt_code(fmt))
+
+
+def smooth_search(W, X_cal, rank, fmt, grids=20, residual_iters=1, early_stop=False, threads=0, stream=None):
+    """Smooth-factor grid search (svdq_smooth_search).  W: host [K, N] fp32;
+    X_cal: device [M, K] bf16 bits (int16 tensor).  Returns the winner's
+    index and exponents, every candidate's score and the winner's canonical
+    prepared arrays (as prepare() returns them)."""
+    torch = _torch()
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    K, N = W.shape
+    M = X_cal.shape[0]
+    f = fmt_code(fmt)
+    n = lib().svdq_smooth_candidates(int(grids), None, None)
+    if n == 0:
+        raise SvdqError(1, "svdq_smooth_search")
+    wsb = search_workspace_bytes(M, K, N, rank, f)
+    if wsb == 0:
+        raise SvdqError(2, "svdq_smooth_search")
+    ws = torch.empty(wsb, dtype=torch.uint8, device=X_cal.device)
+    errors = np.empty(n, np.float64)
+    out = {
+        "lambda": np.empty(K, np.float32), "smooth_inv": np.empty(K, np.float32),
+        "l1": np.empty((K, rank), np.uint16), "l2": np.empty((rank, N), np.uint16),
+        "wq": np.empty((N, K // 2), np.uint8), "ws": np.empty((N, (K // 64) * 2 if f == INT4 else K // 32), np.uint8),
+    }
+    pr = Prepared(_p(out["lambda"]).value, _p(out["smooth_inv"]).value,
+                  _p(out["l1"]).value if rank else None, _p(out["l2"]).value if rank else None,
+                  None, None, _p(out["wq"]).value, _p(out["ws"]).value, None, None)
+    res = SearchResult(0, -1, 0.0, 0.0, _p(errors).value)
+    opts = SearchOpts(int(grids), int(residual_iters), int(bool(early_stop)), int(threads))
+    _check(lib().svdq_smooth_search(_p(W), K, N, rank, f, X_cal.data_ptr(), M, C.byref(opts), ws.data_ptr(),
+                                    ws.numel(), _stream(stream), C.byref(res), C.byref(pr)), "svdq_smooth_search")
+    if f == INT4:
+        out["ws"] = out["ws"].view(np.uint16)
+    out.update(K=K, N=N, rank=rank, fmt=f)
+    return {"best": res.best, "alpha": res.alpha, "beta": res.beta, "errors": errors, "prepared": out}

@@ -23,6 +23,7 @@ UNITS = [
     ("host_prepare.cpp", ["g++"] + HOST_FLAGS + ["-ffp-contract=off"]),
     ("host_eigen.cpp", ["g++"] + HOST_FLAGS + ["-ffp-contract=fast"]),
     ("device_kernels.hip", [HIPCC] + DEVICE_FLAGS),
+    ("device_search.hip", [HIPCC] + DEVICE_FLAGS),
 ]
 
 

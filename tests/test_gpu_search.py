@@ -1,0 +1,67 @@
+"""GPU parity of the smooth-factor grid search (AutoRound doc, "Smooth
+search") against the oracle's search on the same calibration rows.
+
+The library scores a candidate with the device forward, the oracle with its
+fp64 forward.  By the triangle inequality a candidate's two scores differ by
+at most ||Y_dev - Y_oracle||_F / ||X W||_F, which the forward parity bounds
+by its 5e-3 tolerance (scaled by ||Y|| / ||X W||, about 1 here), so every
+score must agree within that bound, and the library's winner must score,
+under the oracle, within twice the bound of the oracle's winner."""
+import numpy as np
+import pytest
+
+import rank_gemm_svdq_amd as B
+from rank_gemm_svdq_amd import synthetic as S
+from oracle import search as SR
+
+pytestmark = pytest.mark.gpu
+TOL = 5e-3
+
+
+def _xdev(x):
+    import torch
+    return torch.from_numpy(S.bf16_bits_of(x).view(np.int16)).cuda()
+
+
+def _search(w, x, rank, fmt, grids):
+    r = B.smooth_search(w, _xdev(x), rank, fmt, grids=grids)
+    ob, pairs, oerr = SR.smooth_search(w, x, rank, fmt, grids=grids)
+    assert B.smooth_candidates(grids) == pairs
+    assert np.all(np.abs(r["errors"] - np.asarray(oerr)) <= TOL), (r["errors"], oerr)
+    assert oerr[r["best"]] <= oerr[ob] + 2 * TOL
+    assert (r["alpha"], r["beta"]) == pairs[r["best"]]
+    # the returned layer is the winner prepared by svdq_prepare
+    amax = B.calib_absmax(S.bf16_bits_of(x))
+    p = B.prepare(w, amax, r["alpha"], rank, fmt, beta=r["beta"])
+    for k in ("lambda", "smooth_inv", "wq", "ws", "l1", "l2"):
+        assert np.array_equal(r["prepared"][k], p[k]), k
+    return r, ob, oerr
+
+
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+def test_search_small_grid(fmt):
+    s = S.spec("tiny", M=128, K=512, N=256, rank=16, fmt=fmt)
+    d = S.make_layer(s)
+    r, ob, _ = _search(d["W"], d["X"], 16, fmt, 4)
+    assert r["alpha"] > 0.0          # the outlier channels make smoothing win
+
+
+def test_search_default_grid_39_candidates():
+    s = S.spec("tiny", M=96, K=384, N=256, rank=16, fmt="int4")
+    d = S.make_layer(s)
+    r, _, _ = _search(d["W"], d["X"], 16, "int4", 20)
+    assert len(r["errors"]) == 39 and np.isfinite(r["errors"]).all()
+
+
+def test_search_exact_layer_keeps_unsmoothed():
+    # exact INT4-grid operands (see the oracle pin): only (0, 0) is lossless
+    rng = np.random.default_rng(3)
+    M, K, N = 64, 256, 128
+    cx, cw = rng.integers(1, 8, K), rng.integers(1, 8, K)
+    x = np.round(rng.uniform(-1, 1, (M, K)) * cx)
+    x[:, ::64] = 7.0
+    w = np.round(rng.uniform(-1, 1, (K, N)) * cw[:, None]) / 64.0
+    w[::64, :] = 7.0 / 64.0
+    r, ob, oerr = _search(w.astype(np.float32), x, 0, "int4", 4)
+    assert r["best"] == ob == 0
+    assert r["errors"][0] == pytest.approx(oerr[0], rel=1e-9)

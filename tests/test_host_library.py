@@ -304,3 +304,40 @@ def test_mxfp4_scale_layout_positions():
             assert row[i] == sc[n, b]
             seen[i] = True
     assert np.all(row[~seen] == 127)
+
+
+def test_smooth_candidates_match_oracle():
+    from oracle import search as SR
+    for g in (2, 4, 20, 33):
+        assert B.smooth_candidates(g) == SR.candidates(g)       # same doubles, same order
+    assert B.lib().svdq_smooth_candidates(1, None, None) == 0
+    assert B.lib().svdq_smooth_candidates(1001, None, None) == 0
+
+
+def test_smooth_search_validates_before_hip():
+    import ctypes as C
+    lib = B.lib()
+    W = np.ones((512, 256), np.float32)
+    res = B.SearchResult(0, -1, 0.0, 0.0, None)
+    opts = B.SearchOpts(4, 1, 0, 0)
+    fake = C.c_void_p(1 << 20)            # never dereferenced: every case fails validation first
+    ws_ok = B.search_workspace_bytes(128, 512, 256, 16, "int4")
+    assert ws_ok > 0 and B.search_workspace_bytes(0, 512, 256, 16, "int4") == 0
+
+    def call(w=W.ctypes.data_as(C.c_void_p), K=512, N=256, rank=16, fmt=0, x=fake, M=128, o=opts, ws=fake,
+             wsb=ws_ok, r=res):
+        return lib.svdq_smooth_search(w, K, N, rank, fmt, x, M, C.byref(o) if o is not None else None, ws, wsb,
+                                      None, C.byref(r) if r is not None else None, None)
+    assert call(w=None) == 1
+    assert call(r=None) == 1
+    assert call(o=B.SearchOpts(1, 1, 0, 0)) == 1
+    assert call(fmt=7) == 4
+    assert call(K=500) == 2
+    assert call(rank=24) == 2
+    assert call(M=0) == 2
+    assert call(x=C.c_void_p((1 << 20) + 2)) == 3
+    assert call(ws=C.c_void_p((1 << 20) + 16)) == 3
+    assert call(wsb=ws_ok - 1) == 5
+    Wn = W.copy()
+    Wn[1, 1] = np.inf
+    assert call(w=Wn.ctypes.data_as(C.c_void_p)) == 6
