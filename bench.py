@@ -108,7 +108,15 @@ def main():
                     help="print the rocprofv3 commands whose output --summarize-profiles reads")
     ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
                     help="summarise rocprofv3 output under DIR into profiles/ (no GPU needed)")
+    ap.add_argument("--smooth-search", type=int, metavar="G", default=0,
+                    help="time the smooth-factor grid search (2G-1 candidates) of the workload's layer on "
+                         "its calibration rows and print that JSON line instead")
+    ap.add_argument("--residual-iters", type=int, metavar="T", default=0,
+                    help="time the host preparation of the workload's layer with T residual iterations "
+                         "and print that JSON line instead")
     args = ap.parse_args()
+    if args.residual_iters:
+        return bench_residual(args)
     if args.print_profile_commands:
         cfg = args.config + (f" --fmt {args.fmt}" if args.fmt else "")
         for k, c in profile_commands(args.print_profile_commands, cfg).items():
@@ -134,6 +142,8 @@ def main():
 
     over = {"fmt": args.fmt} if args.fmt else {}
     s = S.spec(args.config, **over)
+    if args.smooth_search:
+        return bench_search(args, s)
     M, K, N, fmt = s.M, s.K, s.N, s.fmt
     log(f"workload {s.name}: M={M} K={K} N={N} rank={s.rank}+{s.lora_rank} fmt={fmt}")
     d = S.make_layer(s)
@@ -303,6 +313,88 @@ PROFILE_STEPS = {
     "write": "--pmc WRITE_SIZE --output-format csv -d {dir}/write -o run -- "
              "python -u bench.py --config {config} --steps 3 --warmup 1 --skip-oracle --calib-copy",
 }
+
+
+def bench_residual(args):
+    """Host preparation with residual iteration: seconds per iteration and
+    the weight reconstruction error of every iteration (no GPU needed)."""
+    import rank_gemm_svdq_amd as B
+    from rank_gemm_svdq_amd import synthetic as S
+
+    over = {"fmt": args.fmt} if args.fmt else {}
+    s = S.spec(args.config, **over)
+    d = S.make_layer(s, with_x=False)
+    amax = B.calib_absmax(S.bf16_bits_of(d["X_cal"]))
+    T = args.residual_iters
+    t0 = time.perf_counter()
+    p1 = B.prepare(d["W"], amax, s.alpha, s.rank, s.fmt)
+    t1 = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    p = B.prepare(d["W"], amax, s.alpha, s.rank, s.fmt, residual_iters=T)
+    tt = time.perf_counter() - t0
+    e = p["iter_errors"]
+    assert e[0] == p1["iter_errors"][0]
+    out = {
+        "metric": "residual_iteration_seconds", "value": (tt - t1) / max(T - 1, 1), "unit": "s/iteration",
+        "n_gpus": 0, "higher_is_better": False, "data": "synthetic",
+        "config": {"workload": s.name, "K": s.K, "N": s.N, "rank": s.rank, "fmt": s.fmt, "residual_iters": T},
+        "prepare_one_iteration_s": t1, "prepare_total_s": tt, "iter_errors": [float(v) for v in e],
+        "best_iter": p["best_iter"], "error_reduction": float(1.0 - min(e) / e[0]),
+        "host_threads": int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_search(args, s):
+    """The smooth-factor grid search of one layer: host preparation of every
+    candidate plus its scoring forward on the calibration rows."""
+    import torch
+    import rank_gemm_svdq_amd as B
+    from rank_gemm_svdq_amd import synthetic as S
+
+    d = S.make_layer(s, with_x=False)
+    xc = torch.from_numpy(S.bf16_bits_of(d["X_cal"]).view(np.int16)).cuda()
+    mc = xc.shape[0]
+    g = args.smooth_search
+    n = len(B.smooth_candidates(g))
+    log(f"smooth search {s.name}: {n} candidates, calibration rows {mc}, K={s.K} N={s.N} rank={s.rank} {s.fmt}")
+    t0 = time.perf_counter()
+    amax = B.calib_absmax(S.bf16_bits_of(d["X_cal"]))
+    B.prepare(d["W"], amax, s.alpha, s.rank, s.fmt)
+    t_prep = time.perf_counter() - t0
+    log(f"one host preparation {t_prep:.2f} s")
+    # scoring forward alone on the calibration rows
+    prep = B.prepare(d["W"], amax, s.alpha, s.rank, s.fmt)
+    lay = B.DeviceLayer(prep)
+    Y = torch.empty((mc, s.N), dtype=torch.int16, device="cuda")
+    ws = lay.workspace(mc)
+    for _ in range(3):
+        B.linear_forward(lay, xc, Y, ws)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        B.linear_forward(lay, xc, Y, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    fwd_ms = e0.elapsed_time(e1) / 10
+    del lay, ws, Y
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    r = B.smooth_search(d["W"], xc, s.rank, s.fmt, grids=g)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"search {wall:.1f} s; winner alpha={r['alpha']} beta={r['beta']} score={r['errors'][r['best']]:.4e}")
+    out = {
+        "metric": "smooth_search_seconds", "value": wall, "unit": "s", "n_gpus": 1,
+        "higher_is_better": False, "dtype": "u4" if s.fmt == "int4" else "fp4", "data": "synthetic",
+        "config": {"workload": s.name, "M_cal": int(mc), "K": s.K, "N": s.N, "rank": s.rank, "fmt": s.fmt,
+                   "grids": g, "candidates": n},
+        "per_candidate_s": wall / n, "host_prepare_s": t_prep, "scoring_forward_ms": fwd_ms,
+        "host_threads": int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count(),
+        "best": {"alpha": r["alpha"], "beta": r["beta"], "score": float(r["errors"][r["best"]])},
+        "scores": [float(e) for e in r["errors"]],
+    }
+    print(json.dumps(out), flush=True)
 
 
 def profile_commands(d, config):

@@ -141,7 +141,8 @@ typedef struct svdq_prepare_opts {
   const float*   lora_a;          /* host [K, k] (adapter A, unsmoothed coordinates) */
   const float*   lora_b;          /* host [k, N] */
   float          lora_strength;   /* absorbed into B */
-  int32_t        threads;         /* host threads; 0 = all available */
+  int32_t        threads;         /* host threads; 0 = OMP_NUM_THREADS if set, else the CPUs the
+                                     process may run on (at most 64) */
   int32_t        max_iters;       /* eigen solver iteration cap per value; 0 = default, < 0 forces
                                      SVDQ_ERR_NUMERIC (test hook) */
   int32_t        residual_iters;  /* 0 or 1: one SVD; T > 1: residual iteration (below); <= SVDQ_MAX_RESIDUAL_ITERS */
@@ -202,7 +203,7 @@ typedef struct svdq_search_opts {
   int32_t grids;                  /* G; 0 = 20 */
   int32_t residual_iters;         /* per candidate, as in svdq_prepare_opts */
   int32_t residual_early_stop;
-  int32_t threads;                /* host threads of each candidate's preparation; 0 = all */
+  int32_t threads;                /* host threads of each preparation; 0 as in svdq_prepare_opts */
 } svdq_search_opts;
 
 typedef struct svdq_search_result {

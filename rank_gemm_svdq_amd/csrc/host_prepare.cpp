@@ -6,8 +6,11 @@
 // products and divisions exactly (the quantized codes and scales are
 // specified bit for bit).
 
+#include <sched.h>
+
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstdint>
 #include <cstring>
 #include <thread>
@@ -39,10 +42,19 @@ bool geometry(int32_t K, int32_t N, int32_t rank, int32_t fmt, Geometry* g) {
 
 int32_t choose_zsplit(int32_t, int32_t) { return 1; }   // K-A reduces Z inside each block
 
+// 0 requested: OMP_NUM_THREADS when set, else the CPUs this process may run
+// on; at most 64.
 int default_threads(int requested) {
   if (requested > 0) return requested;
-  unsigned h = std::thread::hardware_concurrency();
-  return h ? (int)std::min(h, 64u) : 1;
+  if (const char* env = std::getenv("OMP_NUM_THREADS")) {
+    const long v = std::strtol(env, nullptr, 10);
+    if (v > 0) return (int)std::min(v, 64L);
+  }
+  cpu_set_t set;
+  CPU_ZERO(&set);
+  int h = sched_getaffinity(0, sizeof(set), &set) == 0 ? CPU_COUNT(&set) : 0;
+  if (h <= 0) h = (int)std::thread::hardware_concurrency();
+  return h > 0 ? std::min(h, 64) : 1;
 }
 
 // ----------------------------------------------------------- conversions
