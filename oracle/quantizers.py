@@ -34,10 +34,23 @@ E2M1 magnitudes by code 0..7: 0, 0.5, 1, 1.5, 2, 3, 4, 6.
 Packing: two codes per byte (Zhou notes, Eq. (12) counts mn/2 bytes);
 element 2j goes to the low nibble of byte j, K contiguous, row-major.
 
+W8A8 (Zhou notes, sec. 8: the 8-bit setting quantizes activations per
+token, dynamically, and weights per channel, with rank 16).  One scale per
+row over all K values (a token row of x^, an out-feature row of R^T):
+    amax = max |z| over the row
+    s    = fp32(amax / 127)                    (fp32 scale, stored as is)
+    if s == 0: every code is 0
+    else: rcp = fp32(1 / s); q = clamp(rint(fp32(z * rcp)), -127, 127)
+Readings: the symmetric range -127..127 (as INT4 leaves out -8, the 8-bit
+code leaves out -128), an fp32 scale (the pages fix 16-bit scales only for
+the 4-bit groups), and the same reciprocal-then-multiply division as INT4.
+Codes are stored one signed byte per element, K contiguous, row-major.
+
 Pins (tests/test_oracle_quantizers.py): the worked example of Zhou notes
 sec. 2.2 (range 7 gives step 1; range 1 gives step 1/7), brute-force argmin
-over the 15 INT4 codes and the 8 E2M1 magnitudes, brute-force search for e,
-the no-clipping property and the Eq. (9) per-group error bound.
+over the 15 INT4 codes, the 255 8-bit codes and the 8 E2M1 magnitudes,
+brute-force search for e, the no-clipping property and the Eq. (9) per-group
+error bound (per row for 8-bit).
 """
 
 import numpy as np
@@ -75,6 +88,28 @@ def quantize_int4(z):
         q = np.clip(np.rint(y), -7, 7)
     q = np.where((s16 == 0)[:, :, None], 0.0, q)
     return q.astype(np.int8).reshape(z.shape), s16
+
+
+def quantize_w8(z):
+    """8-bit RTN with one fp32 scale per row.
+
+    z: [rows, K] fp32.  Returns (codes int8 [rows, K] in -127..127, scales
+    float32 [rows]).
+    """
+    z = np.asarray(z, dtype=np.float32)
+    amax = np.max(np.abs(z), axis=1)                        # fp32, exact
+    s = (amax / np.float32(127.0)).astype(np.float32)       # fp32 division
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rcp = (np.float32(1.0) / s).astype(np.float32)
+        y = (z * rcp[:, None]).astype(np.float32)           # fp32 product
+        q = np.clip(np.rint(y), -127, 127)
+    q = np.where((s == 0)[:, None], 0.0, q)
+    return q.astype(np.int8), s
+
+
+def decode_w8(codes, scales):
+    """q * s for every element.  codes [rows, K] int, scales [rows] fp32."""
+    return np.asarray(codes, dtype=np.float64) * np.asarray(scales, dtype=np.float64)[:, None]
 
 
 def mxfp4_block_exponent(amax):
@@ -173,9 +208,14 @@ def unpack_nibbles(packed):
 def quantize(z, fmt):
     """Quantize [rows, K] fp32 values in the named format.
 
-    Returns a dict with 'packed' (u8 [rows, K/2]), 'scales' (fp16 values as
-    float64 for int4, E8M0 bytes for mxfp4) and 'deq' (fp64 decoded values).
+    Returns a dict with 'packed' (u8 [rows, K/2] for the 4-bit formats; for
+    w8a8 the int8 codes viewed as u8 [rows, K]), 'scales' (fp16 values as
+    float64 for int4, E8M0 bytes for mxfp4, fp32 per row for w8a8) and 'deq'
+    (fp64 decoded values).
     """
+    if fmt == "w8a8":
+        q, s = quantize_w8(z)
+        return {"packed": q.view(np.uint8), "scales": s, "codes": q, "deq": decode_w8(q, s)}
     if fmt == "int4":
         q, s = quantize_int4(z)
         return {"packed": pack_nibbles(int4_nibbles(q)), "scales": s,
@@ -189,6 +229,8 @@ def quantize(z, fmt):
 
 def dequantize_packed(packed, scales, fmt):
     """fp64 decoded matrix from packed codes and scales."""
+    if fmt == "w8a8":
+        return decode_w8(np.asarray(packed, dtype=np.uint8).view(np.int8), scales)
     nib = unpack_nibbles(packed)
     if fmt == "int4":
         return decode_int4(nibble_to_int4(nib), scales)

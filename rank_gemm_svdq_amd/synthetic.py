@@ -23,6 +23,8 @@ Workloads (M tokens, K in-features, N out-features):
   flux_lora    8192 x 3072 -> 12288, X as flux_qkv, W as flux_mlp_up, rank 32
                plus a rank-16 LoRA (A ~ N(0, 1/3072), B ~ N(0, 0.01/16),
                strength 1), MXFP4 and INT4
+  flux_qkv_w8a8 the flux_qkv shapes and distributions (own seed), rank 16,
+               8-bit per-token activations and per-channel weights
 A bias ~ N(0, 0.1^2) is drawn for every layer.  The calibration draw has
 min(M, 1024) rows from the same distribution and the same outlier channels.
 """
@@ -71,6 +73,9 @@ SPECS = {
     "flux_lora": LayerSpec("flux_lora", 4, 8192, 3072, 12288, 32, "mxfp4",
                            x_outlier_channels=31, x_outlier_scale=50.0,
                            lora_rank=16, lora_b_var=0.01 / 16),
+    "flux_qkv_w8a8": LayerSpec("flux_qkv_w8a8", 5, 4096, 3072, 9216, 16, "w8a8",
+                               x_outlier_channels=31, x_outlier_scale=50.0,
+                               qkv_splits=(3072, 3072, 3072)),
 }
 
 

@@ -18,7 +18,7 @@ def _tiny(fmt="int4", **kw):
     return s, d, L
 
 
-@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4", "w8a8"])
 def test_eq8_error_identity(fmt):
     s, d, L = _tiny(fmt)
     x = d["X"].astype(np.float64)
@@ -55,6 +55,26 @@ def test_gemm_equals_int64_brute_force():
         ig = qx[:, 64 * g:64 * g + 64] @ qw[:, 64 * g:64 * g + 64].T   # exact int64
         y += out["xs"][:, g][:, None] * L["ws"][:, g][None, :] * ig
     assert np.linalg.norm(y - out["y_main"]) <= 1e-13 * np.linalg.norm(y)
+
+
+def test_w8a8_gemm_equals_int64_brute_force():
+    # per-token x per-channel scales factor out of the whole K sum
+    s, d, L = _tiny("w8a8")
+    out = F.forward(d["X"], L)
+    qx = out["xq_codes"].astype(np.int64)
+    qw = L["wq_codes"].astype(np.int64)
+    y = np.empty((qx.shape[0], qw.shape[0]))
+    for m in range(qx.shape[0]):
+        for n in range(0, qw.shape[0], 64):
+            acc = qw[n:n + 64] @ qx[m]                                 # exact int64 dot products
+            y[m, n:n + 64] = acc * (float(out["xs"][m]) * L["ws"][n:n + 64].astype(np.float64))
+    assert np.linalg.norm(y - out["y_main"]) <= 1e-13 * np.linalg.norm(y)
+    # and the 8-bit layer is far closer to X W than the 4-bit one
+    L4 = P.prepare(d["W"], P.calib_amax(d["X_cal"]), s.alpha, s.rank, "int4")
+    ref = d["X"].astype(np.float64) @ d["W"].astype(np.float64)
+    e8 = np.linalg.norm(out["y"] - ref)
+    e4 = np.linalg.norm(F.forward(d["X"], L4)["y"] - ref)
+    assert e8 < 0.1 * e4
 
 
 def test_forward_terms_and_bias():

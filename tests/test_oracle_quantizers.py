@@ -183,3 +183,55 @@ def test_int4_exact_ties_round_to_even():
     q, s = Q.quantize_int4(z)
     assert s[0, 0] == 1.0
     assert list(q[0, :8]) == [7, 2, -2, 0, 0, 2, 4, -6]
+
+
+# ---------------------------------------------------------------- 8-bit (W8A8)
+# Zhou notes sec. 8: per-token activations and per-channel weights at 8 bits.
+
+@pytest.mark.parametrize("scale", [1e-3, 1.0, 37.0])
+def test_w8_codes_are_the_nearest_code(scale):
+    rng = np.random.default_rng(17)
+    z = (rng.standard_normal((24, 384)) * scale).astype(np.float32)
+    z[3, 5] = 40 * scale      # an outlier in one row
+    z[9] = 0.0                # an all-zero row
+    q, s = Q.quantize_w8(z)
+    assert q.dtype == np.int8 and q.min() >= -127 and q.max() <= 127
+    cand = np.arange(-127, 128, dtype=np.float64)
+    err = np.abs(z.astype(np.float64)[..., None] - s.astype(np.float64)[:, None, None] * cand)
+    best = cand[np.argmin(err, axis=-1)]
+    mism = (q != best) & (s[:, None] > 0)
+    ratio = z.astype(np.float64) / np.where(s > 0, s, 1)[:, None]
+    assert np.all(_near_half_integer(ratio[mism]))
+    assert mism.sum() <= 2
+    assert np.all(q[9] == 0) and s[9] == 0.0
+    # the row maximum lands on the end of the range: nothing is clipped
+    amax_pos = np.argmax(np.abs(z), axis=1)
+    live = s > 0
+    assert np.all(np.abs(q[live, amax_pos[live]]) == 127)
+
+
+def test_w8_scale_and_closed_forms():
+    # amax = 127 * 2^k: the scale is 2^k exactly and integer multiples of it
+    # decode without error; ties of the half-integers go to the even code
+    z = np.zeros((3, 128), np.float32)
+    z[0, :6] = [127.0, -3.0, 2.5, -2.5, 0.5, 126.5]
+    z[1, :3] = [127.0 * 2 ** -10, 5 * 2 ** -10, -64 * 2 ** -10]
+    z[2, 0] = 1.0                                   # s = fp32(1/127), not exact
+    q, s = Q.quantize_w8(z)
+    assert s[0] == 1.0 and s[1] == 2.0 ** -10
+    assert list(q[0, :6]) == [127, -3, 2, -2, 0, 126]
+    assert list(q[1, :3]) == [127, 5, -64]
+    assert s[2] == np.float32(1.0) / np.float32(127.0) and q[2, 0] == 127
+    d = Q.decode_w8(q[:2], s[:2])
+    assert np.array_equal(d[1], z[1].astype(np.float64))
+
+
+def test_w8_row_error_bound_and_roundtrip():
+    rng = np.random.default_rng(5)
+    z = (rng.standard_t(3, (16, 512))).astype(np.float32)
+    d = Q.quantize(z, "w8a8")
+    assert d["packed"].shape == (16, 512) and d["packed"].dtype == np.uint8
+    assert np.array_equal(Q.dequantize_packed(d["packed"], d["scales"], "w8a8"), d["deq"])
+    # |z - q s| <= s / 2 (times the fp32 reciprocal's relative error) per element
+    bound = d["scales"].astype(np.float64)[:, None] * (0.5 + 1e-6)
+    assert np.all(np.abs(z - d["deq"]) <= bound)
