@@ -44,6 +44,8 @@ row over all K values (a token row of x^, an out-feature row of R^T):
 Readings: the symmetric range -127..127 (as INT4 leaves out -8, the 8-bit
 code leaves out -128), an fp32 scale (the pages fix 16-bit scales only for
 the 4-bit groups), and the same reciprocal-then-multiply division as INT4.
+For a row whose scale is an fp32 subnormal below 2^-128, 1/s overflows to
+infinity: non-zero elements then take +-127 and zeros stay 0.
 Codes are stored one signed byte per element, K contiguous, row-major.
 
 Pins (tests/test_oracle_quantizers.py): the worked example of Zhou notes
@@ -103,7 +105,8 @@ def quantize_w8(z):
         rcp = (np.float32(1.0) / s).astype(np.float32)
         y = (z * rcp[:, None]).astype(np.float32)           # fp32 product
         q = np.clip(np.rint(y), -127, 127)
-    q = np.where((s == 0)[:, None], 0.0, q)
+    # a zero element is code 0 (also when s is subnormal and 1/s overflows)
+    q = np.where((s == 0)[:, None] | (z == 0), 0.0, q)
     return q.astype(np.int8), s
 
 

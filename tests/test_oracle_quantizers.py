@@ -224,6 +224,13 @@ def test_w8_scale_and_closed_forms():
     assert s[2] == np.float32(1.0) / np.float32(127.0) and q[2, 0] == 127
     d = Q.decode_w8(q[:2], s[:2])
     assert np.array_equal(d[1], z[1].astype(np.float64))
+    # a row of fp32 subnormals: s underflows so far that 1/s is infinite;
+    # non-zero elements saturate, zeros stay zero
+    t = np.zeros((1, 64), np.float32)
+    t[0, :3] = [3e-39, -1e-45, 0.0]
+    qt, st = Q.quantize_w8(t)
+    assert 0 < st[0] < 2.0 ** -128 and np.isinf(np.float32(1.0) / st[0])
+    assert list(qt[0, :4]) == [127, -127, 0, 0]
 
 
 def test_w8_row_error_bound_and_roundtrip():
