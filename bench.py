@@ -29,8 +29,35 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK = {"mxfp4": 10.1e15, "int4": 5.0e15}          # dense MFMA peaks: FP4 / int8 (MI355X datasheet)
-PEAK_NAME = {"mxfp4": "fp4 MFMA", "int4": "int8 MFMA"}
+PEAK = {"mxfp4": 10.1e15, "int4": 5.0e15, "w8a8": 5.0e15}   # dense MFMA peaks: FP4 / int8 (MI355X datasheet)
+PEAK_NAME = {"mxfp4": "fp4 MFMA", "int4": "int8 MFMA", "w8a8": "int8 MFMA"}
+DTYPE = {"mxfp4": "fp4", "int4": "int4", "w8a8": "int8"}   # operand type of the main contraction
+
+
+# Algorithmic work of one layer (what the kernels must at least move or
+# compute, independent of how they tile it).
+def main_ops(M, N, K):
+    """2MNK: the quantized main contraction."""
+    return 2 * M * N * K
+
+
+def code_and_scale_bytes(rows, K, fmt):
+    """Codes plus scales of `rows` quantized rows of K elements."""
+    if fmt == "w8a8":
+        return rows * K + 4 * rows
+    g, sb = (64, 2) if fmt == "int4" else (32, 1)
+    return rows * K // 2 + rows * (K // g) * sb
+
+
+def ka_bytes(M, K, r, fmt):
+    """K-A: read X (bf16), 1/lambda, L1'; write codes, scales and Z (bf16 hi + lo)."""
+    return 2 * M * K + 4 * K + 2 * K * r + code_and_scale_bytes(M, K, fmt) + 4 * M * r
+
+
+def kb_bytes(M, N, K, r, fmt):
+    """K-B: read activation and weight codes/scales, Z, L2', bias; write Y (bf16)."""
+    return (code_and_scale_bytes(M, K, fmt) + code_and_scale_bytes(N, K, fmt)
+            + 4 * M * r + 2 * r * N + 2 * N + 2 * M * N)
 HBM_PEAK = 8.0e12
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kb_traffic.json")
 
@@ -62,7 +89,10 @@ def kb_kernel_names(fmt, K, rank):
     ntr = ((rank + 31) // 32 * 32) // 32
     if fmt == "mxfp4":
         odd = (K // 128) % 2
-        return (f"kb_mx_kernel<{ntr}, {'true' if odd else 'false'}, 8>", f"kb_mx_kernelILi{ntr}ELb{odd}ELi8E")
+        return (f"kb_mx_kernel<{ntr}, {'true' if odd else 'false'}, 8, false>",
+                f"kb_mx_kernelILi{ntr}ELb{odd}ELi8ELb0E")
+    if fmt == "w8a8":
+        return (f"kb_mx_kernel<{ntr}, false, 8, true>", f"kb_mx_kernelILi{ntr}ELb0ELi8ELb1E")
     return (f"kb_i4_kernel<{ntr}>", f"kb_i4_kernelILi{ntr}E")
 
 
@@ -133,7 +163,6 @@ def main():
     import torch
     import rank_gemm_svdq_amd as B
     from rank_gemm_svdq_amd import synthetic as S
-    from oracle import accounting as A
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
@@ -224,12 +253,29 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    parity = None
-    if not args.skip_oracle:
-        # parity on sampled rows against the oracle's own preparation
+    r = prep["rank"]
+    t_step = ms * 1e-3
+    ops = main_ops(M, N, K)
+    tops = ops / t_step
+    t_kb = float(np.median(kb)) * 1e-3
+    t_ka = float(np.median(ka)) * 1e-3
+    kb_achieved = ops / t_kb
+    ka_b = ka_bytes(M, K, r, fmt)
+    kb_b = kb_bytes(M, N, K, r, fmt)
+    traffic = measured_traffic(s.name if not args.fmt else f"{s.name}_{fmt}")
+    t_step0 = float(np.median(ms0_chunks)) * 1e-3
+    t_stepr = float(np.median(msr_chunks)) * 1e-3
+    t_stepu = float(np.median(msu_chunks)) * 1e-3
+
+    cpu, parity = None, None
+    if not args.no_cpu_baseline and not args.skip_oracle:
+        # The CPU-baseline leg: the fp64 oracle prepares the same layer and
+        # runs its forward on a bounded sample of rows on the host cores; the
+        # device output of those rows is compared with it on the way.
+        from threadpoolctl import threadpool_info
         from oracle import forward as F
         from oracle import prepare as P
-        log("oracle prepare (fp64, LAPACK SVD)")
+        log("cpu baseline: oracle prepare (fp64, LAPACK SVD)")
         t0 = time.time()
         po = P.prepare(d["W"], P.calib_amax(d["X_cal"]), s.alpha, s.rank, fmt, lora=lora)
         t_oracle_prepare = time.time() - t0
@@ -245,24 +291,6 @@ def main():
         mism = int(np.sum(xq[rows] != of["xq"]))
         log(f"parity on {len(rows)} rows: rel_fro={rel:.3e} code mismatches={mism}")
         parity = {"rows": int(len(rows)), "rel_fro": rel, "tolerance": 5e-3, "code_mismatches": mism}
-
-    main_ops = A.main_ops(M, N, K)
-    r = prep["rank"]
-    t_step = ms * 1e-3
-    tops = main_ops / t_step
-    t_kb = float(np.median(kb)) * 1e-3
-    t_ka = float(np.median(ka)) * 1e-3
-    kb_achieved = main_ops / t_kb
-    ka_bytes = A.ka_bytes(M, K, r, fmt)
-    kb_bytes = A.kb_bytes(M, N, K, r, fmt)
-    traffic = measured_traffic(s.name if not args.fmt else f"{s.name}_{fmt}")
-    t_step0 = float(np.median(ms0_chunks)) * 1e-3
-    t_stepr = float(np.median(msr_chunks)) * 1e-3
-    t_stepu = float(np.median(msu_chunks)) * 1e-3
-
-    cpu = None
-    if not args.no_cpu_baseline and not args.skip_oracle:
-        from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
         # bounded sample: the first n token rows of the same layer, n grown
         # until the oracle forward takes about cpu_seconds
@@ -277,19 +305,19 @@ def main():
                "host_cpus": os.cpu_count()}
 
     out = {
-        "metric": "W4A4+low-rank linear TOPS (2MNK / layer time) and % of MFMA peak",
+        "metric": ("W8A8" if fmt == "w8a8" else "W4A4") + "+low-rank linear TOPS (2MNK / layer time) and % of MFMA peak",
         "value": tops / 1e12, "unit": "TOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": fmt, "data": "synthetic (seeded FLUX-shaped layer, random weights)",
+        "dtype": DTYPE[fmt], "data": "synthetic (seeded FLUX-shaped layer, random weights)",
         "config": {"workload": s.name, "M": M, "K": K, "N": N, "rank": r, "format": fmt,
                    "alpha": s.alpha, "bias": True},
         "pct_of_peak": 100.0 * tops / PEAK[fmt], "peak_name": PEAK_NAME[fmt],
         "roofline": {"bound": "mfma", "achieved": kb_achieved / 1e12, "peak": PEAK[fmt] / 1e12, "unit": "TFLOP/s",
                      "frac": kb_achieved / PEAK[fmt],
-                     "traffic": traffic, "kernel": kb_kernel_names(fmt, K, r)[0] + " (W4A4 GEMM + lora_up + bias)",
-                     "algorithmic_ops_per_launch": main_ops, "algorithmic_bytes_per_launch": kb_bytes},
-        "ka": {"us": t_ka * 1e6, "algorithmic_bytes": ka_bytes, "GB_per_s": ka_bytes / t_ka / 1e9,
-               "frac_of_hbm": ka_bytes / t_ka / HBM_PEAK},
+                     "traffic": traffic, "kernel": kb_kernel_names(fmt, K, r)[0] + " (quantized GEMM + lora_up + bias)",
+                     "algorithmic_ops_per_launch": ops, "algorithmic_bytes_per_launch": kb_b},
+        "ka": {"us": t_ka * 1e6, "algorithmic_bytes": ka_b, "GB_per_s": ka_b / t_ka / 1e9,
+               "frac_of_hbm": ka_b / t_ka / HBM_PEAK},
         "kb_us": t_kb * 1e6,
         "lowrank_overhead": t_stepr / t_step0 - 1.0, "rank0_layer_us": t_step0 * 1e6,
         "layer_us_interleaved": t_stepr * 1e6,
@@ -424,7 +452,6 @@ def summarize_profiles(d, config, fmt_override=None):
     under d (made by the commands of profile_commands) -> profiles/."""
     sys.path.insert(0, ROOT)
     from rank_gemm_svdq_amd import synthetic as S
-    from oracle import accounting as A
     s = S.spec(config, **({"fmt": fmt_override} if fmt_override else {}))
     M, K, N, fmt = s.M, s.K, s.N, s.fmt
     r = s.rank + s.lora_rank
@@ -459,7 +486,7 @@ def summarize_profiles(d, config, fmt_override=None):
         lines += ["", f"bench.py under the profiler: K-B median {b['kb_us']:.2f} us (HIP events on the launch "
                       f"stream), K-A median {b['ka']['us']:.2f} us, layer {b['value']:.0f} TOPS."]
     if kb_avg is not None:
-        ops = A.main_ops(M, N, K)
+        ops = main_ops(M, N, K)
         lines += [f"{kb_names[0]}: average {kb_avg:.2f} us -> {ops / (kb_avg * 1e-6) / 1e12:.0f} TOP/s of "
                   f"2MNK = {ops:.4g} ops per launch."]
     open(os.path.join(ROOT, "profiles", f"{short}_{key}_kernel_stats.md"), "w").write("\n".join(lines) + "\n")
@@ -485,8 +512,8 @@ def summarize_profiles(d, config, fmt_override=None):
                       "ka_counter_bytes": float(np.mean(ka)) if ka else None,
                       "kb_dispatches": len(kb), "ka_dispatches": len(ka)}
     f_, w_ = out["fetch"], out["write"]
-    kb_alg = A.kb_bytes(M, N, K, r, fmt)
-    ka_alg = A.ka_bytes(M, K, r, fmt)
+    kb_alg = kb_bytes(M, N, K, r, fmt)
+    ka_alg = ka_bytes(M, K, r, fmt)
     kb_traffic = ka_traffic = None
     if f_["kb_counter_bytes"] and w_["kb_counter_bytes"] and f_["factor"] and w_["factor"]:
         kb_traffic = f_["kb_counter_bytes"] * f_["factor"] + w_["kb_counter_bytes"] * w_["factor"]

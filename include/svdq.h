@@ -53,7 +53,10 @@ typedef enum svdq_status {
   SVDQ_ERR_DEVICE = 7        /* a HIP call failed */
 } svdq_status;
 
-typedef enum svdq_format { SVDQ_INT4_G64 = 0, SVDQ_MXFP4_G32 = 1 } svdq_format;
+/* SVDQ_W8A8: 8-bit codes -127..127 with one fp32 scale per row, i.e. per
+ * token for activations (dynamic) and per out-feature for weights (Zhou
+ * notes sec. 8, the 8-bit setting). */
+typedef enum svdq_format { SVDQ_INT4_G64 = 0, SVDQ_MXFP4_G32 = 1, SVDQ_W8A8 = 2 } svdq_format;
 
 /* ------------------------------------------------------------------------
  * Shape rules (checked by every entry point):
@@ -82,7 +85,8 @@ typedef struct svdq_layer {
 
 typedef struct svdq_sizes {
   size_t wq_bytes, ws_bytes, l1k_bytes, l2k_bytes;
-  size_t wq_canon_bytes, ws_canon_bytes;   /* canonical [N, K/2] codes and [N, K/G] scales */
+  size_t wq_canon_bytes, ws_canon_bytes;   /* canonical codes [N, K/2] (4-bit) or [N, K] (8-bit) and
+                                              scales [N, K/G] (4-bit) or [N] fp32 (8-bit) */
 } svdq_sizes;
 
 /* Byte sizes of the kernel-layout and canonical buffers of a layer.
@@ -105,6 +109,9 @@ typedef struct svdq_sizes {
  *   INT4 weight scales: 2 KB units of 128 rows x 4 steps ordered
  *           [row / 128][4-step group]; inside a unit fp16 index
  *           32 ((row % 128) / 4) + 8 (t % 4) + 2 (row % 4) + (group of the step)
+ *   W8A8: codes in the same 1 KB units with 64 elements per step (byte b
+ *           of step t is element 64 t + b, canonical order), so a row has
+ *           K/64 steps; weight scales are the canonical fp32 [N]
  * Padding rows, steps and records hold zero codes, scale 127 (MXFP4) or 0 (INT4). */
 svdq_status svdq_layer_sizes(int32_t K, int32_t N, int32_t rank, int32_t fmt, svdq_sizes* out);
 
@@ -112,9 +119,11 @@ svdq_status svdq_layer_sizes(int32_t K, int32_t N, int32_t rank, int32_t fmt, sv
 
 /* Per-call device workspace.  Regions, each 256-byte aligned:
  *   xq   activation codes in the codes layout above (rows padded to 16;
- *        ceil(M/16) * 16 * K/2 bytes; padding rows are not written)
+ *        ceil(M/16) * 16 * K/2 bytes, K bytes per row for W8A8; padding
+ *        rows are not written)
  *   xs   activation scale records in the scale-record layout above
- *        (ceil(M/64) * 64 * ceil(K/512) * 16 bytes)
+ *        (ceil(M/64) * 64 * ceil(K/512) * 16 bytes); W8A8: fp32 [M] per
+ *        token scales (ceil(M/16) * 64 bytes)
  *   z    down projection Z: per row and 32-column chunk of the rank
  *        (rounded up to 32), 32 bf16 values hi then 32 bf16 values lo with
  *        hi + lo = Z to about 2^-17 relative (M * rank_pad * 4 bytes)
@@ -238,7 +247,9 @@ svdq_status svdq_smooth_search(const float* W, int32_t K, int32_t N, int32_t ran
 
 /* RTN quantization of a host [rows, K] fp32 matrix, grouped along K, into
  * canonical codes [rows, K/2] (element 2j in the low nibble of byte j) and
- * canonical scales [rows, K/G] (fp16 bits or E8M0 bytes).  Errors: ARG, SHAPE. */
+ * canonical scales [rows, K/G] (fp16 bits or E8M0 bytes); for W8A8 one
+ * group per row: codes [rows, K] int8 and scales [rows] fp32 (Zhou notes
+ * sec. 8).  Errors: ARG, SHAPE. */
 svdq_status svdq_pack_host(const float* x, int32_t rows, int32_t K, int32_t fmt,
                            uint8_t* codes, uint8_t* scales);
 
@@ -261,8 +272,9 @@ svdq_status svdq_kernel_layout(int32_t K, int32_t N, int32_t rank, int32_t fmt,
                                const uint16_t* l1, const uint16_t* l2,
                                uint8_t* wq_k, uint8_t* ws_k, uint16_t* l1k, uint16_t* l2k);
 
-/* Host copy of a workspace -> canonical activation codes [M, K/2], scales
- * [M, K/G] and (if z != NULL) the summed down projection z [M, rank] fp32. */
+/* Host copy of a workspace -> canonical activation codes [M, K/2] ([M, K]
+ * for W8A8), scales [M, K/G] ([M] fp32 for W8A8) and (if z != NULL) the
+ * summed down projection z [M, rank] fp32. */
 svdq_status svdq_unpack_activations(const void* ws_host, int32_t M, int32_t K, int32_t rank, int32_t fmt,
                                     uint8_t* xq, uint8_t* xs, float* z);
 
@@ -271,13 +283,16 @@ svdq_status svdq_unpack_activations(const void* ws_host, int32_t M, int32_t K, i
 /* K-A: fused smoothing + group absmax + 4-bit quantize/pack + lora_down
  * (notes, Algorithm 2 steps 1-3; AutoRound/msModelSlim "lora_down").
  * Reads X once: x~ = fp32(x * smooth_inv), per-group scales and codes into
- * the workspace, z = X diag(smooth_inv) L1' as fp32 partial sums.
+ * the workspace, z = x~ L1' as bf16 hi + lo pairs.  W8A8: the per-token
+ * scale needs the whole row's maximum, so the codes are written in a second
+ * pass over the block's rows of X (a cache re-read).
  * X: device [M, K] bf16.  Errors: ARG, SHAPE, ALIGN, WORKSPACE, UNSUPPORTED, DEVICE. */
 svdq_status svdq_quantize_lora_down(const svdq_layer* layer, const uint16_t* X, int32_t M,
                                     void* ws, size_t ws_bytes, void* stream);
 
 /* K-B: W4A4 GEMM with per-group scales, lora_up epilogue (z L2') and bias,
- * one bf16 store of Y (notes, Algorithm 2 steps 4-7).
+ * one bf16 store of Y (notes, Algorithm 2 steps 4-7).  W8A8: int8 GEMM with
+ * exact int32 accumulation, scaled by s_x[m] s_w[n] after the K loop.
  * Y: device [M, N] bf16.  Errors: as above. */
 svdq_status svdq_gemm_lora_up(const svdq_layer* layer, const void* ws, size_t ws_bytes, int32_t M,
                               uint16_t* Y, void* stream);

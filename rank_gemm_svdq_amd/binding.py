@@ -22,6 +22,7 @@ __all__ = [
 
 INT4 = 0
 MXFP4 = 1
+W8A8 = 2
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libsvdq.so")
 
 
@@ -30,7 +31,25 @@ def fmt_code(fmt):
         return INT4
     if fmt in (MXFP4, "mxfp4"):
         return MXFP4
+    if fmt in (W8A8, "w8a8"):
+        return W8A8
     raise ValueError(f"unknown format {fmt!r}")
+
+
+def _canon(rows, K, f):
+    """Empty canonical code and scale arrays of `rows` rows in format f."""
+    if f == W8A8:
+        return np.empty((rows, K), np.uint8), np.empty((rows, 4), np.uint8)
+    return np.empty((rows, K // 2), np.uint8), np.empty((rows, (K // 64) * 2 if f == INT4 else K // 32), np.uint8)
+
+
+def _scales_view(a, f):
+    """Canonical scale bytes as fp16 bits (INT4), E8M0 bytes (MXFP4) or fp32 [rows] (W8A8)."""
+    if f == INT4:
+        return a.view(np.uint16)
+    if f == W8A8:
+        return a.view(np.float32).reshape(-1)
+    return a
 
 
 class SvdqError(RuntimeError):
@@ -177,11 +196,9 @@ def pack_host(x, fmt):
     x = np.ascontiguousarray(x, dtype=np.float32)
     rows, K = x.shape
     f = fmt_code(fmt)
-    codes = np.empty((rows, K // 2), np.uint8)
-    g, sb = (64, 2) if f == INT4 else (32, 1)
-    scales = np.empty((rows, (K // g) * sb), np.uint8)
+    codes, scales = _canon(rows, K, f)
     _check(lib().svdq_pack_host(_p(x), rows, K, f, _p(codes), _p(scales)), "svdq_pack_host")
-    return codes, (scales.view(np.uint16) if f == INT4 else scales)
+    return codes, _scales_view(scales, f)
 
 
 def prepare(W, act_amax, alpha, rank, fmt, lora=None, threads=0, want_residual=False, max_iters=0,
@@ -198,10 +215,10 @@ def prepare(W, act_amax, alpha, rank, fmt, lora=None, threads=0, want_residual=F
     out = {
         "lambda": np.empty(K, np.float32), "smooth_inv": np.empty(K, np.float32),
         "l1": np.empty((K, rt), np.uint16), "l2": np.empty((rt, N), np.uint16),
-        "sigma": np.empty(max(rank, 1), np.float64), "wq": np.empty((N, K // 2), np.uint8),
-        "ws": np.empty((N, (K // 64) * 2 if f == INT4 else K // 32), np.uint8),
+        "sigma": np.empty(max(rank, 1), np.float64),
         "iter_errors": np.empty(T, np.float64), "best_iter": np.zeros(1, np.int32),
     }
+    out["wq"], out["ws"] = _canon(N, K, f)
     if want_residual:
         out["residual"] = np.empty((K, N), np.float32)
     opts = PrepareOpts(0, None, None, 1.0, threads, max_iters, int(residual_iters), int(bool(early_stop)),
@@ -220,8 +237,7 @@ def prepare(W, act_amax, alpha, rank, fmt, lora=None, threads=0, want_residual=F
                   _p(out["best_iter"]).value)
     _check(lib().svdq_prepare(_p(W), _p(act_amax), K, N, float(alpha), rank, f, C.byref(opts), C.byref(pr)),
            "svdq_prepare")
-    if f == INT4:
-        out["ws"] = out["ws"].view(np.uint16)
+    out["ws"] = _scales_view(out["ws"], f)
     out["sigma"] = out["sigma"][:rank]
     out["best_iter"] = int(out["best_iter"][0])
     out.update(K=K, N=N, rank=rt, fmt=f)
@@ -266,12 +282,11 @@ def unpack_activations(ws_host, M, K, rank, fmt):
     """Host copy of a workspace -> canonical (xq [M, K/2] u8, xs, z [M, rank] fp32)."""
     f = fmt_code(fmt)
     ws_host = np.ascontiguousarray(ws_host).view(np.uint8)
-    xq = np.empty((M, K // 2), np.uint8)
-    xs = np.empty((M, (K // 64) * 2 if f == INT4 else K // 32), np.uint8)
+    xq, xs = _canon(M, K, f)
     z = np.empty((M, max(rank, 1)), np.float32)
     _check(lib().svdq_unpack_activations(_p(ws_host), M, K, rank, f, _p(xq), _p(xs), _p(z) if rank else None),
            "svdq_unpack_activations")
-    return xq, (xs.view(np.uint16) if f == INT4 else xs), z[:, :rank]
+    return xq, _scales_view(xs, f), z[:, :rank]
 
 
 # ------------------------------------------------------------ device side
@@ -370,8 +385,8 @@ def smooth_search(W, X_cal, rank, fmt, grids=20, residual_iters=1, early_stop=Fa
     out = {
         "lambda": np.empty(K, np.float32), "smooth_inv": np.empty(K, np.float32),
         "l1": np.empty((K, rank), np.uint16), "l2": np.empty((rank, N), np.uint16),
-        "wq": np.empty((N, K // 2), np.uint8), "ws": np.empty((N, (K // 64) * 2 if f == INT4 else K // 32), np.uint8),
     }
+    out["wq"], out["ws"] = _canon(N, K, f)
     pr = Prepared(_p(out["lambda"]).value, _p(out["smooth_inv"]).value,
                   _p(out["l1"]).value if rank else None, _p(out["l2"]).value if rank else None,
                   None, None, _p(out["wq"]).value, _p(out["ws"]).value, None, None)
@@ -379,7 +394,6 @@ def smooth_search(W, X_cal, rank, fmt, grids=20, residual_iters=1, early_stop=Fa
     opts = SearchOpts(int(grids), int(residual_iters), int(bool(early_stop)), int(threads))
     _check(lib().svdq_smooth_search(_p(W), K, N, rank, f, X_cal.data_ptr(), M, C.byref(opts), ws.data_ptr(),
                                     ws.numel(), _stream(stream), C.byref(res), C.byref(pr)), "svdq_smooth_search")
-    if f == INT4:
-        out["ws"] = out["ws"].view(np.uint16)
+    out["ws"] = _scales_view(out["ws"], f)
     out.update(K=K, N=N, rank=rank, fmt=f)
     return {"best": res.best, "alpha": res.alpha, "beta": res.beta, "errors": errors, "prepared": out}

@@ -85,7 +85,9 @@ __global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __res
   constexpr int NTZ = NT > 0 ? NT : 1;
   constexpr bool WRING = NT > 0 && NT <= (SL ? 4 : 2);   // down-factor fragments in the ring
   constexpr int NW = WRING ? 4 * NT : 1;
+  constexpr bool W8 = FMT == SVDQ_W8A8 && !ZONLY;
   __shared__ float zred[NT > 0 ? KA_WAVES * 16 * NT * 16 : 1];
+  __shared__ float mred[W8 ? KA_WAVES * 16 : 1];
   extern __shared__ __attribute__((aligned(16))) float svl[];   // K floats when SL
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -130,10 +132,11 @@ __global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __res
   v4f acc[NTZ];
 #pragma unroll
   for (int nt = 0; nt < NTZ; ++nt) acc[nt] = (v4f){0.f, 0.f, 0.f, 0.f};
+  float rmax = 0.f;   // W8A8: running |x^| maximum of this lane's share of its row
 
-  auto process = [&](int t, const Slot& sl) __attribute__((always_inline)) {
+  // x^ = fp32(x * 1/lambda) for the lane's 32 elements of step t
+  auto smooth = [&](int t, const Slot& sl, float* xh) __attribute__((always_inline)) {
     const int k0 = t * 128 + 32 * g;
-    float xh[32];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const v4f iv = SL ? *reinterpret_cast<const v4f*>(svl + k0 + 4 * c) : sl.s[SL ? 0 : c];
@@ -143,12 +146,21 @@ __global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __res
       xh[4 * c + 2] = bf16_lo(w1) * iv[2];
       xh[4 * c + 3] = bf16_hi(w1) * iv[3];
     }
+  };
+
+  auto process = [&](int t, const Slot& sl) __attribute__((always_inline)) {
+    float xh[32];
+    smooth(t, sl, xh);
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(xh[i]));
 
     if constexpr (ZONLY) {
       // down projection only (the unfused baseline's separate pass over X)
+    } else if constexpr (FMT == SVDQ_W8A8) {
+      // per-token scale: the whole row's maximum is needed first; the codes
+      // are written in a second pass below
+      rmax = fmaxf(rmax, amax);
     } else if constexpr (FMT == SVDQ_MXFP4_G32) {
       // smallest e with amax <= 6 * 2^e, clamped to [-127, 127]
       const uint32_t ab = __float_as_uint(amax);
@@ -273,6 +285,52 @@ __global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __res
       }
     }
   }
+  if constexpr (W8) {
+    // row maximum over the 4 lane groups and the 8 waves, then s = amax/127
+    // and a second pass over the wave's steps (X is re-read, now from cache)
+    float m = fmaxf(rmax, __shfl_xor(rmax, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    if (g == 0) mred[wave * 16 + r] = m;
+    __syncthreads();
+    float am = 0.f;
+#pragma unroll
+    for (int w = 0; w < KA_WAVES; ++w) am = fmaxf(am, mred[w * 16 + r]);
+    const float sc = am / 127.0f;
+    if (wave == 0 && g == 0 && live) reinterpret_cast<float*>(xs)[row] = sc;
+    const float rcp = 1.0f / sc;   // sc == 0 only for an all-zero row
+    const int steps8 = 2 * steps;
+    for (int t = t0; t < t1; ++t) {
+      Slot sl;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sl.x[c] = *reinterpret_cast<const v4i*>(xrow + (size_t)t * 128 + 8 * c);
+      if constexpr (!SL) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) sl.s[c] = *reinterpret_cast<const v4f*>(sinv + t * 128 + 32 * g + 4 * c);
+      }
+      float xh[32];
+      smooth(t, sl, xh);
+      uint32_t d[8];
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        d[w] = 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // a zero stays 0 also when rcp is infinite (s below 2^-128)
+          float q = xh[4 * w + j] == 0.f ? 0.f : __builtin_rintf(xh[4 * w + j] * rcp);
+          q = fminf(fmaxf(q, -127.f), 127.f);
+          d[w] |= ((uint32_t)(int)q & 0xFFu) << (8 * j);
+        }
+      }
+      if (live) {
+        // elements 128 t + 32 g .. +32: bytes 32 (g & 1) .. +32 of 8-bit step 2 t + g / 2
+        const int t8 = 2 * t + (g >> 1), b0 = 32 * (g & 1);
+        *reinterpret_cast<v4i*>(xq + code_offset(row, t8, b0, steps8)) =
+            (v4i){(int)d[0], (int)d[1], (int)d[2], (int)d[3]};
+        *reinterpret_cast<v4i*>(xq + code_offset(row, t8, b0 + 16, steps8)) =
+            (v4i){(int)d[4], (int)d[5], (int)d[6], (int)d[7]};
+      }
+    }
+  }
 }
 
 // ----------------------------------------------------------------- K-B
@@ -373,7 +431,7 @@ __device__ __forceinline__ int mx_nrow(int nt, int q) {
   return 32 * (nt >> 1) + 8 * (q >> 2) + 4 * (nt & 1) + (q & 3);
 }
 
-template <int NTR, bool ODD, int WAVES>
+template <int NTR, bool ODD, int WAVES, bool W8 = false>
 __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const float* __restrict__ zp, int zsplit,
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws, const uint16_t* __restrict__ l2k,
@@ -392,7 +450,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
   int tm, tn;
   mx_tile_of(blockIdx.x, tiles_m, tiles_n, &tm, &tn);
   const int tile_m = tm * MX_BM, tile_n = tn * MX_BN;
-  const int steps = K / 128;
+  // 64-byte code steps: 128 FP4 elements, or 64 int8 elements (W8)
+  const int steps = W8 ? K / 64 : K / 128;
   const int ks4 = (steps + 3) / 4;
   const int m_base = tile_m + 128 * wm, n_base = tile_n + 16 * NTW * wn;
 
@@ -430,6 +489,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
     for (int j = 0; j < UPW; ++j) dma16(cbase + (size_t)t * 1024, coff[j], b + 1024u * j);
   };
   auto issue_scales = [&](int grp) __attribute__((always_inline)) {
+    if constexpr (W8) return;   // W8: per-row scales, applied after the K loop
 #pragma unroll
     for (int j = 0; j < RPW; ++j)
       dma16(sbase + (size_t)grp * 1024, soff[j],
@@ -462,6 +522,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
   // even, in their low half: a 16-bit read from the group's dwords
   uint32_t asc[NTW], bsc[8];
   auto read_scales = [&](int tp) __attribute__((always_inline)) {
+    if constexpr (W8) return;
     uint32_t so = (uint32_t)(MX_NBUF * MX_STEP_BYTES + ((tp >> 2) & 1) * MX_SC_BYTES + 2 * ((tp >> 1) & 1));
     asm volatile("" : "+s"(so));
     const uint8_t* sc = lds + so;
@@ -582,13 +643,21 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
       if (mt < NTW) wf[J ^ 1][mt] = read_a(bn, mt);
       tk[(mt + 3) & 3] = mt + 3 < 8 ? read_b(bc, mt + 3) : read_b(bn, mt - 5);
       const v4i bq = tk[mt & 3];
-      const v8i b = (v8i){bq[0], bq[1], bq[2], bq[3], 0, 0, 0, 0};
+      if constexpr (W8) {
+        // int8 x int8 with exact int32 accumulation in the same registers
 #pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) {
-        const v4i aq = wf[J][nt];
-        const v8i a = (v8i){aq[0], aq[1], aq[2], aq[3], 0, 0, 0, 0};
-        acc[nt][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[nt][mt], 4, 4, J, (int)asc[nt], J,
-                                                                      (int)bsc[mt]);
+        for (int nt = 0; nt < NTW; ++nt)
+          acc[nt][mt] = __builtin_bit_cast(
+              v4f, __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[J][nt], bq, __builtin_bit_cast(v4i, acc[nt][mt]), 0, 0, 0));
+      } else {
+        const v8i b = (v8i){bq[0], bq[1], bq[2], bq[3], 0, 0, 0, 0};
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+          const v4i aq = wf[J][nt];
+          const v8i a = (v8i){aq[0], aq[1], aq[2], aq[3], 0, 0, 0, 0};
+          acc[nt][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[nt][mt], 4, 4, J, (int)asc[nt], J,
+                                                                        (int)bsc[mt]);
+        }
       }
       // keep each group's reads next to its MFMAs: hoisting all reads of a
       // step to its top would need twice the fragment registers
@@ -620,6 +689,24 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
     step(steps - 1, J0{}, H0{});
   }
 
+  if constexpr (W8) {
+    // y = float(I) * (s_w[n] s_x[m]): per-channel weight scale of MFMA row
+    // 4 g + i of tile nt, per-token scale of the lane's column
+    const float* sxp = reinterpret_cast<const float*>(xs);
+    const float* swp = reinterpret_cast<const float*>(ws);
+    float sxv[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) sxv[mt] = sxp[min(m_base + 16 * mt + l16, M - 1)];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float sw = swp[min(n_base + mx_nrow(nt, 4 * g + i), N - 1)];
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+          acc[nt][mt][i] = (float)__builtin_bit_cast(v4i, acc[nt][mt])[i] * (sw * sxv[mt]);
+      }
+  }
   // ---- low-rank up projection and bias, then one 16-byte store per pair
   if constexpr (NTR > 0) {
     for (int u = 0; u < NTR; ++u) {
@@ -1048,15 +1135,19 @@ static hipError_t launch_ka(const svdq_layer& L, const uint16_t* X, int M, uint8
   return hipGetLastError();
 }
 
-template <int NTR>
+template <int NTR, bool W8 = false>
 static void launch_kb_mx(const svdq_layer& L, const uint8_t* ws, const svdq_ws_layout& W, int M, uint16_t* Y,
                          hipStream_t st) {
   const int rp = rank_pad(L.rank);
   const int tiles = ((M + MX_BM - 1) / MX_BM) * ((L.N + MX_BN - 1) / MX_BN);
-  // the K loop runs in pairs of 128-wide steps; an odd step count takes the
-  // variant with one trailing step
+  // the K loop runs in pairs of 64-byte steps; an odd step count takes the
+  // variant with one trailing step (8-bit codes always have an even count)
   constexpr int WV = SVDQ_MX_WAVES;
-  if ((L.K / 128) % 2 == 0)
+  if constexpr (W8)
+    hipLaunchKernelGGL((kb_mx_kernel<NTR, false, WV, true>), dim3(tiles), dim3(WV * 64), 0, st, ws + W.xq_off,
+                       ws + W.xs_off, reinterpret_cast<const float*>(ws + W.z_off), W.zsplit, L.wq, L.ws, L.l2k,
+                       L.bias, Y, M, L.N, L.K, rp);
+  else if ((L.K / 128) % 2 == 0)
     hipLaunchKernelGGL((kb_mx_kernel<NTR, false, WV>), dim3(tiles), dim3(WV * 64), 0, st, ws + W.xq_off,
                        ws + W.xs_off, reinterpret_cast<const float*>(ws + W.z_off), W.zsplit, L.wq, L.ws, L.l2k,
                        L.bias, Y, M, L.N, L.K, rp);
@@ -1070,13 +1161,14 @@ template <int FMT>
 static hipError_t launch_kb(const svdq_layer& L, const uint8_t* ws, const svdq_ws_layout& W, int M, uint16_t* Y,
                             hipStream_t st) {
   const int rp = rank_pad(L.rank);
-  if constexpr (FMT == SVDQ_MXFP4_G32) {
+  if constexpr (FMT == SVDQ_MXFP4_G32 || FMT == SVDQ_W8A8) {
+    constexpr bool W8 = FMT == SVDQ_W8A8;
     switch (rp / 32) {
-      case 0: launch_kb_mx<0>(L, ws, W, M, Y, st); break;
-      case 1: launch_kb_mx<1>(L, ws, W, M, Y, st); break;
-      case 2: launch_kb_mx<2>(L, ws, W, M, Y, st); break;
-      case 3: launch_kb_mx<3>(L, ws, W, M, Y, st); break;
-      case 4: launch_kb_mx<4>(L, ws, W, M, Y, st); break;
+      case 0: launch_kb_mx<0, W8>(L, ws, W, M, Y, st); break;
+      case 1: launch_kb_mx<1, W8>(L, ws, W, M, Y, st); break;
+      case 2: launch_kb_mx<2, W8>(L, ws, W, M, Y, st); break;
+      case 3: launch_kb_mx<3, W8>(L, ws, W, M, Y, st); break;
+      case 4: launch_kb_mx<4, W8>(L, ws, W, M, Y, st); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -1161,7 +1253,8 @@ svdq_status svdq_quantize_lora_down(const svdq_layer* layer, const uint16_t* X, 
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = layer->fmt == SVDQ_MXFP4_G32
                      ? launch_ka<SVDQ_MXFP4_G32>(*layer, X, M, static_cast<uint8_t*>(ws), W, st)
-                     : launch_ka<SVDQ_INT4_G64>(*layer, X, M, static_cast<uint8_t*>(ws), W, st);
+                 : layer->fmt == SVDQ_W8A8 ? launch_ka<SVDQ_W8A8>(*layer, X, M, static_cast<uint8_t*>(ws), W, st)
+                                           : launch_ka<SVDQ_INT4_G64>(*layer, X, M, static_cast<uint8_t*>(ws), W, st);
   return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_DEVICE;
 }
 
@@ -1178,7 +1271,8 @@ svdq_status svdq_gemm_lora_up(const svdq_layer* layer, const void* ws, size_t ws
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = layer->fmt == SVDQ_MXFP4_G32
                      ? launch_kb<SVDQ_MXFP4_G32>(*layer, static_cast<const uint8_t*>(ws), W, M, Y, st)
-                     : launch_kb<SVDQ_INT4_G64>(*layer, static_cast<const uint8_t*>(ws), W, M, Y, st);
+                 : layer->fmt == SVDQ_W8A8 ? launch_kb<SVDQ_W8A8>(*layer, static_cast<const uint8_t*>(ws), W, M, Y, st)
+                                           : launch_kb<SVDQ_INT4_G64>(*layer, static_cast<const uint8_t*>(ws), W, M, Y, st);
   return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_DEVICE;
 }
 
@@ -1207,13 +1301,20 @@ svdq_status svdq_linear_forward_unfused(const svdq_layer* layer, const uint16_t*
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   svdq_layer plain = *layer;   // the same kernels with the low-rank branch left out
   plain.rank = 0;
-  const bool mx = layer->fmt == SVDQ_MXFP4_G32;
-  hipError_t e = mx ? launch_ka<SVDQ_MXFP4_G32>(plain, X, M, w8, W, st) : launch_ka<SVDQ_INT4_G64>(plain, X, M, w8, W, st);
-  if (e == hipSuccess && layer->rank > 0)
-    e = mx ? launch_ka<SVDQ_MXFP4_G32, true>(*layer, X, M, w8, W, st)
-           : launch_ka<SVDQ_INT4_G64, true>(*layer, X, M, w8, W, st);
+  const int f = layer->fmt;
+  auto ka = [&](const svdq_layer& L, bool zonly) {
+    if (f == SVDQ_MXFP4_G32)
+      return zonly ? launch_ka<SVDQ_MXFP4_G32, true>(L, X, M, w8, W, st) : launch_ka<SVDQ_MXFP4_G32>(L, X, M, w8, W, st);
+    if (f == SVDQ_W8A8)
+      return zonly ? launch_ka<SVDQ_W8A8, true>(L, X, M, w8, W, st) : launch_ka<SVDQ_W8A8>(L, X, M, w8, W, st);
+    return zonly ? launch_ka<SVDQ_INT4_G64, true>(L, X, M, w8, W, st) : launch_ka<SVDQ_INT4_G64>(L, X, M, w8, W, st);
+  };
+  hipError_t e = ka(plain, false);
+  if (e == hipSuccess && layer->rank > 0) e = ka(*layer, true);
   if (e == hipSuccess)
-    e = mx ? launch_kb<SVDQ_MXFP4_G32>(plain, w8, W, M, Y, st) : launch_kb<SVDQ_INT4_G64>(plain, w8, W, M, Y, st);
+    e = f == SVDQ_MXFP4_G32 ? launch_kb<SVDQ_MXFP4_G32>(plain, w8, W, M, Y, st)
+        : f == SVDQ_W8A8    ? launch_kb<SVDQ_W8A8>(plain, w8, W, M, Y, st)
+                            : launch_kb<SVDQ_INT4_G64>(plain, w8, W, M, Y, st);
   if (e == hipSuccess && layer->rank > 0) {
     const int rp = rank_pad(layer->rank);
     const int tiles = ((M + 15) / 16) * ((layer->N + 63) / 64);

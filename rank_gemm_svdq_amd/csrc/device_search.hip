@@ -228,10 +228,9 @@ svdq_status svdq_smooth_search(const float* W, int32_t K, int32_t N, int32_t ran
   // host buffers of one candidate (canonical and kernel layout)
   Geometry g;
   geometry(K, N, rank, fmt, &g);
-  const int G = group_size(fmt);
   std::vector<float> lam(K), sinv(K);
   std::vector<uint16_t> l1((size_t)K * std::max(rank, 1)), l2((size_t)std::max(rank, 1) * N);
-  std::vector<uint8_t> wq((size_t)N * (K / 2)), wsc((size_t)N * (K / G) * (fmt == SVDQ_INT4_G64 ? 2 : 1));
+  std::vector<uint8_t> wq(canon_code_bytes(N, K, fmt)), wsc(canon_scale_bytes(N, K, fmt));
   std::vector<uint8_t> wq_k(g.wq_bytes), ws_k(g.ws_bytes);
   std::vector<uint16_t> l1k(std::max<size_t>(g.l1k_bytes / 2, 8)), l2k(std::max<size_t>(g.l2k_bytes / 2, 8));
   std::vector<double> alphas(count), betas(count), errs(count, std::nan(""));

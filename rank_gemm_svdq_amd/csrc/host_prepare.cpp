@@ -26,15 +26,18 @@ bool valid_kn(int32_t K, int32_t N) {
   return K >= kStep && K <= 65536 && K % kStep == 0 && N >= 16 && N <= 262144 && N % 16 == 0;
 }
 bool valid_rank(int32_t rank) { return rank >= 0 && rank <= SVDQ_MAX_RANK && rank % 16 == 0; }
-bool valid_fmt(int32_t fmt) { return fmt == SVDQ_INT4_G64 || fmt == SVDQ_MXFP4_G32; }
+bool valid_fmt(int32_t fmt) { return fmt == SVDQ_INT4_G64 || fmt == SVDQ_MXFP4_G32 || fmt == SVDQ_W8A8; }
 
 bool geometry(int32_t K, int32_t N, int32_t rank, int32_t fmt, Geometry* g) {
   if (!valid_kn(K, N) || !valid_rank(rank) || !valid_fmt(fmt)) return false;
   g->K = K; g->N = N; g->rank = rank; g->rpad = rank_pad(rank); g->fmt = fmt;
   g->steps = K / kStep;
   g->ks4 = (g->steps + 3) / 4;
-  g->wq_bytes = code_bytes(N, g->steps);   // N % 16 == 0: exactly N K / 2
-  g->ws_bytes = fmt == SVDQ_INT4_G64 ? int4_wscale_bytes(N, g->ks4) : scale_record_bytes(N, g->ks4);
+  g->csteps = code_steps(K, fmt);
+  g->wq_bytes = code_bytes(N, g->csteps);   // N % 16 == 0: exactly the canonical size
+  g->ws_bytes = fmt == SVDQ_INT4_G64   ? int4_wscale_bytes(N, g->ks4)
+                : fmt == SVDQ_MXFP4_G32 ? scale_record_bytes(N, g->ks4)
+                                        : (size_t)N * 4;
   g->l1k_bytes = (size_t)K * g->rpad * 2;
   g->l2k_bytes = (size_t)N * g->rpad * 2;
   return true;
@@ -184,6 +187,26 @@ void quant_mxfp4_group(const float* x, uint8_t* nib, uint8_t* scale_byte) {
   }
 }
 
+// 8-bit (one fp32 scale per row of K values): s = fp32(amax / 127),
+// codes = clamp(rint(x * fp32(1/s)), -127, 127), zero elements 0; s == 0
+// gives all zeros.
+void quant_w8_row(const float* x, int32_t K, int8_t* q, float* scale) {
+  float amax = 0.0f;
+  for (int32_t i = 0; i < K; ++i) amax = std::max(amax, std::fabs(x[i]));
+  const float s = amax / 127.0f;
+  *scale = s;
+  if (s == 0.0f) {
+    std::memset(q, 0, (size_t)K);
+    return;
+  }
+  const float rcp = 1.0f / s;   // infinite when s is below 2^-128: zeros stay 0
+  for (int32_t i = 0; i < K; ++i) {
+    float v = x[i] == 0.0f ? 0.0f : std::nearbyint(x[i] * rcp);
+    v = std::min(127.0f, std::max(-127.0f, v));
+    q[i] = (int8_t)v;
+  }
+}
+
 static bool all_finite(const float* p, size_t n) {
   for (size_t i = 0; i < n; ++i)
     if (!std::isfinite(p[i])) return false;
@@ -223,8 +246,8 @@ svdq_status svdq_layer_sizes(int32_t K, int32_t N, int32_t rank, int32_t fmt, sv
   out->ws_bytes = g.ws_bytes;
   out->l1k_bytes = g.l1k_bytes;
   out->l2k_bytes = g.l2k_bytes;
-  out->wq_canon_bytes = (size_t)N * K / 2;
-  out->ws_canon_bytes = fmt == SVDQ_INT4_G64 ? (size_t)N * (K / 64) * 2 : (size_t)N * (K / 32);
+  out->wq_canon_bytes = canon_code_bytes(N, K, fmt);
+  out->ws_canon_bytes = canon_scale_bytes(N, K, fmt);
   return SVDQ_OK;
 }
 
@@ -235,9 +258,9 @@ svdq_status svdq_workspace_layout(int32_t M, int32_t K, int32_t rank, int32_t fm
   const int32_t steps = K / kStep, ks4 = (steps + 3) / 4;
   out->zsplit = rank > 0 ? choose_zsplit(M, K) : 0;
   out->xq_off = 0;
-  out->xq_bytes = code_bytes(M, steps);
+  out->xq_bytes = code_bytes(M, code_steps(K, fmt));
   out->xs_off = align256(out->xq_bytes);
-  out->xs_bytes = scale_record_bytes(M, ks4);
+  out->xs_bytes = is_w8(fmt) ? (size_t)(M + 15) / 16 * 64 : scale_record_bytes(M, ks4);
   out->z_off = align256(out->xs_off + out->xs_bytes);
   out->z_bytes = rank > 0 ? (size_t)out->zsplit * M * rank_pad(rank) * 4 : 0;
   out->total = align256(out->z_off + out->z_bytes);
@@ -266,6 +289,17 @@ svdq_status svdq_calib_absmax(const uint16_t* x, int64_t rows, int32_t K, float*
 svdq_status svdq_pack_host(const float* x, int32_t rows, int32_t K, int32_t fmt, uint8_t* codes, uint8_t* scales) {
   if (!x || !codes || !scales || rows < 0) return SVDQ_ERR_ARG;
   if (!valid_fmt(fmt)) return SVDQ_ERR_UNSUPPORTED;
+  if (is_w8(fmt)) {
+    if (K <= 0) return SVDQ_ERR_SHAPE;
+    parallel_for(rows, default_threads(0), [&](int64_t lo, int64_t hi) {
+      for (int64_t r = lo; r < hi; ++r) {
+        float sc;
+        quant_w8_row(x + (size_t)r * K, K, reinterpret_cast<int8_t*>(codes) + (size_t)r * K, &sc);
+        std::memcpy(scales + (size_t)r * 4, &sc, 4);
+      }
+    });
+    return SVDQ_OK;
+  }
   const int G = group_size(fmt);
   if (K <= 0 || K % G != 0) return SVDQ_ERR_SHAPE;
   parallel_for(rows, default_threads(0), [&](int64_t lo, int64_t hi) {
@@ -322,13 +356,20 @@ static double decode_mxfp4(uint8_t nib, uint8_t e8m0) {
 static void decode_transposed(const uint8_t* wq, const uint8_t* ws, int32_t N, int32_t K, int32_t fmt, int threads,
                               double* out) {
   constexpr int32_t NB = 32;
-  const int32_t G = group_size(fmt);
+  const int32_t G = is_w8(fmt) ? K : group_size(fmt);
   parallel_for((N + NB - 1) / NB, threads, [&](int64_t lo, int64_t hi) {
     std::vector<double> blk((size_t)NB * K);
     for (int64_t b = lo; b < hi; ++b) {
       const int32_t n0 = (int32_t)b * NB, nn = std::min(NB, N - n0);
       for (int32_t i = 0; i < nn; ++i) {
         const int32_t n = n0 + i;
+        if (is_w8(fmt)) {
+          float sc;
+          std::memcpy(&sc, ws + 4 * (size_t)n, 4);
+          const int8_t* q8 = reinterpret_cast<const int8_t*>(wq) + (size_t)n * K;
+          for (int32_t k = 0; k < K; ++k) blk[(size_t)i * K + k] = (double)q8[k] * (double)sc;
+          continue;
+        }
         const uint8_t* codes = wq + (size_t)n * (K / 2);
         for (int32_t k = 0; k < K; ++k) {
           const uint8_t nib = (codes[k >> 1] >> ((k & 1) * 4)) & 0xF;
@@ -389,9 +430,8 @@ static svdq_status fit_candidate(const std::vector<double>& wt, const double* ta
       }
     }
   });
-  const int G = group_size(fmt);
-  c.wq.resize((size_t)N * (K / 2));
-  c.ws.resize((size_t)N * (K / G) * (fmt == SVDQ_INT4_G64 ? 2 : 1));
+  c.wq.resize(canon_code_bytes(N, K, fmt));
+  c.ws.resize(canon_scale_bytes(N, K, fmt));
   const svdq_status st = svdq_pack_host(rt.data(), N, K, fmt, c.wq.data(), c.ws.data());
   if (st != SVDQ_OK) return st;
   // Q(R) = decoded codes, transposed back to [K, N]; error = ||R - Q(R)||_F
@@ -514,6 +554,16 @@ svdq_status svdq_kernel_layout(int32_t K, int32_t N, int32_t rank, int32_t fmt, 
   if (!geometry(K, N, rank, fmt, &g)) return SVDQ_ERR_SHAPE;
   if (rank > 0 && (!l1 || !l2 || !l1k || !l2k)) return SVDQ_ERR_ARG;
   const int32_t steps = g.steps, rp = g.rpad;
+  if (is_w8(fmt)) {
+    // 8-bit codes: element k of row n is byte k % 64 of 64-byte step k / 64;
+    // the per-channel fp32 scales are stored as they are
+    const int32_t cs = g.csteps;
+    parallel_for(N, default_threads(0), [&](int64_t lo, int64_t hi) {
+      for (int64_t n = lo; n < hi; ++n)
+        for (int32_t k = 0; k < K; ++k) wq_k[code_offset((int)n, k >> 6, k & 63, cs)] = wq[(size_t)n * K + k];
+    });
+    std::memcpy(ws_k, ws, (size_t)N * 4);
+  } else {
   // codes: tiled 1 KB units (INT4 bytes first permuted inside each step)
   parallel_for(N, default_threads(0), [&](int64_t lo, int64_t hi) {
     for (int64_t n = lo; n < hi; ++n)
@@ -549,6 +599,7 @@ svdq_status svdq_kernel_layout(int32_t K, int32_t N, int32_t rank, int32_t fmt, 
       for (int32_t t = 0; t < steps; ++t)
         for (int G = 0; G < 2; ++G) d[int4_wscale_index(n, t, G, g.ks4)] = s[(size_t)n * (K / 64) + 2 * t + G];
   }
+  }
   if (rank == 0) return SVDQ_OK;
   // down factor: L1' (bf16) in the order of K-A's MFMA B operand,
   // [step][s 0..3][n-tile][lane 0..63][i 0..7] with
@@ -581,6 +632,12 @@ svdq_status svdq_unpack_activations(const void* ws_host, int32_t M, int32_t K, i
   const uint8_t* base = static_cast<const uint8_t*>(ws_host);
   const uint8_t* q = base + L.xq_off;
   const int32_t steps = K / kStep, ks4 = (steps + 3) / 4;
+  if (is_w8(fmt)) {
+    const int32_t cs = code_steps(K, fmt);
+    for (int32_t m = 0; m < M; ++m)
+      for (int32_t k = 0; k < K; ++k) xq[(size_t)m * K + k] = q[code_offset(m, k >> 6, k & 63, cs)];
+    std::memcpy(xs, base + L.xs_off, (size_t)M * 4);
+  } else {
   for (int32_t m = 0; m < M; ++m) {
     for (int32_t t = 0; t < steps; ++t) {
       uint8_t src[64];
@@ -611,6 +668,7 @@ svdq_status svdq_unpack_activations(const void* ws_host, int32_t M, int32_t K, i
       for (int32_t t = 0; t < steps; ++t)
         for (int G = 0; G < 2; ++G)
           std::memcpy(xs16 + (size_t)m * (K / 64) + 2 * t + G, s + scale_record_offset(m, t / 4, 4 * (t % 4) + 2 * G, ks4), 2);
+  }
   }
   if (z && rank > 0) {
     const int32_t rp = rank_pad(rank);

@@ -51,7 +51,7 @@ def _check(name, fmt, alpha=None, lora=False):
     assert err <= Y_TOL, f"{name}/{fmt}: rel_fro {err:.3e}"
     # all rows: decoded operands, fp32 product on the GPU, against Y
     import torch
-    sc = lambda v: v.view(np.float16).astype(np.float64) if fmt == "int4" else v
+    sc = lambda v: v.view(np.float16).astype(np.float64) if fmt == "int4" else v   # E8M0 bytes / fp32 as is
     xd = torch.from_numpy(Q.dequantize_packed(xq, sc(xs), fmt).astype(np.float32)).cuda()
     wd = torch.from_numpy(Q.dequantize_packed(run.prep["wq"], sc(run.prep["ws"]), fmt).astype(np.float32)).cuda()
     l2 = torch.from_numpy(bf16_to_f64(run.prep["l2"]).astype(np.float32)).cuda()
@@ -81,6 +81,11 @@ def test_flux_mlp_up_mxfp4():
 @pytest.mark.parametrize("alpha", [0.3, 0.5, 0.7])
 def test_flux_mlp_down_int4_alpha(alpha):
     _check("flux_mlp_down", "int4", alpha=alpha)
+
+
+def test_flux_qkv_w8a8():
+    # the 8-bit setting: rank 16, per-token activations, per-channel weights
+    _check("flux_qkv_w8a8", "w8a8")
 
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "int4"])

@@ -31,7 +31,7 @@ def _check_full(run, po, x, bias, z_tol=2e-5):
     return err
 
 
-@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4", "w8a8"])
 @pytest.mark.parametrize("use_bias", [True, False])
 def test_tiny_layer(fmt, use_bias):
     s = S.spec("tiny", fmt=fmt)
@@ -41,7 +41,7 @@ def test_tiny_layer(fmt, use_bias):
     _check_full(run, po, d["X"], d["bias"] if use_bias else None)
 
 
-@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4", "w8a8"])
 @pytest.mark.parametrize("M,K,N,rank", [
     (1, 512, 512, 16), (17, 512, 512, 16), (255, 512, 512, 16),   # ragged token counts
     (300, 1024, 400, 32),                                          # several tiles, ragged N
@@ -57,7 +57,7 @@ def test_shapes_and_tails(fmt, M, K, N, rank):
     _check_full(run, po, d["X"], d["bias"])
 
 
-@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4", "w8a8"])
 def test_lora_rank48(fmt):
     s = S.spec("flux_lora", M=200, K=512, N=640, fmt=fmt)
     d = S.make_layer(s)
@@ -67,10 +67,11 @@ def test_lora_rank48(fmt):
     _check_full(run, po, d["X"], d["bias"])
 
 
-@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4", "w8a8"])
 def test_quantizer_edge_values(fmt):
-    """Zero rows, bf16 subnormals (MXFP4 scale clamped at 2^-127), huge
-    values and exact ties go through K-A; codes and scales bit-exact."""
+    """Zero rows, bf16 subnormals (MXFP4 scale clamped at 2^-127; 8-bit
+    scale below 2^-128), huge values and exact ties go through K-A; codes
+    and scales bit-exact."""
     M, K, N = 48, 512, 64
     x = S.random_bf16(5, (M, K), 2.0)
     x[0] = 0.0
@@ -100,7 +101,7 @@ def test_workspace_reuse_and_determinism():
     assert bool((run.Y == y1).all())
 
 
-@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4", "w8a8"])
 @pytest.mark.parametrize("M,K,N,rank", [(300, 1024, 400, 32), (17, 512, 272, 48), (130, 640, 144, 0)])
 def test_unfused_baseline(fmt, M, K, N, rank):
     """The four-kernel baseline computes the same layer: within the
@@ -122,7 +123,7 @@ def test_unfused_baseline(fmt, M, K, N, rank):
     assert np.array_equal(xq, of["xq"])
 
 
-@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4", "w8a8"])
 def test_residual_iterated_layer(fmt):
     """A layer prepared with residual iteration (refits to W~ - Q(R_prev),
     the best of 6 kept) runs through the same device path: codes bit-exact,

@@ -33,7 +33,7 @@ def _oracle_scales(ws, fmt):
     return np.float16(ws).view(np.uint16) if fmt == "int4" else ws
 
 
-@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4", "w8a8"])
 def test_packer_bit_exact_against_oracle(fmt):
     rng = np.random.default_rng(3)
     x = (rng.standard_t(3, (64, 1024)) * 0.7).astype(np.float32)
@@ -45,6 +45,9 @@ def test_packer_bit_exact_against_oracle(fmt):
     x[4, :32] = -0.0
     x[5, :32] = 1e-39                                # MXFP4 scale clamped at 2^-127
     x[6] *= 1e4
+    x[7, :] = 0.0                                    # all-zero row (8-bit: one scale per row)
+    x[8, :] = 0.0
+    x[8, :8] = [127.0, -3.0, 2.5, -2.5, 0.5, 126.5, -0.5, 1.5]   # 8-bit exact ties at scale 1
     codes, scales = B.pack_host(x, fmt)
     q = Q.quantize(x, fmt)
     assert np.array_equal(codes, q["packed"])
@@ -81,7 +84,7 @@ def _compare_prepare(W, amax, alpha, rank, fmt, lora=None, **kw):
     return pc, po
 
 
-@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4", "w8a8"])
 def test_prepare_matches_oracle_tiny(fmt):
     s = S.spec("tiny")
     d = S.make_layer(s)
@@ -227,12 +230,17 @@ def _rec_off(row, q, j, ks4):
 
 
 def test_workspace_layout_regions():
-    for M, K, r, f in [(1, 128, 0, 0), (4096, 3072, 32, 1), (8192, 3072, 48, 0), (17, 512, 16, 1)]:
+    for M, K, r, f in [(1, 128, 0, 0), (4096, 3072, 32, 1), (8192, 3072, 48, 0), (17, 512, 16, 1),
+                       (17, 512, 16, 2), (4096, 3072, 16, 2)]:
         w = B.workspace_layout(M, K, r, f)
         ks4 = (K // 128 + 3) // 4
         assert w["xq_off"] % 256 == 0 and w["xs_off"] % 256 == 0 and w["z_off"] % 256 == 0
-        assert w["xq_bytes"] == (M + 15) // 16 * 16 * K // 2
-        assert w["xs_bytes"] == (M + 63) // 64 * 64 * ks4 * 16
+        if f == 2:
+            assert w["xq_bytes"] == (M + 15) // 16 * 16 * K
+            assert w["xs_bytes"] == (M + 15) // 16 * 16 * 4
+        else:
+            assert w["xq_bytes"] == (M + 15) // 16 * 16 * K // 2
+            assert w["xs_bytes"] == (M + 63) // 64 * 64 * ks4 * 16
         assert w["xs_off"] >= w["xq_off"] + w["xq_bytes"] and w["z_off"] >= w["xs_off"] + w["xs_bytes"]
         assert w["total"] >= w["z_off"] + w["z_bytes"]
         if r:
@@ -284,6 +292,26 @@ def test_mxfp4_code_layout_positions():
         for t in range(steps):
             for b in range(64):
                 assert wk[_code_off(n, t, b, steps)] == codes[n, 64 * t + b]
+
+
+def test_w8a8_code_and_scale_layout_positions():
+    # 8-bit codes: byte b of 64-byte step t is element 64 t + b; scales as they are
+    K, N = 384, 48
+    steps = K // 64
+    rng = np.random.default_rng(4)
+    codes = rng.integers(0, 256, (N, K)).astype(np.uint8)
+    sc = rng.standard_normal(N).astype(np.float32)
+    prep = {"K": K, "N": N, "rank": 0, "fmt": 2, "smooth_inv": np.ones(K, np.float32), "wq": codes, "ws": sc}
+    kl = B.kernel_layout(prep)
+    wk = kl["wq_k"].reshape(-1)
+    assert wk.size == N * K
+    for n in range(N):
+        for t in range(steps):
+            for b in range(64):
+                assert wk[_code_off(n, t, b, steps)] == codes[n, 64 * t + b]
+    assert np.array_equal(kl["ws_k"].view(np.float32), sc)
+    s = B.layer_sizes(K, N, 16, 2)
+    assert s["wq_canon_bytes"] == N * K and s["ws_canon_bytes"] == N * 4
 
 
 def test_mxfp4_scale_layout_positions():

@@ -35,3 +35,16 @@ def test_kernel_byte_counts_flux_mlp_up():
     b = A.kb_bytes(4096, 12288, 3072, 32, "mxfp4")
     assert abs(b / 1e6 - 128.7) < 0.1
     assert A.main_ops(4096, 12288, 3072) == 2 * 4096 * 12288 * 3072
+
+
+def test_bench_accounting_matches_oracle():
+    # bench.py keeps its own copy of the algorithmic byte counts (the oracle
+    # serves only its CPU-baseline leg); for the 4-bit formats both agree
+    import bench
+    for M, N, K, r in [(4096, 9216, 3072, 32), (4096, 12288, 3072, 32), (8192, 12288, 3072, 48), (256, 512, 512, 16)]:
+        assert bench.main_ops(M, N, K) == A.main_ops(M, N, K)
+        for fmt in ("int4", "mxfp4"):
+            assert bench.ka_bytes(M, K, r, fmt) == A.ka_bytes(M, K, r, fmt)
+            assert bench.kb_bytes(M, N, K, r, fmt) == A.kb_bytes(M, N, K, r, fmt)
+    # 8-bit: one byte per code and one fp32 scale per row
+    assert bench.kb_bytes(16, 32, 128, 16, "w8a8") == 16 * 128 + 64 + 32 * 128 + 128 + 4 * 16 * 16 + 2 * 16 * 32 + 64 + 2 * 16 * 32
