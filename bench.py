@@ -322,7 +322,7 @@ def main():
         "lowrank_overhead": t_stepr / t_step0 - 1.0, "rank0_layer_us": t_step0 * 1e6,
         "layer_us_interleaved": t_stepr * 1e6,
         "unfused": {"layer_us": t_stepu * 1e6, "lowrank_overhead": t_stepu / t_step0 - 1.0,
-                    "kernels": "quantize; down projection (second pass over X); W4A4 GEMM + bias; Y += Z L2'"},
+                    "kernels": "quantize; down projection (second pass over X); quantized GEMM + bias; Y += Z L2'"},
         "rank0_ka_us": float(np.median(ka0)) * 1e3, "rank0_kb_us": float(np.median(kb0)) * 1e3,
         "parity": parity,
         "cpu_baseline": cpu,
@@ -458,7 +458,7 @@ def summarize_profiles(d, config, fmt_override=None):
     rp = (r + 31) // 32 * 32 if r else 0
     kb_names = kb_kernel_names(fmt, K, r)
     ka_names = ("ka_kernel",)
-    short = "kb_mx" if fmt == "mxfp4" else "kb_int4"
+    short = {"mxfp4": "kb_mx", "int4": "kb_int4", "w8a8": "kb_w8a8"}[fmt]
     key = s.name if not fmt_override else f"{s.name}_{fmt}"
     cmds = profile_commands("gpurun_out/prof_" + key, config + (f" --fmt {fmt_override}" if fmt_override else ""))
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
