@@ -375,6 +375,7 @@ constexpr int MX_NBUF = 4;
 constexpr int MX_SC_BYTES = (MX_BM + MX_BN) * 16;     // scale dwords of one 4-step group
 constexpr int MX_DUMMY = MX_NBUF * MX_STEP_BYTES + 2 * MX_SC_BYTES;   // 1 KB per wave, see below
 constexpr int MX_LDS = MX_DUMMY + 8 * 1024;
+constexpr int MX_LDS_LRF = MX_DUMMY + 16 * 1024;   // the dummy region doubles as the first L2' chunk
 
 #define SVDQ_AS3 __attribute__((address_space(3)))
 
@@ -436,7 +437,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const float* __restrict__ zp, int zsplit,
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws, const uint16_t* __restrict__ l2k,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int M, int N, int K, int rpad) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[MX_LDS];
+  // LRF: the low-rank product Z L2' is formed first, while the first code
+  // steps are in flight (float accumulators only, so not for W8)
+  constexpr bool LRF = !W8 && NTR > 0;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[LRF ? MX_LDS_LRF : MX_LDS];
   const uint32_t lds_u32 = (uint32_t)(size_t)(SVDQ_AS3 uint8_t*)lds;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -546,26 +550,6 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
     __syncthreads();
   };
 
-  issue_scales(0);
-#pragma unroll
-  for (int s0 = 0; s0 < 3; ++s0)
-    if (s0 < steps) issue_codes(s0);
-
-  v4f acc[NTW][8];   // [weight tile][token tile]
-#pragma unroll
-  for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) acc[nt][mt] = (v4f){0.f, 0.f, 0.f, 0.f};
-
-  v4i wf[2][NTW];   // weight fragments of the current and the next step
-  v4i tk[4];      // token fragments, three ahead; fragment q sits in slot q & 3
-  wait_for(0);
-  read_scales(0);
-#pragma unroll
-  for (int nt = 0; nt < NTW; ++nt) wf[0][nt] = read_a(0, nt);
-#pragma unroll
-  for (int q = 0; q < 3; ++q) tk[q] = read_b(0, q);
-
   // The lane index is made opaque in these two so that their address
   // arithmetic is redone where they are called instead of being hoisted out
   // of the main loop into live registers.
@@ -593,10 +577,88 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
             ((uint32_t)n * (uint32_t)rpad + 32u * u) * 2u + 16u * ((ln & 3) ^ lswz(row)), ldst + 1024u * unit);
     }
   };
+  // acc += Z L2' for one 32-column chunk of the rank, from Z (rows of the
+  // wave's tokens, bf16 hi and lo) and L2'^T (rows of its out-features) in LDS
+  auto lr_mfma = [&](uint32_t zoff, uint32_t loff, v4f (&ac)[NTW][8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mh = 0; mh < 2; ++mh) {
+      v8bf bh[4], bl[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int mt = 4 * mh + k;
+        const int zrow = 128 * wm + 16 * mt + l16;
+        bh[k] = *reinterpret_cast<const v8bf*>(lds + zoff + zrow * 128 + 16 * (g ^ zswz(zrow)));
+        bl[k] = *reinterpret_cast<const v8bf*>(lds + zoff + zrow * 128 + 16 * ((4 + g) ^ zswz(zrow)));
+      }
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const int lrow = 16 * NTW * wn + mx_nrow(nt, l16);
+        const v8bf af = *reinterpret_cast<const v8bf*>(lds + loff + lrow * 64 + 16 * (g ^ lswz(lrow)));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          ac[nt][4 * mh + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bh[k], ac[nt][4 * mh + k], 0, 0, 0);
+          ac[nt][4 * mh + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bl[k], ac[nt][4 * mh + k], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  v4f acc[NTW][8];   // [weight tile][token tile]
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) acc[nt][mt] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  // Prologue.  LRF: chunk 0 of Z goes to ring buffer 3 and of L2' to the
+  // dummy region (neither is written by code loads before step 0 has passed
+  // its barrier), ahead of the scales and code steps 0-2; the low-rank MFMAs
+  // run as soon as those two have landed, while the code steps are still in
+  // flight.
+  constexpr uint32_t LR_Z = 3 * MX_STEP_BYTES, LR_L = MX_DUMMY;
+  if constexpr (LRF) {
+    issue_z(0, lds_u32 + LR_Z);
+    issue_l2(0, lds_u32 + LR_L);
+  }
+  issue_scales(0);
+#pragma unroll
+  for (int s0 = 0; s0 < 3; ++s0)
+    if (s0 < steps) issue_codes(s0);
+  if constexpr (LRF) {
+    for (int u = 0; u < NTR; ++u) {
+      if (u == 0) {
+        // everything issued after the Z / L2' loads may still be in flight
+        if (steps >= 3) {
+          if constexpr (WAVES == 8)
+            asm volatile("s_waitcnt vmcnt(13)" ::: "memory");   // 1 scale record + 3 x 4 code units
+          else
+            asm volatile("s_waitcnt vmcnt(26)" ::: "memory");   // 2 + 3 x 8
+        } else {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+      } else {
+        __syncthreads();   // every wave is done with chunk u-1
+        issue_z(u, lds_u32 + LR_Z);
+        issue_l2(u, lds_u32 + LR_L);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      __syncthreads();
+      lr_mfma(LR_Z, LR_L, acc);
+    }
+  }
+
+  v4i wf[2][NTW];   // weight fragments of the current and the next step
+  v4i tk[4];      // token fragments, three ahead; fragment q sits in slot q & 3
+  wait_for(0);
+  read_scales(0);
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) wf[0][nt] = read_a(0, nt);
+#pragma unroll
+  for (int q = 0; q < 3; ++q) tk[q] = read_b(0, q);
+
   // Chunk 0 of Z and L2' is fetched right after the barrier of step
   // steps-2: by then every wave has left steps-4 and steps-3, whose buffers
   // take Z and L2' (no code DMA targets them any more).
-  const bool lr_prefetch = NTR > 0 && steps >= 4;
+  const bool lr_prefetch = !LRF && NTR > 0 && steps >= 4;
   const uint32_t zpre = (uint32_t)((steps - 4 + MX_NBUF) % MX_NBUF) * MX_STEP_BYTES;
   const uint32_t lpre = (uint32_t)((steps - 3 + MX_NBUF) % MX_NBUF) * MX_STEP_BYTES;
   auto lr_prefetch_issue = [&]() __attribute__((always_inline)) {
@@ -707,8 +769,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
           acc[nt][mt][i] = (float)__builtin_bit_cast(v4i, acc[nt][mt])[i] * (sw * sxv[mt]);
       }
   }
-  // ---- low-rank up projection and bias, then one 16-byte store per pair
-  if constexpr (NTR > 0) {
+  // ---- low-rank up projection (here only for W8), bias, then one 16-byte
+  // store per pair
+  if constexpr (NTR > 0 && !LRF) {
     for (int u = 0; u < NTR; ++u) {
       uint32_t zoff, loff;
       if (u == 0 && lr_prefetch) {
@@ -727,27 +790,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
       }
-#pragma unroll
-      for (int mh = 0; mh < 2; ++mh) {
-        v8bf bh[4], bl[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int mt = 4 * mh + k;
-          const int zrow = 128 * wm + 16 * mt + l16;
-          bh[k] = *reinterpret_cast<const v8bf*>(lds + zoff + zrow * 128 + 16 * (g ^ zswz(zrow)));
-          bl[k] = *reinterpret_cast<const v8bf*>(lds + zoff + zrow * 128 + 16 * ((4 + g) ^ zswz(zrow)));
-        }
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-          const int lrow = 16 * NTW * wn + mx_nrow(nt, l16);
-          const v8bf af = *reinterpret_cast<const v8bf*>(lds + loff + lrow * 64 + 16 * (g ^ lswz(lrow)));
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            acc[nt][4 * mh + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bh[k], acc[nt][4 * mh + k], 0, 0, 0);
-            acc[nt][4 * mh + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bl[k], acc[nt][4 * mh + k], 0, 0, 0);
-          }
-        }
-      }
+      lr_mfma(zoff, loff, acc);
     }
   }
   // lane holds out-features n_base + 32 p + 8 g + 0..7 of token m for pair p
