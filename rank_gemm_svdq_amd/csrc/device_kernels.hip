@@ -794,10 +794,20 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
     }
   }
   // lane holds out-features n_base + 32 p + 8 g + 0..7 of token m for pair p
+  auto pack8 = [&](int p2, int mt, const float* bv) __attribute__((always_inline)) -> v4i {
+    v4i o;
 #pragma unroll
-  for (int p2 = 0; p2 < NTW / 2; ++p2) {
-    const int n0 = n_base + 32 * p2 + 8 * g;
-    float bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 2; ++i) {
+      o[i] = (int)(bf16_rne(acc[2 * p2][mt][2 * i] + bv[2 * i]) |
+                   (bf16_rne(acc[2 * p2][mt][2 * i + 1] + bv[2 * i + 1]) << 16));
+      o[2 + i] = (int)(bf16_rne(acc[2 * p2 + 1][mt][2 * i] + bv[4 + 2 * i]) |
+                       (bf16_rne(acc[2 * p2 + 1][mt][2 * i + 1] + bv[4 + 2 * i + 1]) << 16));
+    }
+    return o;
+  };
+  auto bias8 = [&](int n0, float* bv) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) bv[i] = 0.f;
     if (bias != nullptr && n0 < N) {
       const v4i braw = *reinterpret_cast<const v4i*>(bias + n0);
 #pragma unroll
@@ -806,19 +816,51 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
         bv[2 * i + 1] = bf16_hi((uint32_t)braw[i]);
       }
     }
+  };
+  if constexpr (NTW == 4 && (NTR > 0 || W8)) {
+    // The two pairs cover 128 consecutive bytes of each token row.  Lanes
+    // r and r + 8 of a 16-lane row swap one 16-byte piece (DPP row rotate
+    // by 8) so that each store instruction writes whole 128-byte lines of
+    // 8 rows instead of half lines of 16: HBM writes drop from 1.33x to
+    // 1.00x of Y.  (The rank-0 MXFP4 instantiation measured slower with it
+    // and keeps the half-line stores.)
+    const int n00 = n_base + 8 * g, n01 = n00 + 32;
+    float bv0[8], bv1[8];
+    bias8(n00, bv0);
+    bias8(n01, bv1);
+    const bool lo8 = l16 < 8;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
-      const int m = m_base + 16 * mt + l16;
-      if (m >= M || n0 >= N) continue;
-      v4i o;
+      const v4i P0 = pack8(0, mt, bv0), P1 = pack8(1, mt, bv1);
+      v4i S, R;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        o[i] = (int)(bf16_rne(acc[2 * p2][mt][2 * i] + bv[2 * i]) |
-                     (bf16_rne(acc[2 * p2][mt][2 * i + 1] + bv[2 * i + 1]) << 16));
-        o[2 + i] = (int)(bf16_rne(acc[2 * p2 + 1][mt][2 * i] + bv[4 + 2 * i]) |
-                         (bf16_rne(acc[2 * p2 + 1][mt][2 * i + 1] + bv[4 + 2 * i + 1]) << 16));
+      for (int i = 0; i < 4; ++i) {
+        S[i] = lo8 ? P1[i] : P0[i];
+        R[i] = __builtin_amdgcn_mov_dpp(S[i], 0x128 /* row_ror:8 */, 0xF, 0xF, false);
       }
-      *reinterpret_cast<v4i*>(Y + (size_t)m * N + n0) = o;
+      // lane r < 8 now holds row r's and row r+8's first halves; lane r+8
+      // holds the second halves of rows r and r+8
+      const int m = m_base + 16 * mt + l16;
+      const int mA = lo8 ? m : m - 8, mB = lo8 ? m + 8 : m;
+      const int nc = lo8 ? n00 : n01;
+      const v4i dA = lo8 ? P0 : R, dB = lo8 ? R : P1;
+      if (nc < N) {
+        if (mA < M) *reinterpret_cast<v4i*>(Y + (size_t)mA * N + nc) = dA;
+        if (mB < M) *reinterpret_cast<v4i*>(Y + (size_t)mB * N + nc) = dB;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int p2 = 0; p2 < NTW / 2; ++p2) {
+      const int n0 = n_base + 32 * p2 + 8 * g;
+      float bv[8];
+      bias8(n0, bv);
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        const int m = m_base + 16 * mt + l16;
+        if (m >= M || n0 >= N) continue;
+        *reinterpret_cast<v4i*>(Y + (size_t)m * N + n0) = pack8(p2, mt, bv);
+      }
     }
   }
 }
