@@ -17,18 +17,22 @@
 // K-B computes Y^T tiles: A = weights (rows n), B = activations (rows m), so
 // each lane owns 4 consecutive outputs n of one token m (an 8-byte store).
 //
-// Layouts (all per row, K split into 128-element steps):
-//   MXFP4 codes: canonical, element 2j in the low nibble of byte j.
-//   MXFP4 scales: row of ceil(steps/4) * 16 bytes, block b = 4t + g at
-//     byte 16 (t / 4) + 4 g + (t % 4) (one dword per lane serves 4 steps).
-//   INT4 codes: within a step's 64 bytes, element k (G = k / 64, g = k % 64
-//     / 16, j = k % 16) sits at byte 16 g + 8 G + j / 2, nibble j % 2, so the
-//     16 bytes of lane group g hold 16 elements of each of the step's two
-//     64-element groups.
-//   INT4 activation scales: per row ceil(steps/4) * 16 bytes, the fp16 pair
-//     of step t (groups 2t, 2t+1) in the dword at byte 16 (t / 4) + 4 (t % 4).
-//   INT4 weight scales: [N/4][4 ceil(steps/4)][4 rows][2 groups] fp16, so a
-//     4-row block holds 64 contiguous bytes per 4 steps.
+// Layouts (offsets in layout.h; K split into steps of 64 code bytes per
+// row: 128 4-bit elements or 64 int8 elements):
+//   Codes (activations and weights, every format): 1 KB units of 16 rows x
+//     one step, ordered [row / 16][step]; inside a unit, 16-byte slot
+//     4 (row % 16) + q holds chunk q ^ swz(row % 32) of the row-step.  MXFP4
+//     and W8A8 keep canonical byte order inside a row-step; INT4 places
+//     element k (G = k / 64, g = k % 64 / 16, j = k % 16) at byte
+//     16 g + 8 G + j / 2, nibble j % 2, so the 16 bytes of lane group g
+//     hold 16 elements of each of the step's two 64-element groups.
+//   Scale records (MXFP4 both operands, INT4 activations): 16 bytes per row
+//     and 4 steps, 1 KB units of 64 rows ordered [row / 64][4-step group];
+//     MXFP4 block 4 t + q at record byte 4 q + t % 4, INT4 the fp16 pair of
+//     step t at bytes 4 (t % 4) and + 2.
+//   INT4 weight scales: 2 KB units of 128 rows x 4 steps, [4-row block]
+//     [step % 4][row % 4][group of 64] fp16.
+//   W8A8 scales: fp32 per token row (workspace) and per out-feature (layer).
 //   Down factor: L1' (bf16), ordered [step][s][n-tile][lane][8] with
 //     k = 128 step + 32 (lane/16) + 8 s + i, n = 16 n-tile + lane % 16.
 //   Up factor: L2'^T, [N][rpad] bf16, rpad = rank rounded up to 32.
