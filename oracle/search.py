@@ -19,10 +19,20 @@ S3  The score is the relative Frobenius error ||Y - X W||_F / ||X W||_F
     (any monotone function of the squared error selects the same pair);
     ties keep the earlier candidate in the order above.
 
+The doc caps the calibration calls each group keeps by reservoir sampling.
+S4  Reading: Algorithm R (Vitter, "Random sampling with a reservoir", ACM
+    TOMS 1985): the first k calls fill the reservoir; call i >= k draws j
+    uniform in 0..i and replaces slot j when j < k.  The draws come from
+    SplitMix64 (Steele, Lea and Flood, OOPSLA 2014) seeded with the caller's
+    seed, one output per call i >= k, mapped to 0..i by the high 64 bits of
+    the 128-bit product output * (i + 1).  The kept call indices are returned
+    in increasing order.
+
 Pins (tests/test_oracle_search.py): the candidate set against the pages'
 count and description, the selection rule on hand-made score lists, an
-exactly representable layer for which only (0, 0) is lossless, and an
-outlier-activation layer for which smoothing must win.
+exactly representable layer for which only (0, 0) is lossless, an
+outlier-activation layer for which smoothing must win, and the reservoir's
+inclusion frequencies (k / n for every call) over many seeds.
 """
 
 import numpy as np
@@ -57,6 +67,33 @@ def select(errors):
         if np.isfinite(e) and (best is None or e < errors[best]):
             best = i
     return best
+
+
+MASK64 = (1 << 64) - 1
+
+
+def splitmix64(state):
+    """One SplitMix64 step: (next state, output), 64-bit unsigned ints."""
+    state = (state + 0x9E3779B97F4A7C15) & MASK64
+    z = state
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & MASK64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & MASK64
+    return state, z ^ (z >> 31)
+
+
+def reservoir_select(n_calls, k, seed):
+    """S4: indices of the calls kept by a reservoir of size k."""
+    n_calls, k = int(n_calls), int(k)
+    if k <= 0 or n_calls <= 0:
+        return []
+    slots = list(range(min(k, n_calls)))
+    state = int(seed) & MASK64
+    for i in range(k, n_calls):
+        state, r = splitmix64(state)
+        j = (r * (i + 1)) >> 64
+        if j < k:
+            slots[j] = i
+    return sorted(slots)
 
 
 def smooth_search(w, x_cal, rank, fmt, grids=20, residual_iters=1):

@@ -38,7 +38,7 @@ def _search(w, x, rank, fmt, grids):
     return r, ob, oerr
 
 
-@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4", "w8a8"])
 def test_search_small_grid(fmt):
     s = S.spec("tiny", M=128, K=512, N=256, rank=16, fmt=fmt)
     d = S.make_layer(s)

@@ -127,7 +127,8 @@ def test_prepare_lora_matches_oracle():
     assert np.array_equal(bf16_from_bits(pc["l2"])[32:], po["l2p"][32:])
 
 
-@pytest.mark.parametrize("fmt,rank,early", [("int4", 16, False), ("mxfp4", 48, False), ("mxfp4", 48, True)])
+@pytest.mark.parametrize("fmt,rank,early", [("int4", 16, False), ("mxfp4", 48, False), ("mxfp4", 48, True),
+                                             ("w8a8", 16, False)])
 def test_residual_iterations_match_oracle(fmt, rank, early):
     # AutoRound doc, "Residual iteration": same error sequence, same kept
     # iteration and the same codes as the oracle's loop

@@ -62,3 +62,37 @@ def test_outlier_activations_select_smoothing():
     assert pairs[best][0] > 0.0
     assert errs[best] < 0.8 * errs[0]
     assert all(np.isfinite(errs))
+
+
+def test_reservoir_small_cases():
+    assert SR.reservoir_select(5, 8, 1) == [0, 1, 2, 3, 4]      # fewer calls than slots: all kept
+    assert SR.reservoir_select(8, 8, 1) == list(range(8))
+    assert SR.reservoir_select(0, 4, 1) == [] and SR.reservoir_select(4, 0, 1) == []
+    got = SR.reservoir_select(1000, 128, 7)
+    assert len(got) == 128 and len(set(got)) == 128 and all(0 <= i < 1000 for i in got)
+    assert got == SR.reservoir_select(1000, 128, 7)               # deterministic per seed
+    assert got != SR.reservoir_select(1000, 128, 8)
+
+
+def test_reservoir_inclusion_is_uniform():
+    # Algorithm R keeps every call with probability k / n; over many seeds
+    # each call's inclusion count is Binomial(trials, k / n)
+    n, k, trials = 40, 10, 4000
+    counts = np.zeros(n)
+    for seed in range(trials):
+        for i in SR.reservoir_select(n, k, seed):
+            counts[i] += 1
+    p = k / n
+    sd = np.sqrt(trials * p * (1 - p))
+    assert np.all(np.abs(counts - trials * p) < 5 * sd)
+    # the late calls are not favoured or starved relative to the early ones
+    assert abs(counts[:20].mean() - counts[20:].mean()) < 3 * sd / np.sqrt(20) * np.sqrt(2) + 1
+
+
+def test_splitmix64_is_a_bijective_mixer_on_small_states():
+    # distinct states give distinct outputs (the finaliser is invertible)
+    outs = {SR.splitmix64(s)[1] for s in range(5000)}
+    assert len(outs) == 5000
+    # and the output bits are balanced
+    bits = np.array([[(SR.splitmix64(s)[1] >> b) & 1 for b in range(64)] for s in range(2000)])
+    assert np.all(np.abs(bits.mean(0) - 0.5) < 0.06)
