@@ -223,6 +223,16 @@ typedef struct svdq_search_result {
                                      prepared (optional, caller-allocated) */
 } svdq_search_result;
 
+/* Reservoir selection of calibration calls (AutoRound doc, "Smooth search":
+ * each group keeps at most k calls, chosen by reservoir sampling).  Algorithm
+ * R (Vitter 1985): calls 0..k-1 fill the reservoir; call i >= k draws
+ * j = hi64(r * (i + 1)) with r the next SplitMix64 output (Steele, Lea and
+ * Flood 2014; state starts at `seed`) and replaces slot j when j < k.
+ * Writes the min(n_calls, k) kept indices in increasing order to out (host,
+ * caller-allocated) and returns their count; 0 if n_calls <= 0 or k <= 0;
+ * -1 if out is NULL. */
+int64_t svdq_reservoir_select(int64_t n_calls, int64_t k, uint64_t seed, int64_t* out);
+
 /* Device workspace bytes of svdq_smooth_search (0 on an invalid shape). */
 size_t svdq_search_workspace_bytes(int32_t M, int32_t K, int32_t N, int32_t rank, int32_t fmt);
 

@@ -17,7 +17,7 @@ __all__ = [
     "layer_sizes", "workspace_layout", "workspace_bytes", "calib_absmax", "pack_host",
     "prepare", "attach_lora", "kernel_layout", "unpack_activations", "DeviceLayer",
     "quantize_lora_down", "gemm_lora_up", "linear_forward", "linear_forward_unfused", "fmt_code", "LIB_PATH",
-    "ABI_VERSION", "smooth_candidates", "search_workspace_bytes", "smooth_search", "SearchOpts", "SearchResult",
+    "ABI_VERSION", "reservoir_select", "smooth_candidates", "search_workspace_bytes", "smooth_search", "SearchOpts", "SearchResult",
 ]
 
 INT4 = 0
@@ -131,6 +131,8 @@ def lib():
     L.svdq_gemm_lora_up.argtypes = [C.POINTER(Layer), vp, sz, i32, vp, vp]
     L.svdq_linear_forward.argtypes = [C.POINTER(Layer), vp, i32, vp, vp, sz, vp]
     L.svdq_linear_forward_unfused.argtypes = [C.POINTER(Layer), vp, i32, vp, vp, sz, vp]
+    L.svdq_reservoir_select.restype = C.c_int64
+    L.svdq_reservoir_select.argtypes = [C.c_int64, C.c_int64, C.c_uint64, vp]
     L.svdq_smooth_candidates.restype = i32
     L.svdq_smooth_candidates.argtypes = [i32, vp, vp]
     L.svdq_search_workspace_bytes.restype = sz
@@ -397,3 +399,13 @@ def smooth_search(W, X_cal, rank, fmt, grids=20, residual_iters=1, early_stop=Fa
     out["ws"] = _scales_view(out["ws"], f)
     out.update(K=K, N=N, rank=rank, fmt=f)
     return {"best": res.best, "alpha": res.alpha, "beta": res.beta, "errors": errors, "prepared": out}
+
+
+def reservoir_select(n_calls, k, seed):
+    """Indices of the calibration calls a reservoir of size k keeps
+    (svdq_reservoir_select), in increasing order."""
+    out = np.empty(max(1, min(int(n_calls), int(k))), np.int64)
+    n = lib().svdq_reservoir_select(int(n_calls), int(k), int(seed) & ((1 << 64) - 1), _p(out))
+    if n < 0:
+        raise SvdqError(1, "svdq_reservoir_select")
+    return out[:n].tolist()

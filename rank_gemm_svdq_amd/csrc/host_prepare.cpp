@@ -545,6 +545,26 @@ svdq_status svdq_prepare(const float* W, const float* act_amax, int32_t K, int32
   return SVDQ_OK;
 }
 
+int64_t svdq_reservoir_select(int64_t n_calls, int64_t k, uint64_t seed, int64_t* out) {
+  if (!out) return -1;
+  if (n_calls <= 0 || k <= 0) return 0;
+  const int64_t kept = std::min(n_calls, k);
+  for (int64_t i = 0; i < kept; ++i) out[i] = i;
+  uint64_t state = seed;
+  for (int64_t i = k; i < n_calls; ++i) {
+    // SplitMix64
+    state += 0x9E3779B97F4A7C15ull;
+    uint64_t z = state;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    const uint64_t j = (uint64_t)(((unsigned __int128)z * (unsigned __int128)(uint64_t)(i + 1)) >> 64);
+    if (j < (uint64_t)k) out[j] = i;
+  }
+  std::sort(out, out + kept);
+  return kept;
+}
+
 svdq_status svdq_kernel_layout(int32_t K, int32_t N, int32_t rank, int32_t fmt, const float* smooth_inv,
                                const uint8_t* wq, const uint8_t* ws, const uint16_t* l1, const uint16_t* l2,
                                uint8_t* wq_k, uint8_t* ws_k, uint16_t* l1k, uint16_t* l2k) {

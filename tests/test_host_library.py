@@ -370,3 +370,10 @@ def test_smooth_search_validates_before_hip():
     Wn = W.copy()
     Wn[1, 1] = np.inf
     assert call(w=Wn.ctypes.data_as(C.c_void_p)) == 6
+
+
+def test_reservoir_select_matches_oracle():
+    from oracle import search as SR
+    for n, k, seed in [(5, 8, 1), (1000, 128, 7), (300, 17, 2 ** 63 + 5), (129, 128, 0), (0, 3, 1), (3, 0, 1)]:
+        assert B.reservoir_select(n, k, seed) == SR.reservoir_select(n, k, seed)
+    assert B.lib().svdq_reservoir_select(10, 3, 1, None) == -1
