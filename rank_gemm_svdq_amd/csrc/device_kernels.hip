@@ -353,17 +353,18 @@ __device__ __forceinline__ int swz(int r, int c) { return r * 64 + 16 * (c ^ swz
 // 4 x 8 MFMA tiles of 16 x 16 (128 fp32 accumulators per lane).
 //
 // Codes travel global -> LDS by direct-to-LDS loads (no register staging)
-// into a ring of four 32 KB step buffers, three steps ahead of the MFMAs;
-// scale dwords (one per row and 4 steps) travel the same way into a double
-// buffer.  The K loop runs in pairs of steps: the weight fragments of the
-// next step are read into the other half of a two-deep register set while
-// the current MFMAs run, and token fragments stream through four registers
-// three MFMA groups ahead, so the barrier at the top of each step exposes no
-// LDS latency and no fragment is ever copied between registers.  A 16-bit
-// LDS read per pair gives each scale register the E8M0 bytes of both steps;
-// the MFMA's op_sel picks the byte.  The low-rank epilogue (Z L2') is
-// applied after the K loop from Z and L2' tiles DMA'd into ring buffers the
-// last steps no longer use.
+// into a ring of four 32 KB step buffers; scale dwords (one per row and 4
+// steps) travel the same way into a double buffer.  The K loop runs in
+// pairs of steps with one barrier per pair: the first step of a pair loads
+// the next pair into the two buffers the previous pair has left.  The
+// weight fragments of the next step are read into the other half of a
+// two-deep register set while the current MFMAs run, and token fragments
+// stream through four registers three MFMA groups ahead, so no fragment is
+// ever copied between registers.  A 16-bit LDS read per pair gives each
+// scale register the E8M0 bytes of both steps; the MFMA's op_sel picks the
+// byte.  The low-rank product Z L2' is formed before the K loop while the
+// first code steps are in flight (MXFP4), or after it from Z and L2' tiles
+// loaded into ring buffers the last pair no longer uses (W8A8).
 //
 // Weight rows are permuted inside each pair of 16-row MFMA tiles (2p, 2p+1):
 // MFMA row q of tile 2p + h is out-feature 32 p + 8 (q / 4) + 4 h + q % 4, so
@@ -540,20 +541,6 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
     for (int nt = 0; nt < NTW; ++nt)
       asc[nt] = *reinterpret_cast<const uint16_t*>(sc + ((MX_BM + 16 * NTW * wn + mx_nrow(nt, l16)) * 4 + g) * 4);
   };
-  // every DMA issued before step s's must be done; only step s + 1's (UPW
-  // per wave) may still be in flight
-  auto wait_for = [&](int s) __attribute__((always_inline)) {
-    if (s + 1 < steps) {
-      if constexpr (UPW == 4)
-        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    }
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  };
-
   // The lane index is made opaque in these two so that their address
   // arithmetic is redone where they are called instead of being hoisted out
   // of the main loop into live registers.
@@ -615,7 +602,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
 
   // Prologue.  LRF: chunk 0 of Z goes to ring buffer 3 and of L2' to the
   // dummy region (neither is written by code loads before step 0 has passed
-  // its barrier), ahead of the scales and code steps 0-2; the low-rank MFMAs
+  // its barrier), ahead of the scales and code steps 0-1; the low-rank MFMAs
   // run as soon as those two have landed, while the code steps are still in
   // flight.
   constexpr uint32_t LR_Z = 3 * MX_STEP_BYTES, LR_L = MX_DUMMY;
@@ -625,17 +612,17 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
   }
   issue_scales(0);
 #pragma unroll
-  for (int s0 = 0; s0 < 3; ++s0)
+  for (int s0 = 0; s0 < 2; ++s0)
     if (s0 < steps) issue_codes(s0);
   if constexpr (LRF) {
     for (int u = 0; u < NTR; ++u) {
       if (u == 0) {
         // everything issued after the Z / L2' loads may still be in flight
-        if (steps >= 3) {
+        if (steps >= 2) {
           if constexpr (WAVES == 8)
-            asm volatile("s_waitcnt vmcnt(13)" ::: "memory");   // 1 scale record + 3 x 4 code units
+            asm volatile("s_waitcnt vmcnt(9)" ::: "memory");    // 1 scale record + 2 x 4 code units
           else
-            asm volatile("s_waitcnt vmcnt(26)" ::: "memory");   // 2 + 3 x 8
+            asm volatile("s_waitcnt vmcnt(18)" ::: "memory");   // 2 + 2 x 8
         } else {
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
@@ -652,62 +639,74 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
 
   v4i wf[2][NTW];   // weight fragments of the current and the next step
   v4i tk[4];      // token fragments, three ahead; fragment q sits in slot q & 3
-  wait_for(0);
-  read_scales(0);
-#pragma unroll
-  for (int nt = 0; nt < NTW; ++nt) wf[0][nt] = read_a(0, nt);
-#pragma unroll
-  for (int q = 0; q < 3; ++q) tk[q] = read_b(0, q);
 
-  // Chunk 0 of Z and L2' is fetched right after the barrier of step
-  // steps-2: by then every wave has left steps-4 and steps-3, whose buffers
-  // take Z and L2' (no code DMA targets them any more).
-  const bool lr_prefetch = !LRF && NTR > 0 && steps >= 4;
-  const uint32_t zpre = (uint32_t)((steps - 4 + MX_NBUF) % MX_NBUF) * MX_STEP_BYTES;
-  const uint32_t lpre = (uint32_t)((steps - 3 + MX_NBUF) % MX_NBUF) * MX_STEP_BYTES;
-  auto lr_prefetch_issue = [&]() __attribute__((always_inline)) {
-    if (lr_prefetch) {
+  // The K loop runs in pairs of steps (t, t+1), t even, with one barrier
+  // per pair.  At the top of a pair every wave waits for all its loads and
+  // passes the barrier: steps t and t+1 are then in LDS, and the two ring
+  // buffers of the previous pair are free for steps t+2 and t+3, whose
+  // loads the first step of the pair issues (one 1 KB unit per MFMA group
+  // with 8 waves).  Loads past the last step re-read it into this wave's
+  // dummy region (in bounds, and the loop stays free of branches).
+  //
+  // Chunk 0 of Z and L2' (the low-rank epilogue, W8) is fetched at the top
+  // of the last pair, t_last, into the buffers of t_last-2 and t_last-1,
+  // which no load targets any more.
+  const int t_last = (steps - 1) & ~1;
+  const bool lr_prefetch = !LRF && NTR > 0 && t_last >= 2;
+  const uint32_t zpre = (uint32_t)((t_last + 2) % MX_NBUF) * MX_STEP_BYTES;
+  const uint32_t lpre = (uint32_t)((t_last + 3) % MX_NBUF) * MX_STEP_BYTES;
+  auto pair_top = [&](int t) __attribute__((always_inline)) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if ((t & 3) == 0 && (t >> 2) + 1 < ks4) issue_scales((t >> 2) + 1);
+    if (lr_prefetch && t == t_last) {
       issue_z(0, lds_u32 + zpre);
       issue_l2(0, lds_u32 + lpre);
     }
+    // scale bytes of steps t, t+1 and the first fragments of step t
+    const uint32_t b0 = buf_of(t);
+    read_scales(t);
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) wf[0][nt] = read_a(b0, nt);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) tk[q] = read_b(b0, q);
   };
-  // step t, J = t & 1: the barrier publishes step t+1's buffer; the buffer
-  // of step t-1 (all waves are past it) receives step t+3.  While the MFMAs
-  // of t run, the weight fragments of t+1 and the token fragments three MFMA
-  // groups ahead are read.  The scale registers hold the bytes of steps
-  // (t & ~1, t | 1) in their low half; the MFMA's op_sel picks byte J.  The
-  // last step also reads the next buffer; those reads stay inside LDS and
-  // are never used.
-  auto step = [&](int t, auto jtag, auto hooktag) __attribute__((always_inline)) {
+  // step t, J = t & 1.  While the MFMAs of t run, the token fragments three
+  // MFMA groups ahead are read and, in the first step of a pair, the weight
+  // fragments of t+1.  The scale registers hold the bytes of steps (t & ~1,
+  // t | 1) in their low half; the MFMA's op_sel picks byte J.  LAST: the
+  // second step of a pair (or a single trailing step), which issues no loads
+  // and reads nothing of the next step.
+  auto step = [&](int t, auto jtag, auto lasttag) __attribute__((always_inline)) {
     constexpr int J = decltype(jtag)::value;
-    constexpr int HOOK = decltype(hooktag)::value;   // 0 none, 1 always, 2 at step steps-2
-    wait_for(t + 1);
-    if ((t & 3) == 0 && (t >> 2) + 1 < ks4) issue_scales((t >> 2) + 1);
-    if constexpr (HOOK == 1) lr_prefetch_issue();
-    if constexpr (HOOK == 2) {
-      if (t == steps - 2) lr_prefetch_issue();
-    }
+    constexpr bool LAST = decltype(lasttag)::value;
     const uint32_t bc = buf_of(t), bn = buf_of(t + 1);
-    // The code loads of step t+3 go out one per odd MFMA group, so no wave
-    // stalls its MFMAs behind a burst of vector-memory issues.  In the last
-    // three steps there is no step t+3: the loads then re-read the last step
-    // (in bounds) into this wave's 1 KB dummy region, which keeps the loop
-    // free of branches and every step's load count (the vmcnt arithmetic)
-    // the same.
-    const bool more = t + 3 < steps;
-    const uint8_t* csrc = cbase + (size_t)(more ? t + 3 : steps - 1) * 1024;
-    const uint32_t cdst = more ? lds_u32 + (uint32_t)((t + 3) % MX_NBUF) * MX_STEP_BYTES + (uint32_t)wave * (1024u * UPW)
+    const bool more = t + 2 < steps, more2 = t + 3 < steps;
+    const uint8_t* csrc = cbase + (size_t)(more ? t + 2 : steps - 1) * 1024;
+    const uint32_t cdst = more ? lds_u32 + (uint32_t)((t + 2) % MX_NBUF) * MX_STEP_BYTES + (uint32_t)wave * (1024u * UPW)
                                : lds_u32 + MX_DUMMY + (uint32_t)wave * 1024u;
     const uint32_t cinc = more ? 1024u : 0u;
+    const uint8_t* csrc2 = cbase + (size_t)(more2 ? t + 3 : steps - 1) * 1024;
+    const uint32_t cdst2 = more2 ? lds_u32 + (uint32_t)((t + 3) % MX_NBUF) * MX_STEP_BYTES + (uint32_t)wave * (1024u * UPW)
+                                 : lds_u32 + MX_DUMMY + (uint32_t)wave * 1024u;
+    const uint32_t cinc2 = more2 ? 1024u : 0u;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
-      if constexpr (UPW == 8) {
-        dma16(csrc, coff[mt], cdst + cinc * mt);
+      if constexpr (!LAST) {
+        // groups 0-3 load step t+2, groups 4-7 step t+3; UPW / 4 units each
+#pragma unroll
+        for (int j = 0; j < UPW / 4; ++j) {
+          const int u = (UPW / 4) * (mt & 3) + j;
+          if (mt < 4)
+            dma16(csrc, coff[u], cdst + cinc * u);
+          else
+            dma16(csrc2, coff[u], cdst2 + cinc2 * u);
+        }
+        if (mt < NTW) wf[J ^ 1][mt] = read_a(bn, mt);
+        tk[(mt + 3) & 3] = mt + 3 < 8 ? read_b(bc, mt + 3) : read_b(bn, mt - 5);
       } else {
-        if (mt & 1) dma16(csrc, coff[mt >> 1], cdst + cinc * (mt >> 1));
+        if (mt + 3 < 8) tk[(mt + 3) & 3] = read_b(bc, mt + 3);
       }
-      if (mt < NTW) wf[J ^ 1][mt] = read_a(bn, mt);
-      tk[(mt + 3) & 3] = mt + 3 < 8 ? read_b(bc, mt + 3) : read_b(bn, mt - 5);
       const v4i bq = tk[mt & 3];
       if constexpr (W8) {
         // int8 x int8 with exact int32 accumulation in the same registers
@@ -732,27 +731,16 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
   };
   using J0 = std::integral_constant<int, 0>;
   using J1 = std::integral_constant<int, 1>;
-  using H0 = std::integral_constant<int, 0>;
-  using H1 = std::integral_constant<int, 1>;
-  using H2 = std::integral_constant<int, 2>;
-  // Pairs of steps; one loop exit keeps the accumulators in place.  With an
-  // even step count the last pair is peeled and the prefetch sits in it;
-  // with an odd one the prefetch is tested in the loop and one step follows.
-  if constexpr (!ODD) {
-    for (int t0 = 0; t0 < steps - 2; t0 += 2) {
-      step(t0, J0{}, H0{});
-      step(t0 + 1, J1{}, H0{});
-      read_scales(t0 + 2);
-    }
-    step(steps - 2, J0{}, H1{});
-    step(steps - 1, J1{}, H0{});
-  } else {
-    for (int t0 = 0; t0 < steps - 1; t0 += 2) {
-      step(t0, J0{}, H0{});
-      step(t0 + 1, J1{}, H2{});
-      read_scales(t0 + 2);
-    }
-    step(steps - 1, J0{}, H0{});
+  using L0 = std::integral_constant<bool, false>;
+  using L1 = std::integral_constant<bool, true>;
+  for (int t0 = 0; t0 < (ODD ? steps - 1 : steps); t0 += 2) {
+    pair_top(t0);
+    step(t0, J0{}, L0{});
+    step(t0 + 1, J1{}, L1{});
+  }
+  if constexpr (ODD) {
+    pair_top(steps - 1);
+    step(steps - 1, J0{}, L1{});
   }
 
   if constexpr (W8) {
