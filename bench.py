@@ -159,6 +159,9 @@ def main():
     ap.add_argument("--residual-iters", type=int, metavar="T", default=0,
                     help="time the host preparation of the workload's layer with T residual iterations "
                          "and print that JSON line instead")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="time the vendor library's plain GEMMs (through torch) on the workload's shape "
+                         "beside this library's forward and print that JSON line instead")
     args = ap.parse_args()
     if args.residual_iters:
         return bench_residual(args)
@@ -188,6 +191,8 @@ def main():
     s = S.spec(args.config, **over)
     if args.smooth_search:
         return bench_search(args, s)
+    if args.vendor_gemm:
+        return bench_vendor(args, s)
     M, K, N, fmt = s.M, s.K, s.N, s.fmt
     log(f"workload {s.name}: M={M} K={K} N={N} rank={s.rank}+{s.lora_rank} fmt={fmt}")
     d = S.make_layer(s)
@@ -436,6 +441,96 @@ def bench_search(args, s):
         "host_threads": int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count(),
         "best": {"alpha": r["alpha"], "beta": r["beta"], "score": float(r["errors"][r["best"]])},
         "scores": [float(e) for e in r["errors"]],
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_vendor(args, s):
+    """Context, not a baseline of this method: the vendor GEMMs reachable
+    from torch (hipBLASLt) on the layer's M x K x N with random operands --
+    bf16, int8, FP8 E4M3 with one scale per tensor, MXFP4 with E8M0 scales
+    per 32 -- next to this library's whole forward (K-A + K-B, low-rank
+    branch and bias included) on the layer itself."""
+    import torch
+    import torch.nn.functional as TF
+    import rank_gemm_svdq_amd as B
+    from rank_gemm_svdq_amd import synthetic as S
+
+    M, K, N = s.M, s.K, s.N
+    ops = main_ops(M, N, K)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.steps
+        return {"us": us, "TOPS": ops / us / 1e6}
+
+    res = {}
+    d = S.make_layer(s)
+    lora = {"A": d["lora_A"], "B": d["lora_B"], "strength": 1.0} if s.lora_rank else None
+    amax = B.calib_absmax(S.bf16_bits_of(d["X_cal"]))
+    prep = B.prepare(d["W"], amax, s.alpha, s.rank, s.fmt, lora=lora)
+    lay = B.DeviceLayer(prep, S.bf16_bits_of(d["bias"]))
+    X = torch.from_numpy(S.bf16_bits_of(d["X"]).view(np.int16)).cuda()
+    Y = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    ws = lay.workspace(M)
+
+    def ours(tag):
+        res[f"svdq_linear_forward_{tag}"] = timed(lambda: B.linear_forward(lay, X, Y, ws))
+        # K-B alone (quantized GEMM + low-rank up projection + bias) on the
+        # codes K-A left in the workspace
+        B.quantize_lora_down(lay, X, ws)
+        res[f"svdq_gemm_lora_up_{tag}"] = timed(lambda: B.gemm_lora_up(lay, ws, M, Y))
+
+    # this library first and last, the vendor GEMMs between (clock drift shows)
+    ours("first")
+    # K-B once more with uniformly random code bytes in place of both
+    # operands' codes (scales kept): the vendor GEMMs below run on random
+    # operands too, and random codes keep the matrix units busiest
+    wl = B.workspace_layout(M, K, s.rank, s.fmt)
+    gr = torch.Generator(device="cuda")
+    gr.manual_seed(1)
+    wsv = ws.view(torch.uint8) if ws.dtype != torch.uint8 else ws
+    xq = wsv[wl["xq_off"]:wl["xq_off"] + wl["xq_bytes"]]
+    xq.copy_(torch.randint(0, 256, xq.shape, device="cuda", dtype=torch.uint8, generator=gr))
+    wq = lay.wq.view(torch.uint8) if lay.wq.dtype != torch.uint8 else lay.wq
+    wq_saved = wq.clone()
+    wq.copy_(torch.randint(0, 256, wq.shape, device="cuda", dtype=torch.uint8, generator=gr))
+    res["svdq_gemm_lora_up_random_codes"] = timed(lambda: B.gemm_lora_up(lay, ws, M, Y))
+    wq.copy_(wq_saved)
+    del wq_saved
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16, generator=g)
+    b = torch.randn(N, K, device="cuda", dtype=torch.bfloat16, generator=g)
+    res["bf16_matmul"] = timed(lambda: a @ b.t())
+    ai = torch.randint(-127, 128, (M, K), device="cuda", dtype=torch.int8, generator=g)
+    bi = torch.randint(-127, 128, (N, K), device="cuda", dtype=torch.int8, generator=g)
+    res["int8_int_mm"] = timed(lambda: torch._int_mm(ai, bi.t()))
+    a8, b8 = a.to(torch.float8_e4m3fn), b.to(torch.float8_e4m3fn)
+    one = torch.ones((), device="cuda")
+    res["fp8_e4m3_scaled_mm"] = timed(lambda: torch._scaled_mm(a8, b8.t(), one, one, out_dtype=torch.bfloat16))
+    af = torch.randint(0, 256, (M, K // 2), device="cuda", dtype=torch.uint8, generator=g).view(torch.float4_e2m1fn_x2)
+    bf = torch.randint(0, 256, (N, K // 2), device="cuda", dtype=torch.uint8, generator=g).view(torch.float4_e2m1fn_x2)
+    sa = torch.randint(120, 128, (M, K // 32), device="cuda", dtype=torch.uint8, generator=g).view(torch.float8_e8m0fnu)
+    sb = torch.randint(120, 128, (N, K // 32), device="cuda", dtype=torch.uint8, generator=g).view(torch.float8_e8m0fnu)
+    bw, nsw = TF.ScalingType.BlockWise1x32, TF.SwizzleType.NO_SWIZZLE
+    res["mxfp4_scaled_mm"] = timed(lambda: TF.scaled_mm(af, bf.t(), sa, bw, sb, bw, swizzle_a=nsw, swizzle_b=nsw,
+                                                        output_dtype=torch.bfloat16))
+    del a, b, ai, bi, a8, b8, af, bf, sa, sb
+
+    ours("last")
+    out = {
+        "metric": "vendor_gemm_context", "unit": "us", "n_gpus": 1, "data": "synthetic",
+        "config": {"workload": s.name, "M": M, "K": K, "N": N, "rank": s.rank, "format": s.fmt},
+        "ops_per_call": ops, "steps": args.steps, "warmup": args.warmup, "results": res,
     }
     print(json.dumps(out), flush=True)
 
