@@ -360,6 +360,8 @@ PROFILE_STEPS = {
              "python -u bench.py --config {config} --steps 3 --warmup 1 --skip-oracle --calib-copy",
     "write": "--pmc WRITE_SIZE --output-format csv -d {dir}/write -o run -- "
              "python -u bench.py --config {config} --steps 3 --warmup 1 --skip-oracle --calib-copy",
+    "mfma": "--pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_WAVES --output-format csv "
+            "-d {dir}/mfma -o run -- python -u bench.py --config {config} --steps 3 --warmup 1 --skip-oracle",
 }
 
 
@@ -656,6 +658,47 @@ def summarize_profiles(d, config, fmt_override=None):
               "fetch": f_, "write": w_, "commands": [cmds["fetch"], cmds["write"]]}
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(t, fh, indent=1, sort_keys=True)
+    print("\n".join(lines))
+    if os.path.isdir(os.path.join(d, "mfma")):
+        summarize_mfma(d, key, M, N, K, r, fmt, kb_names, kb_avg, cmds["mfma"], short)
+
+
+def summarize_mfma(d, key, M, N, K, r, fmt, kb_names, kb_avg, cmd, short):
+    """MFMA utilisation of K-B from counters: SQ_VALU_MFMA_BUSY_CYCLES (summed
+    over the SIMDs) per SIMD against SQ_BUSY_CYCLES (summed over the shader
+    engines) per engine, i.e. the share of busy cycles in which a SIMD's
+    matrix pipe is busy; the engine cycles over the kernel-trace duration
+    give the clock the kernel ran at."""
+    cc = _csv(_find(os.path.join(d, "mfma"), "counter_collection.csv"))
+    agent = [a for a in _csv(_find(os.path.join(d, "mfma"), "agent_info.csv")) if int(a.get("Simd_Count", 0) or 0) > 0]
+    simds = int(agent[0]["Simd_Count"])
+    engines = int(agent[0]["Num_Shader_Banks"])
+    vals = {}
+    for row in cc:
+        if _matches(row["Kernel_Name"], kb_names):
+            vals.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+    mean = {k: float(np.mean(v)) for k, v in vals.items()}
+    busy_simd = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / simds
+    busy_se = mean["SQ_BUSY_CYCLES"] / engines
+    ops = main_ops(M, N, K)
+    ideal = ops / simds / (PEAK[fmt] / simds / 2.4e9)   # MFMA cycles per SIMD at the dense peak rate
+    lines = [f"# MFMA utilisation of K-B, {key} (M={M} K={K} N={N} rank={r} {fmt})", "",
+             "Command (from the repository root, TMPDIR=/tmp):", "", "    " + cmd, "",
+             f"Agent: {simds} SIMDs, {engines} shader engines. Means over {len(vals.get('SQ_BUSY_CYCLES', []))} "
+             f"dispatches of {kb_names[0]}.", "",
+             "| counter | per dispatch | per SIMD or engine |", "|---|---|---|",
+             f"| SQ_VALU_MFMA_BUSY_CYCLES | {mean['SQ_VALU_MFMA_BUSY_CYCLES']:.4g} | {busy_simd:.0f} per SIMD |",
+             f"| SQ_BUSY_CYCLES | {mean['SQ_BUSY_CYCLES']:.4g} | {busy_se:.0f} per engine |",
+             f"| GRBM_GUI_ACTIVE | {mean['GRBM_GUI_ACTIVE']:.4g} | |",
+             f"| SQ_WAVES | {mean['SQ_WAVES']:.4g} | |", "",
+             f"MFMA busy / engine busy = {busy_simd / busy_se:.3f} (share of the kernel's busy cycles in which a "
+             f"SIMD's matrix pipe works).",
+             f"2MNK at the dense {PEAK_NAME[fmt]} rate needs {ideal:.0f} MFMA cycles per SIMD "
+             f"(counter: {busy_simd:.0f}, ratio {busy_simd / ideal:.3f})."]
+    if kb_avg:
+        lines.append(f"Engine busy cycles over the kernel-trace average ({kb_avg:.2f} us): "
+                     f"{busy_se / (kb_avg * 1e3):.2f} GHz.")
+    open(os.path.join(ROOT, "profiles", f"{short}_{key}_mfma.md"), "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
