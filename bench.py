@@ -696,8 +696,11 @@ def summarize_mfma(d, key, M, N, K, r, fmt, kb_names, kb_avg, cmd, short):
              f"2MNK at the dense {PEAK_NAME[fmt]} rate needs {ideal:.0f} MFMA cycles per SIMD "
              f"(counter: {busy_simd:.0f}, ratio {busy_simd / ideal:.3f})."]
     if kb_avg:
+        xcc = int(agent[0].get("Num_Xcc", 0) or 0)
         lines.append(f"Engine busy cycles over the kernel-trace average ({kb_avg:.2f} us): "
-                     f"{busy_se / (kb_avg * 1e3):.2f} GHz.")
+                     f"{busy_se / (kb_avg * 1e3):.2f} GHz" +
+                     (f"; GRBM_GUI_ACTIVE per XCD ({xcc}) over the same: "
+                      f"{mean['GRBM_GUI_ACTIVE'] / xcc / (kb_avg * 1e3):.2f} GHz." if xcc else "."))
     open(os.path.join(ROOT, "profiles", f"{short}_{key}_mfma.md"), "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
