@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define SVDQ_ABI_VERSION 2
+#define SVDQ_ABI_VERSION 3   /* 3: kernel code layout swizzle changed */
 #define SVDQ_MAX_RANK 128   /* msModelSlim doc, svd_res: rank not above 128 recommended */
 
 typedef enum svdq_status {
@@ -98,7 +98,7 @@ typedef struct svdq_sizes {
  * nibble k % 2):
  *   codes   1 KB units of 16 rows x one step, ordered [row / 16][step];
  *           16-byte slot 4 (row % 16) + q of a unit holds chunk
- *           q ^ (((r >> 1) ^ (r >> 3)) & 3) of the row-step, r = row % 32;
+ *           q ^ (((r >> 1) & 1) | ((r >> 2) & 2)) of the row-step, r = row;
  *           rows are padded to a multiple of 16
  *   scale records (MXFP4 weights and both formats' activations): 16 bytes
  *           per row and 4 steps, in 1 KB units of 64 rows ordered

@@ -339,12 +339,10 @@ __global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __res
 
 // ----------------------------------------------------------------- K-B
 
-// swizzled byte offset of 16-byte chunk c of row r inside a [rows][64 B] tile.
-// A fragment read has 16 consecutive rows at one chunk; with f(r) =
-// ((r >> 1) ^ (r >> 3)) & 3 any 8 consecutive rows hit 8 distinct 16-byte
-// slots of a 128-byte bank line and any 16 rows 16 slots of 256 bytes.
-__device__ __forceinline__ int swz_f(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
-__device__ __forceinline__ int swz(int r, int c) { return r * 64 + 16 * (c ^ swz_f(r)); }
+// swizzled byte offset of 16-byte chunk c of row r inside a [rows][64 B]
+// tile: the codes layout's XOR swizzle (chunk_swz, which makes the fragment
+// reads free of LDS bank conflicts)
+__device__ __forceinline__ int swz(int r, int c) { return r * 64 + 16 * (c ^ chunk_swz(r)); }
 
 // ----------------------------------------------------- K-B, MXFP4, large tile
 //
@@ -527,19 +525,28 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
   auto read_a = [&](uint32_t bo, int nt) __attribute__((always_inline)) -> v4i {
     return *reinterpret_cast<const v4i*>(lds + bo + aoff[nt]);
   };
-  // scale registers hold the E8M0 bytes of a pair of steps (tp, tp+1), tp
-  // even, in their low half: a 16-bit read from the group's dwords
+  // Scale registers: the lane's record dword holds the E8M0 bytes of the 4
+  // steps of a group; it is read at the group's first pair (tp % 4 == 0)
+  // and shifted down by 16 bits for its second, so that the bytes of steps
+  // (tp, tp+1) always sit in the low half and the MFMA's op_sel picks byte J.
   uint32_t asc[NTW], bsc[8];
   auto read_scales = [&](int tp) __attribute__((always_inline)) {
     if constexpr (W8) return;
-    uint32_t so = (uint32_t)(MX_NBUF * MX_STEP_BYTES + ((tp >> 2) & 1) * MX_SC_BYTES + 2 * ((tp >> 1) & 1));
+    if ((tp & 3) != 0) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) bsc[q] >>= 16;
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) asc[nt] >>= 16;
+      return;
+    }
+    uint32_t so = (uint32_t)(MX_NBUF * MX_STEP_BYTES + ((tp >> 2) & 1) * MX_SC_BYTES);
     asm volatile("" : "+s"(so));
     const uint8_t* sc = lds + so;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) bsc[q] = *reinterpret_cast<const uint16_t*>(sc + ((128 * wm + 16 * q + l16) * 4 + g) * 4);
+    for (int q = 0; q < 8; ++q) bsc[q] = *reinterpret_cast<const uint32_t*>(sc + ((128 * wm + 16 * q + l16) * 4 + g) * 4);
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt)
-      asc[nt] = *reinterpret_cast<const uint16_t*>(sc + ((MX_BM + 16 * NTW * wn + mx_nrow(nt, l16)) * 4 + g) * 4);
+      asc[nt] = *reinterpret_cast<const uint32_t*>(sc + ((MX_BM + 16 * NTW * wn + mx_nrow(nt, l16)) * 4 + g) * 4);
   };
   // The lane index is made opaque in these two so that their address
   // arithmetic is redone where they are called instead of being hoisted out

@@ -3,9 +3,8 @@
 // K is cut into steps of 128 elements (64 bytes of codes per row).  Codes
 // are stored in 1 KB units of 16 rows x one step, units ordered [row / 16]
 // [step], so every direct-to-LDS load moves one contiguous kilobyte.  Inside
-// a unit, 16-byte slot p = 4 (row % 16) + q holds chunk q ^ chunk_swz(row %
-// 32) of that row's 64 bytes: the XOR swizzle the GEMM kernels read LDS with
-// (rows modulo 32 because their tiles start at multiples of 32 rows).
+// a unit, 16-byte slot p = 4 (row % 16) + q holds chunk q ^ chunk_swz(row)
+// of that row's 64 bytes: the XOR swizzle the GEMM kernels read LDS with.
 //
 // Scale records (16 bytes per row and 4 steps) are stored in 1 KB units of
 // 64 rows, ordered [row / 64][4-step group].  INT4 weight scales are stored
@@ -25,7 +24,13 @@
 
 namespace svdq {
 
-SVDQ_HD inline int chunk_swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// chunk_swz(row) = row bit 1 + 2 x row bit 3.  A 16-byte LDS read of a wave
+// is served 16 lanes per cycle, lanes grouped by (lane bit 5, parity of lane
+// bits 2-4), and two lanes of a group conflict when their addresses agree in
+// bits 4-7; with this swizzle the GEMM kernels' fragment reads (16 rows at
+// one chunk, lanes 16 g + i reading row i, chunk g; consecutive rows or rows
+// 8 j + i, i < 4) give every group 16 distinct slots.
+SVDQ_HD inline int chunk_swz(int row) { return ((row >> 1) & 1) | ((row >> 2) & 2); }
 
 // byte b (0..63) of step t of row `row`
 SVDQ_HD inline size_t code_offset(int row, int t, int b, int steps) {

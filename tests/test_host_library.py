@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     lib = B.lib()
     for n in sorted(names):
         assert hasattr(lib, n), n
-    assert B.abi_version() == B.ABI_VERSION == 2
+    assert B.abi_version() == B.ABI_VERSION == 3
     assert B.status_str(0) == "ok"
 
 
@@ -220,9 +220,9 @@ def test_error_codes_device_entry_points_validate_before_hip():
 def _code_off(row, t, b, steps):
     """Codes layout as documented in svdq.h: 1 KB units of 16 rows x one
     step ordered [row / 16][step]; slot 4 (row % 16) + q holds chunk
-    q ^ swz(row % 32) of the row-step."""
+    q ^ swz(row) of the row-step, swz = row bit 1 + 2 x row bit 3."""
     r = row % 32
-    swz = ((r >> 1) ^ (r >> 3)) & 3
+    swz = ((r >> 1) & 1) | ((r >> 2) & 2)
     return ((row // 16) * steps + t) * 1024 + (4 * (row % 16) + ((b // 16) ^ swz)) * 16 + b % 16
 
 
