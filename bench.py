@@ -79,10 +79,11 @@ def kernel_source_hash():
     out, so a comment edit keeps counter measurements of the same code."""
     p = os.path.join(ROOT, "rank_gemm_svdq_amd", "csrc", "device_kernels.hip")
     lines = []
-    for line in open(p, encoding="utf-8"):
-        code = line.split("//", 1)[0].rstrip()
-        if code:
-            lines.append(code)
+    with open(p, encoding="utf-8") as fh:
+        for line in fh:
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                lines.append(code)
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
 
 
@@ -90,7 +91,8 @@ def measured_traffic(config):
     """HBM bytes per K-B launch from the committed rocprofv3 counter runs, if
     they were taken on the current kernel source; else None."""
     try:
-        t = json.load(open(TRAFFIC_FILE))
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
     except (OSError, ValueError):
         return None
     e = t.get(config)
@@ -541,6 +543,11 @@ def profile_commands(d, config):
     return {k: "rocprofv3 " + v.format(dir=d, config=config) for k, v in PROFILE_STEPS.items()}
 
 
+def _write(path, text):
+    with open(path, "w") as fh:
+        fh.write(text)
+
+
 def _csv(path):
     import csv
     with open(path, newline="") as f:
@@ -594,14 +601,15 @@ def summarize_profiles(d, config, fmt_override=None):
             kb_avg = avg
     bench_json = os.path.join(d, "stats.json")
     if os.path.exists(bench_json):
-        b = json.loads(open(bench_json).read().strip().splitlines()[-1])
+        with open(bench_json) as fh:
+            b = json.loads(fh.read().strip().splitlines()[-1])
         lines += ["", f"bench.py under the profiler: K-B median {b['kb_us']:.2f} us (HIP events on the launch "
                       f"stream), K-A median {b['ka']['us']:.2f} us, layer {b['value']:.0f} TOPS."]
     if kb_avg is not None:
         ops = main_ops(M, N, K)
         lines += [f"{kb_names[0]}: average {kb_avg:.2f} us -> {ops / (kb_avg * 1e-6) / 1e12:.0f} TOP/s of "
                   f"2MNK = {ops:.4g} ops per launch."]
-    open(os.path.join(ROOT, "profiles", f"{short}_{key}_kernel_stats.md"), "w").write("\n".join(lines) + "\n")
+    _write(os.path.join(ROOT, "profiles", f"{short}_{key}_kernel_stats.md"), "\n".join(lines) + "\n")
 
     # HBM traffic: FETCH_SIZE / WRITE_SIZE (KiB per dispatch), scaled by a
     # 256 MiB device copy measured in the same run
@@ -647,9 +655,10 @@ def summarize_profiles(d, config, fmt_override=None):
              f"({'n/a' if kb_traffic is None else f'{kb_traffic / kb_alg:.2f}x'}).",
              f"K-A scaled traffic {fmtb(ka_traffic)} against {fmtb(ka_alg)} algorithmic "
              f"({'n/a' if ka_traffic is None else f'{ka_traffic / ka_alg:.2f}x'})."]
-    open(os.path.join(ROOT, "profiles", f"{short}_{key}_traffic.md"), "w").write("\n".join(lines) + "\n")
+    _write(os.path.join(ROOT, "profiles", f"{short}_{key}_traffic.md"), "\n".join(lines) + "\n")
     try:
-        t = json.load(open(TRAFFIC_FILE))
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
     except (OSError, ValueError):
         t = {}
     t[key] = {"kernel": kb_names[0], "kernel_source_sha256_16": kernel_source_hash(),
@@ -701,7 +710,7 @@ def summarize_mfma(d, key, M, N, K, r, fmt, kb_names, kb_avg, cmd, short):
                      f"{busy_se / (kb_avg * 1e3):.2f} GHz" +
                      (f"; GRBM_GUI_ACTIVE per XCD ({xcc}) over the same: "
                       f"{mean['GRBM_GUI_ACTIVE'] / xcc / (kb_avg * 1e3):.2f} GHz." if xcc else "."))
-    open(os.path.join(ROOT, "profiles", f"{short}_{key}_mfma.md"), "w").write("\n".join(lines) + "\n")
+    _write(os.path.join(ROOT, "profiles", f"{short}_{key}_mfma.md"), "\n".join(lines) + "\n")
     print("\n".join(lines))
 
 

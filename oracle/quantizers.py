@@ -101,7 +101,7 @@ def quantize_w8(z):
     z = np.asarray(z, dtype=np.float32)
     amax = np.max(np.abs(z), axis=1)                        # fp32, exact
     s = (amax / np.float32(127.0)).astype(np.float32)       # fp32 division
-    with np.errstate(divide="ignore", invalid="ignore"):
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
         rcp = (np.float32(1.0) / s).astype(np.float32)
         y = (z * rcp[:, None]).astype(np.float32)           # fp32 product
         q = np.clip(np.rint(y), -127, 127)

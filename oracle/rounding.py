@@ -45,7 +45,8 @@ def round_f16(x32):
     Returns float64 values of the fp16 results.
     """
     x32 = np.asarray(x32, dtype=np.float32)
-    return x32.astype(np.float16).astype(np.float64)
+    with np.errstate(over="ignore"):                 # out-of-range values become +-inf
+        return x32.astype(np.float16).astype(np.float64)
 
 
 def bf16_bits(v):

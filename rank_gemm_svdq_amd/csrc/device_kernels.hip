@@ -437,7 +437,7 @@ __device__ __forceinline__ int mx_nrow(int nt, int q) {
 
 template <int NTR, bool ODD, int WAVES, bool W8 = false>
 __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
-    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const float* __restrict__ zp, int zsplit,
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const float* __restrict__ zp,
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws, const uint16_t* __restrict__ l2k,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int M, int N, int K, int rpad) {
   // LRF: the low-rank product Z L2' is formed first, while the first code
@@ -1229,15 +1229,15 @@ static void launch_kb_mx(const svdq_layer& L, const uint8_t* ws, const svdq_ws_l
   constexpr int WV = SVDQ_MX_WAVES;
   if constexpr (W8)
     hipLaunchKernelGGL((kb_mx_kernel<NTR, false, WV, true>), dim3(tiles), dim3(WV * 64), 0, st, ws + W.xq_off,
-                       ws + W.xs_off, reinterpret_cast<const float*>(ws + W.z_off), W.zsplit, L.wq, L.ws, L.l2k,
+                       ws + W.xs_off, reinterpret_cast<const float*>(ws + W.z_off), L.wq, L.ws, L.l2k,
                        L.bias, Y, M, L.N, L.K, rp);
   else if ((L.K / 128) % 2 == 0)
     hipLaunchKernelGGL((kb_mx_kernel<NTR, false, WV>), dim3(tiles), dim3(WV * 64), 0, st, ws + W.xq_off,
-                       ws + W.xs_off, reinterpret_cast<const float*>(ws + W.z_off), W.zsplit, L.wq, L.ws, L.l2k,
+                       ws + W.xs_off, reinterpret_cast<const float*>(ws + W.z_off), L.wq, L.ws, L.l2k,
                        L.bias, Y, M, L.N, L.K, rp);
   else
     hipLaunchKernelGGL((kb_mx_kernel<NTR, true, WV>), dim3(tiles), dim3(WV * 64), 0, st, ws + W.xq_off,
-                       ws + W.xs_off, reinterpret_cast<const float*>(ws + W.z_off), W.zsplit, L.wq, L.ws, L.l2k,
+                       ws + W.xs_off, reinterpret_cast<const float*>(ws + W.z_off), L.wq, L.ws, L.l2k,
                        L.bias, Y, M, L.N, L.K, rp);
 }
 

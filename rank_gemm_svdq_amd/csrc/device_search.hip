@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void sqdiff_kernel(const uint16_t* __restrict_
   red[threadIdx.x] = s;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
-    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
     __syncthreads();
   }
   if (threadIdx.x == 0) part[blockIdx.x] = red[0];

@@ -19,7 +19,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def test_library_exports_every_declared_symbol():
-    hdr = open(os.path.join(ROOT, "include", "svdq.h")).read()
+    with open(os.path.join(ROOT, "include", "svdq.h")) as f:
+        hdr = f.read()
     names = set(re.findall(r"\b(svdq_[a-z_0-9]+)\s*\(", hdr))
     assert len(names) >= 15
     lib = B.lib()

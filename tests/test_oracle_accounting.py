@@ -6,7 +6,8 @@ from oracle import accounting as A
 
 
 def test_eq11_eq12_printed_values(golden_dir):
-    fx = json.load(open(os.path.join(golden_dir, "accounting.json")))
+    with open(os.path.join(golden_dir, "accounting.json")) as f:
+        fx = json.load(f)
     e = fx["eq11"]
     assert abs(100 * A.rho_mac(e["m"], e["n"], e["r"]) - e["rho_mac_percent"]) < 1e-12
     e = fx["eq12"]
@@ -16,7 +17,8 @@ def test_eq11_eq12_printed_values(golden_dir):
 
 
 def test_table4_ratios(golden_dir):
-    fx = json.load(open(os.path.join(golden_dir, "accounting.json")))
+    with open(os.path.join(golden_dir, "accounting.json")) as f:
+        fx = json.load(f)
     t, r = fx["table4_ms"], fx["table4_ratios"]
     assert round(100 * (t["svdquant_unfused"] / t["naive_int4"] - 1), 1) == r["unfused_over_naive_percent"]
     assert round(100 * (t["svdquant_fused"] / t["naive_int4"] - 1), 1) == r["fused_over_naive_percent"]
