@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define SVDQ_ABI_VERSION 3   /* 3: kernel code layout swizzle changed */
+#define SVDQ_ABI_VERSION 4   /* 4: kernel code swizzle and scale-record order changed */
 #define SVDQ_MAX_RANK 128   /* msModelSlim doc, svd_res: rank not above 128 recommended */
 
 typedef enum svdq_status {
@@ -101,8 +101,11 @@ typedef struct svdq_sizes {
  *           q ^ (((r >> 1) & 1) | ((r >> 2) & 2)) of the row-step, r = row;
  *           rows are padded to a multiple of 16
  *   scale records (MXFP4 weights and both formats' activations): 16 bytes
- *           per row and 4 steps, in 1 KB units of 64 rows ordered
- *           [row / 64][4-step group], record bytes at (row % 64) * 16;
+ *           per row and 4 steps (4 dwords), in 1 KB units of 64 rows
+ *           ordered [row / 64][4-step group]; dword d of row r at unit
+ *           dword 64 (r % 64 / 16) + 16 d + r % 16; MXFP4 weight rows are
+ *           first permuted inside each 64-row block, row 32 p + 8 j + 4 h +
+ *           i (i, j < 4, h < 2) taking the place of row 16 (2 p + h) + 4 j + i;
  *           MXFP4: block b = 4t + g (32 elements) at record byte 4 g + t % 4;
  *           INT4: the fp16 scales of step t (groups 2t, 2t+1) at record
  *           bytes 4 (t % 4) and 4 (t % 4) + 2

@@ -542,11 +542,16 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
     uint32_t so = (uint32_t)(MX_NBUF * MX_STEP_BYTES + ((tp >> 2) & 1) * MX_SC_BYTES);
     asm volatile("" : "+s"(so));
     const uint8_t* sc = lds + so;
+    // 1 KB records of 64 rows: token fragment q is rows 16 (q % 4) .. of
+    // record 2 wm + q / 4; the weight records hold the wave's fragments in
+    // order (16 rows per tile nt); dword g of 16 rows = 256 contiguous bytes
 #pragma unroll
-    for (int q = 0; q < 8; ++q) bsc[q] = *reinterpret_cast<const uint32_t*>(sc + ((128 * wm + 16 * q + l16) * 4 + g) * 4);
+    for (int q = 0; q < 8; ++q)
+      bsc[q] = *reinterpret_cast<const uint32_t*>(sc + 1024 * (2 * wm + (q >> 2)) + 4 * (64 * (q & 3) + 16 * g + l16));
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt)
-      asc[nt] = *reinterpret_cast<const uint32_t*>(sc + ((MX_BM + 16 * NTW * wn + mx_nrow(nt, l16)) * 4 + g) * 4);
+      asc[nt] = *reinterpret_cast<const uint32_t*>(sc + 1024 * ((MX_BM + 16 * NTW * wn) / 64 + (nt >> 2)) +
+                                                   4 * (64 * (nt & 3) + 16 * g + l16));
   };
   // The lane index is made opaque in these two so that their address
   // arithmetic is redone where they are called instead of being hoisted out
@@ -1008,7 +1013,7 @@ __global__ __launch_bounds__(I4_THREADS, 1) void kb_i4_kernel(
     const uint8_t* sc = lds + so;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
-      sx[mt] = *reinterpret_cast<const uint32_t*>(sc + (64 * wm + 16 * mt + l16) * 16 + 4 * (t & 3));
+      sx[mt] = *reinterpret_cast<const uint32_t*>(sc + 1024 * wm + 4 * (64 * mt + 16 * (t & 3) + l16));
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const int blk = 16 * wn + 8 * (nt >> 1) + 2 * g + (nt & 1);

@@ -609,7 +609,7 @@ svdq_status svdq_kernel_layout(int32_t K, int32_t N, int32_t rank, int32_t fmt, 
     for (int32_t n = 0; n < N; ++n)
       for (int32_t b = 0; b < K / 32; ++b) {
         const int32_t t = b / 4, gq = b % 4;
-        ws_k[scale_record_offset(n, t / 4, 4 * gq + t % 4, g.ks4)] = ws[(size_t)n * (K / 32) + b];
+        ws_k[scale_record_offset(wrec_row(n), t / 4, 4 * gq + t % 4, g.ks4)] = ws[(size_t)n * (K / 32) + b];
       }
   } else {
     const uint16_t* s = reinterpret_cast<const uint16_t*>(ws);

@@ -39,9 +39,20 @@ SVDQ_HD inline size_t code_offset(int row, int t, int b, int steps) {
 }
 SVDQ_HD inline size_t code_bytes(int rows, int steps) { return (size_t)((rows + 15) / 16) * steps * 1024; }
 
-// byte j (0..15) of the scale record of row `row` for 4-step group q
+// byte j (0..15) of the scale record of row `row` for 4-step group q.  A
+// row's record is 4 dwords; dword d of row r sits at dword 64 (r % 64 / 16)
+// + 16 d + r % 16 of the 1 KB unit, so the GEMM's scale read (64 lanes:
+// 16 rows x dword g) covers 256 contiguous bytes.
 SVDQ_HD inline size_t scale_record_offset(int row, int q, int j, int ks4) {
-  return ((size_t)(row >> 6) * ks4 + q) * 1024 + (size_t)(row & 63) * 16 + j;
+  return ((size_t)(row >> 6) * ks4 + q) * 1024 +
+         (size_t)(64 * ((row & 63) >> 4) + 16 * (j >> 2) + (row & 15)) * 4 + (j & 3);
+}
+// MXFP4 weight scale records hold their rows in the order the GEMM's weight
+// fragments read them: inside each 64-row block, row 32 p + 8 j + 4 h + i
+// (i < 4, j < 4, h < 2) is stored as row 16 (2 p + h) + 4 j + i.
+SVDQ_HD inline int wrec_row(int row) {
+  const int r = row & 63;
+  return (row & ~63) | (16 * (2 * (r >> 5) + ((r >> 2) & 1)) + 4 * ((r >> 3) & 3) + (r & 3));
 }
 SVDQ_HD inline size_t scale_record_bytes(int rows, int ks4) { return (size_t)((rows + 63) / 64) * ks4 * 1024; }
 

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = B.lib()
     for n in sorted(names):
         assert hasattr(lib, n), n
-    assert B.abi_version() == B.ABI_VERSION == 3
+    assert B.abi_version() == B.ABI_VERSION == 4
     assert B.status_str(0) == "ok"
 
 
@@ -228,7 +228,18 @@ def _code_off(row, t, b, steps):
 
 
 def _rec_off(row, q, j, ks4):
-    return ((row // 64) * ks4 + q) * 1024 + (row % 64) * 16 + j
+    """Scale records as documented in svdq.h: dword d = j // 4 of row r at
+    unit dword 64 ((r % 64) // 16) + 16 d + r % 16."""
+    r = row % 64
+    return ((row // 64) * ks4 + q) * 1024 + (64 * (r // 16) + 16 * (j // 4) + r % 16) * 4 + j % 4
+
+
+def _wrec_row(row):
+    """MXFP4 weight records: row 32 p + 8 j + 4 h + i of a 64-row block stored
+    as row 16 (2 p + h) + 4 j + i."""
+    r = row % 64
+    p, j, h, i = r // 32, (r // 8) % 4, (r // 4) % 2, r % 4
+    return row - r + 16 * (2 * p + h) + 4 * j + i
 
 
 def test_workspace_layout_regions():
@@ -330,7 +341,7 @@ def test_mxfp4_scale_layout_positions():
     for n in range(N):
         for b in range(K // 32):
             t, g = divmod(b, 4)
-            i = _rec_off(n, t // 4, 4 * g + t % 4, ks4)
+            i = _rec_off(_wrec_row(n), t // 4, 4 * g + t % 4, ks4)
             assert row[i] == sc[n, b]
             seen[i] = True
     assert np.all(row[~seen] == 127)
