@@ -19,7 +19,8 @@
  *  - Plain pointers and sizes only.  "host" pointers are CPU memory,
  *    "device" pointers are HIP device memory on the current device.
  *  - The caller owns every buffer.  The library allocates no device memory
- *    and keeps no global mutable state; all entry points are re-entrant.
+ *    and keeps no global mutable state apart from a write-once per-device
+ *    record of the gfx950 check (atomic); all entry points are re-entrant.
  *  - Device calls are asynchronous on `stream` (a hipStream_t, NULL = the
  *    default stream) and never synchronize.  All arguments are validated on
  *    the host before any HIP call; a failed validation returns an error and
