@@ -900,8 +900,16 @@ constexpr int I4_Z0 = I4_SC0 + 2 * I4_SC_BYTES;       // Z chunk: 256 rows x 32 
 constexpr int I4_L20 = I4_Z0 + I4_BM * 128;           // L2' chunk: 128 rows x 32 bf16
 constexpr int I4_LDS = I4_L20 + I4_BN * 64;
 
-__device__ __forceinline__ float f16_half(uint32_t w, int hi) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)(hi ? (w >> 16) : (w & 0xFFFFu)));
+// product of the fp16 halves G of a and b, formed exactly in fp32 by one
+// mixed-precision FMA (the fp16 inputs are widened inside it, addend 0)
+template <int G>
+__device__ __forceinline__ float f16_product(uint32_t a, uint32_t b) {
+  float d;
+  if constexpr (G == 0)
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,1,0]" : "=v"(d) : "v"(a), "v"(b));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[1,1,0] op_sel_hi:[1,1,0]" : "=v"(d) : "v"(a), "v"(b));
+  return d;
 }
 
 // int8 MFMA operand of group G from a 16-byte INT4 fragment: bytes 16 q
@@ -1067,18 +1075,26 @@ __global__ __launch_bounds__(I4_THREADS, 1) void kb_i4_kernel(
     for (int mt = 0; mt < 4; ++mt) {
       wp[mt] = read_a(bn, mt);
       tk[(mt + 2) & 3] = mt + 2 < 4 ? read_b(bc, mt + 2) : read_b(bn, mt - 2);
+      // all 8 MFMAs of the group first, then their scaling, so that no
+      // result is read right after its MFMA
+      v4i I[2][4];
 #pragma unroll
       for (int G = 0; G < 2; ++G) {
         const v4i b8 = i4_unpack(tk[mt], G);
-        const float sxg = f16_half(sx[mt], G);
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const v4i I = __builtin_amdgcn_mfma_i32_16x16x64_i8(wu[nt][G], b8, (v4i){0, 0, 0, 0}, 0, 0, 0);
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[nt][mt][i] = __builtin_fmaf((float)I[i], sxg * f16_half((uint32_t)sw[nt][i], G), acc[nt][mt][i]);
-        }
+        for (int nt = 0; nt < 4; ++nt)
+          I[G][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wu[nt][G], b8, (v4i){0, 0, 0, 0}, 0, 0, 0);
       }
+#pragma unroll
+      for (int G = 0; G < 2; ++G)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p = G == 0 ? f16_product<0>(sx[mt], (uint32_t)sw[nt][i])
+                                   : f16_product<1>(sx[mt], (uint32_t)sw[nt][i]);
+            acc[nt][mt][i] = __builtin_fmaf((float)I[G][nt][i], p, acc[nt][mt][i]);
+          }
     }
   }
 #pragma unroll
