@@ -54,6 +54,8 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -237,16 +239,22 @@ __global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __res
 
     if constexpr (NT > 0) {
       // Z += (x^hi + x^lo) L1': MFMA s covers elements 32 g + 8 s .. + 8 of
-      // every lane group, i.e. k = 128 t + 32 (lane / 16) + 8 s + i
+      // every lane group, i.e. k = 128 t + 32 (lane / 16) + 8 s + i.
+      // hi = bf16_rne(x^) and lo = bf16_rne(x^ - hi) (the difference is
+      // exact in fp32), both converted two elements at a time; hi is widened
+      // back from its packed bits by a shift or a mask
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
-        v8bf hi, lo;
+        v4i hw, lw;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const __bf16 h = (__bf16)xh[8 * s4 + i];
-          hi[i] = h;
-          lo[i] = (__bf16)(xh[8 * s4 + i] - (float)h);
+        for (int i = 0; i < 4; ++i) {
+          const float x0 = xh[8 * s4 + 2 * i], x1 = xh[8 * s4 + 2 * i + 1];
+          const uint32_t hp = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){x0, x1}, v2bf));
+          const float r0 = x0 - __uint_as_float(hp << 16), r1 = x1 - __uint_as_float(hp & 0xFFFF0000u);
+          hw[i] = (int)hp;
+          lw[i] = (int)__builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){r0, r1}, v2bf));
         }
+        const v8bf hi = __builtin_bit_cast(v8bf, hw), lo = __builtin_bit_cast(v8bf, lw);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const v8bf b = WRING ? sl.w[WRING ? s4 * NT + nt : 0] : l1k[(((size_t)t * 4 + s4) * NT + nt) * 64 + lane];
