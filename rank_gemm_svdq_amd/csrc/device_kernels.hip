@@ -877,36 +877,39 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
   }
 }
 
-// ------------------------------------------------------ K-B, INT4, large tile
+// ------------------------------------------------------------ K-B, INT4
 //
-// 256 (tokens) x 128 (out-features) per block of 8 waves, two per SIMD; wave
-// w owns tokens 64 (w & 3) .. +64 and out-features 64 (w >> 2) .. +64, i.e.
-// 4 x 4 MFMA tiles of 16 x 16 (64 fp32 accumulators per lane).  Codes travel
-// global -> LDS by direct-to-LDS loads into a ring of four 24 KB step
-// buffers, three steps ahead; the scale records of 4 steps (token rows: one
-// dword per step; weights: 4 rows x one dword per step, 64 bytes per 4-row
-// block) are double buffered the same way.
+// 128 (tokens) x 128 (out-features) per block of 4 waves, three blocks per
+// compute unit, so each SIMD runs three waves of different blocks: one
+// block's barrier or load wait is covered by the others' VALU work, and
+// the tile count of a layer splits evenly over the compute units more
+// often than with larger tiles.  Wave w owns tokens 64 (w & 1) .. +64 and
+// out-features 64 (w >> 1) .. +64, i.e. 4 x 4 MFMA tiles of 16 x 16 (64
+// fp32 accumulators per lane).  Codes travel global -> LDS by direct-to-LDS
+// loads into a ring of two 16 KB step buffers, one step ahead; the scale
+// records of 4 steps (token rows: one dword per step; weights: 4 rows x one
+// dword per step, 64 bytes per 4-row block) are double buffered the same
+// way.
 //
 // Each 16-byte fragment holds 16 codes of each of the step's two 64-element
 // groups.  Nibbles become bytes 16 q, the int8 MFMA operand, so one MFMA per
 // group gives 2^8 times the exact integer dot product I; the accumulator
 // takes float(I) * (sx * sw), the fp16 scale product formed exactly in fp32,
-// and the 2^8 is removed once after the K loop.  The weight fragments of the
-// next step are read while the current ones (unpacked at the top of the
-// step) feed the MFMAs; token fragments stream two MFMA groups ahead.
+// and the 2^8 is removed once after the K loop.
 //
-// Chunk 0 of Z and L2' is fetched into its own LDS region at the start, so
-// the K loop carries no prefetch logic; weight rows are permuted inside tile
-// pairs as in the MXFP4 kernel for 16-byte stores.
+// After the K loop the two step buffers take the low-rank chunks (Z and
+// L2'); weight rows are permuted inside tile pairs as in the MXFP4 kernel
+// for 16-byte stores.
 
-constexpr int I4_BM = 256, I4_BN = 128, I4_THREADS = 512;
+constexpr int I4_BM = 128, I4_BN = 128, I4_WAVES = 4, I4_THREADS = 64 * I4_WAVES;
 constexpr int I4_STEP_BYTES = (I4_BM + I4_BN) * 64;   // codes of one step, both operands
-constexpr int I4_NBUF = 4;
+constexpr int I4_NBUF = 2;
 constexpr int I4_SC_BYTES = (I4_BM + I4_BN) * 16;     // scale records of one 4-step group
 constexpr int I4_SC0 = I4_NBUF * I4_STEP_BYTES;
-constexpr int I4_Z0 = I4_SC0 + 2 * I4_SC_BYTES;       // Z chunk: 256 rows x 32 fp32
-constexpr int I4_L20 = I4_Z0 + I4_BM * 128;           // L2' chunk: 128 rows x 32 bf16
-constexpr int I4_LDS = I4_L20 + I4_BN * 64;
+constexpr int I4_LDS = I4_SC0 + 2 * I4_SC_BYTES;
+// after the K loop the step buffers hold a low-rank chunk: Z (128 rows x 32
+// fp32) in buffer 0, L2' (128 rows x 32 bf16) in buffer 1
+constexpr int I4_Z0 = 0, I4_L20 = I4_STEP_BYTES;
 
 // product of the fp16 halves G of a and b, formed exactly in fp32 by one
 // mixed-precision FMA (the fp16 inputs are widened inside it, addend 0)
@@ -928,7 +931,7 @@ __device__ __forceinline__ v4i i4_unpack(const v4i f, int G) {
 }
 
 template <int NTR>
-__global__ __launch_bounds__(I4_THREADS, 1) void kb_i4_kernel(
+__global__ __launch_bounds__(I4_THREADS) __attribute__((amdgpu_waves_per_eu(3))) void kb_i4_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const float* __restrict__ zp,
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws, const uint16_t* __restrict__ l2k,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int M, int N, int K, int rpad) {
@@ -936,7 +939,7 @@ __global__ __launch_bounds__(I4_THREADS, 1) void kb_i4_kernel(
   const uint32_t lds_u32 = (uint32_t)(size_t)(SVDQ_AS3 uint8_t*)lds;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 3, wn = wave >> 2;
+  const int wm = wave & 1, wn = wave >> 1;
   const int l16 = lane & 15, g = lane >> 4;
   const int tiles_m = (M + I4_BM - 1) / I4_BM, tiles_n = (N + I4_BN - 1) / I4_BN;
   int tm, tn;
@@ -946,26 +949,24 @@ __global__ __launch_bounds__(I4_THREADS, 1) void kb_i4_kernel(
   const int ks4 = (steps + 3) / 4;
   const int m_base = tile_m + 64 * wm, n_base = tile_n + 64 * wn;
 
-  // ---- DMA plan.  Codes: 24 contiguous 1 KB units per step (codes layout;
-  // units 0-15: token row groups, 16-23: weight row groups); wave w moves
-  // units 3w .. 3w+2, lane i 16 bytes.  Units past the last row group
-  // repeat it (their outputs are never stored).
-  const uint8_t* cbase[3];
-  uint32_t coff[3];
+  // ---- DMA plan.  Codes: 16 contiguous 1 KB units per step (units 0-7:
+  // token row groups, 8-15: weight row groups); wave w moves units 4w ..
+  // 4w+3, lane i 16 bytes.  Units past the last row group repeat it.
+  const bool tokw = wave < 2;
+  const uint8_t* cbase = tokw ? xq : wq;
+  uint32_t coff[4];
 #pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    const int u = 3 * wave + j;
-    const bool tok = u < 16;
-    const int grp16 = tok ? min((tile_m >> 4) + u, (M + 15) / 16 - 1) : min((tile_n >> 4) + u - 16, N / 16 - 1);
-    cbase[j] = tok ? xq : wq;
+  for (int j = 0; j < 4; ++j) {
+    const int u = 4 * (wave & 1) + j;
+    const int grp16 = tokw ? min((tile_m >> 4) + u, (M + 15) / 16 - 1) : min((tile_n >> 4) + u, N / 16 - 1);
     coff[j] = (uint32_t)grp16 * (uint32_t)steps * 1024u + 16u * lane;
   }
-  // Scales of 4-step group grp: waves 0-3 move the 1 KB records of token
-  // rows 64 w .. (64 rows x 16 bytes), waves 4-5 the 2 KB weight-scale unit
-  // of the block's 128 out-features (32 blocks of 4 rows x 4 steps).
-  const uint8_t* sbase = wave < 4 ? xs : ws;
+  // Scales of 4-step group grp: waves 0-1 move the 1 KB records of token
+  // rows 64 w .., waves 2-3 the two halves of the 2 KB weight-scale unit of
+  // the block's 128 out-features (32 blocks of 4 rows x 4 steps).
+  const uint8_t* sbase = tokw ? xs : ws;
   uint32_t soff, sstride;
-  if (wave < 4) {
+  if (tokw) {
     soff = (uint32_t)min((tile_m >> 6) + wave, (M + 63) / 64 - 1) * (uint32_t)ks4 * 1024u + 16u * lane;
     sstride = 1024;
   } else {
@@ -973,17 +974,16 @@ __global__ __launch_bounds__(I4_THREADS, 1) void kb_i4_kernel(
     sstride = 2048;
   }
   auto issue_codes = [&](int t) __attribute__((always_inline)) {
-    const uint32_t b = lds_u32 + (uint32_t)(t % I4_NBUF) * I4_STEP_BYTES + (uint32_t)wave * 3072u;
+    const uint32_t b = lds_u32 + (uint32_t)(t % I4_NBUF) * I4_STEP_BYTES + (uint32_t)wave * 4096u;
 #pragma unroll
-    for (int j = 0; j < 3; ++j) dma16(cbase[j] + (size_t)t * 1024, coff[j], b + 1024u * j);
+    for (int j = 0; j < 4; ++j) dma16(cbase + (size_t)t * 1024, coff[j], b + 1024u * j);
   };
   auto issue_scales = [&](int grp) __attribute__((always_inline)) {
-    if (wave < 6)
-      dma16(sbase + (size_t)grp * sstride, soff,
-            lds_u32 + I4_SC0 + (uint32_t)(grp & 1) * I4_SC_BYTES + (uint32_t)wave * 1024u);
+    dma16(sbase + (size_t)grp * sstride, soff,
+          lds_u32 + I4_SC0 + (uint32_t)(grp & 1) * I4_SC_BYTES + (uint32_t)wave * 1024u);
   };
-  // Z (256 rows x 128 B, 32 units of 8 rows) and L2' (128 rows x 64 B, 8
-  // units of 16 rows) chunk u into their LDS regions
+  // Z (128 rows x 128 B, 16 units of 8 rows) and L2' (128 rows x 64 B, 8
+  // units of 16 rows) chunk u into step buffers 0 and 1
   auto issue_lowrank = [&](int u) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -993,11 +993,14 @@ __global__ __launch_bounds__(I4_THREADS, 1) void kb_i4_kernel(
             ((uint32_t)m * (uint32_t)rpad + 32u * u) * 4u + 16u * ((lane & 7) ^ zswz(row)),
             lds_u32 + I4_Z0 + 1024u * unit);
     }
-    const int row = 16 * wave + (lane >> 2);
-    const int n = min(tile_n + row, N - 1);
-    dma16(reinterpret_cast<const uint8_t*>(l2k),
-          ((uint32_t)n * (uint32_t)rpad + 32u * u) * 2u + 16u * ((lane & 3) ^ lswz(row)),
-          lds_u32 + I4_L20 + 1024u * wave);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int unit = 2 * wave + j, row = 16 * unit + (lane >> 2);
+      const int n = min(tile_n + row, N - 1);
+      dma16(reinterpret_cast<const uint8_t*>(l2k),
+            ((uint32_t)n * (uint32_t)rpad + 32u * u) * 2u + 16u * ((lane & 3) ^ lswz(row)),
+            lds_u32 + I4_L20 + 1024u * unit);
+    }
   };
 
   // fragment addresses inside a step buffer: token fragment q reads row
@@ -1036,19 +1039,13 @@ __global__ __launch_bounds__(I4_THREADS, 1) void kb_i4_kernel(
       sw[nt] = *reinterpret_cast<const v4i*>(sc + I4_BM * 16 + blk * 64 + 16 * (t & 3));
     }
   };
-  auto wait_for = [&](int s) __attribute__((always_inline)) {
-    if (s + 1 < steps)
-      asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  };
 
-  if constexpr (NTR > 0) issue_lowrank(0);
+  // Ring of two step buffers: the top of step t waits for step t's loads
+  // and a barrier, after which step t-1's buffer (every wave is past it)
+  // receives step t+1; steps 0 and 1 are issued before the loop.
   issue_scales(0);
-#pragma unroll
-  for (int s0 = 0; s0 < 3; ++s0)
-    if (s0 < steps) issue_codes(s0);
+  issue_codes(0);
+  if (steps > 1) issue_codes(1);
 
   v4f acc[4][4];   // [weight tile][token tile]
 #pragma unroll
@@ -1056,53 +1053,44 @@ __global__ __launch_bounds__(I4_THREADS, 1) void kb_i4_kernel(
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) acc[nt][mt] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  v4i wp[4];   // packed weight fragments (the next step's, once read)
-  v4i tk[4];   // packed token fragments; fragment q sits in slot q
-  wait_for(0);
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) wp[nt] = read_a(0, nt);
-#pragma unroll
-  for (int q = 0; q < 2; ++q) tk[q] = read_b(0, q);
-
   for (int t = 0; t < steps; ++t) {
-    // the barrier publishes step t+1's buffer; the buffer of step t-1 (all
-    // waves are past it) receives step t+3.  The last step also reads the
-    // next buffer; those reads stay inside LDS and are never used.
-    wait_for(t + 1);
+    if (t == 0 && steps > 1)
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t >= 1 && t + 1 < steps) issue_codes(t + 1);
     if ((t & 3) == 0 && (t >> 2) + 1 < ks4) issue_scales((t >> 2) + 1);
-    if (t + 3 < steps) issue_codes(t + 3);
     read_scales(t);
-    const uint32_t bc = buf_of(t), bn = buf_of(t + 1);
-    v4i wu[4][2];
+    const uint32_t bc = buf_of(t);
+    v4i wu[4][2], tk[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      wu[nt][0] = i4_unpack(wp[nt], 0);
-      wu[nt][1] = i4_unpack(wp[nt], 1);
+      const v4i wp = read_a(bc, nt);
+      wu[nt][0] = i4_unpack(wp, 0);
+      wu[nt][1] = i4_unpack(wp, 1);
     }
 #pragma unroll
+    for (int q = 0; q < 4; ++q) tk[q] = read_b(bc, q);
+#pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      wp[mt] = read_a(bn, mt);
-      tk[(mt + 2) & 3] = mt + 2 < 4 ? read_b(bc, mt + 2) : read_b(bn, mt - 2);
-      // all 8 MFMAs of the group first, then their scaling, so that no
-      // result is read right after its MFMA
-      v4i I[2][4];
 #pragma unroll
       for (int G = 0; G < 2; ++G) {
+        // the group's 4 MFMAs first, then their scaling
         const v4i b8 = i4_unpack(tk[mt], G);
+        v4i I[4];
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
-          I[G][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wu[nt][G], b8, (v4i){0, 0, 0, 0}, 0, 0, 0);
-      }
-#pragma unroll
-      for (int G = 0; G < 2; ++G)
+          I[nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wu[nt][G], b8, (v4i){0, 0, 0, 0}, 0, 0, 0);
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float p = G == 0 ? f16_product<0>(sx[mt], (uint32_t)sw[nt][i])
                                    : f16_product<1>(sx[mt], (uint32_t)sw[nt][i]);
-            acc[nt][mt][i] = __builtin_fmaf((float)I[G][nt][i], p, acc[nt][mt][i]);
+            acc[nt][mt][i] = __builtin_fmaf((float)I[nt][i], p, acc[nt][mt][i]);
           }
+      }
     }
   }
 #pragma unroll
@@ -1115,10 +1103,8 @@ __global__ __launch_bounds__(I4_THREADS, 1) void kb_i4_kernel(
   // ---- low-rank up projection and bias, then one 16-byte store per pair
   if constexpr (NTR > 0) {
     for (int u = 0; u < NTR; ++u) {
-      if (u > 0) {
-        __syncthreads();   // every wave is done with chunk u-1
-        issue_lowrank(u);
-      }
+      __syncthreads();   // every wave is done with the step buffers (or chunk u-1)
+      issue_lowrank(u);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       v8bf bh[4], bl[4];
