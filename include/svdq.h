@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define SVDQ_ABI_VERSION 4   /* 4: kernel code swizzle and scale-record order changed */
+#define SVDQ_ABI_VERSION 5   /* 5: the down factor's kernel layout holds rank / 16 column tiles */
 #define SVDQ_MAX_RANK 128   /* msModelSlim doc, svd_res: rank not above 128 recommended */
 
 typedef enum svdq_status {
@@ -278,8 +278,8 @@ svdq_status svdq_attach_lora(const float* lambda, const uint16_t* l1, const uint
 /* Canonical host buffers -> kernel-layout host buffers (sizes from
  * svdq_layer_sizes).  l1 may be NULL when rank == 0.  The down factor L1'
  * (bf16) is stored in the order of the quantize kernel's MFMA operand,
- * [step][s 0..3][16-column tile][lane 0..63][i 0..7] holding
- * L1'[128 step + 32 (lane / 16) + 8 s + i][16 tile + lane % 16] (0 past rank);
+ * [step][s 0..3][16-column tile 0..rank/16-1][lane 0..63][i 0..7] holding
+ * L1'[128 step + 32 (lane / 16) + 8 s + i][16 tile + lane % 16];
  * the up factor as L2'^T [N][rank rounded up to 32] (0 past rank). */
 svdq_status svdq_kernel_layout(int32_t K, int32_t N, int32_t rank, int32_t fmt,
                                const float* smooth_inv, const uint8_t* wq, const uint8_t* ws,

@@ -99,7 +99,7 @@ class SearchResult(C.Structure):
 
 
 _lib = None
-ABI_VERSION = 4   # SVDQ_ABI_VERSION of include/svdq.h that these structures mirror
+ABI_VERSION = 5   # SVDQ_ABI_VERSION of include/svdq.h that these structures mirror
 
 
 def lib():

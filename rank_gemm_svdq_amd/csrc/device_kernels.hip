@@ -26,15 +26,17 @@
 //     element k (G = k / 64, g = k % 64 / 16, j = k % 16) at byte
 //     16 g + 8 G + j / 2, nibble j % 2, so the 16 bytes of lane group g
 //     hold 16 elements of each of the step's two 64-element groups.
-//   Scale records (MXFP4 both operands, INT4 activations): 16 bytes per row
-//     and 4 steps, 1 KB units of 64 rows ordered [row / 64][4-step group];
-//     MXFP4 block 4 t + q at record byte 4 q + t % 4, INT4 the fp16 pair of
-//     step t at bytes 4 (t % 4) and + 2.
+//   Scale records (MXFP4 both operands, INT4 activations): 1 KB units of 64
+//     rows x 4 steps ordered [row / 64][4-step group]; dword d of row r sits
+//     at unit dword 64 (r % 64 / 16) + 16 d + r % 16.  MXFP4: dword d holds
+//     the E8M0 scales of 32-element block d of the 4 steps (byte t % 4), the
+//     weight rows permuted inside their 64-row group (wrec_row); INT4: dword
+//     t % 4 is the fp16 pair of step t.
 //   INT4 weight scales: 2 KB units of 128 rows x 4 steps, [4-row block]
 //     [step % 4][row % 4][group of 64] fp16.
 //   W8A8 scales: fp32 per token row (workspace) and per out-feature (layer).
-//   Down factor: L1' (bf16), ordered [step][s][n-tile][lane][8] with
-//     k = 128 step + 32 (lane/16) + 8 s + i, n = 16 n-tile + lane % 16.
+//   Down factor: L1' (bf16), ordered [step][s][n-tile < rank/16][lane][8]
+//     with k = 128 step + 32 (lane/16) + 8 s + i, n = 16 n-tile + lane % 16.
 //   Up factor: L2'^T, [N][rpad] bf16, rpad = rank rounded up to 32.
 //   Z (down projection): per row and 32-column chunk, 32 bf16 hi values then
 //     32 bf16 lo values (hi + lo = Z to about 2^-17), rpad * 4 bytes per row.
@@ -281,17 +283,22 @@ __global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __res
 #pragma unroll
       for (int i = 0; i < 4; ++i) zred[(wave * 16 + 4 * g + i) * W + 16 * nt + r] = acc[nt][i];
     __syncthreads();
-    for (int idx = threadIdx.x; idx < 16 * W; idx += 64 * KA_WAVES) {
-      const int rr = idx / W, cc = idx % W;
+    // columns from the rank up to WP = rpad (the rank rounded up to 32) are
+    // written as 0
+    constexpr int WP = (W + 31) / 32 * 32;
+    for (int idx = threadIdx.x; idx < 16 * WP; idx += 64 * KA_WAVES) {
+      const int rr = idx / WP, cc = idx % WP;
       float sum = 0.f;
+      if (cc < W) {
 #pragma unroll
-      for (int w = 0; w < KA_WAVES; ++w) sum += zred[(w * 16 + rr) * W + cc];
+        for (int w = 0; w < KA_WAVES; ++w) sum += zred[(w * 16 + rr) * W + cc];
+      }
       // Z leaves as the bf16 pair hi + lo the up projection multiplies with:
       // per row and 32-column chunk, 32 hi values then 32 lo values
       if (row0 + rr < M) {
         const __bf16 hi = (__bf16)sum;
         const __bf16 lo = (__bf16)(sum - (float)hi);
-        uint16_t* zr = reinterpret_cast<uint16_t*>(zout) + (size_t)(row0 + rr) * 2 * rpad + 64 * (cc >> 5) + (cc & 31);
+        uint16_t* zr = reinterpret_cast<uint16_t*>(zout) + (size_t)(row0 + rr) * 2 * WP + 64 * (cc >> 5) + (cc & 31);
         zr[0] = __builtin_bit_cast(uint16_t, hi);
         zr[32] = __builtin_bit_cast(uint16_t, lo);
       }
@@ -1222,11 +1229,16 @@ static hipError_t launch_ka(const svdq_layer& L, const uint16_t* X, int M, uint8
       hipLaunchKernelGGL((ka_kernel<FMT, NTV, false, ZONLY>), grid, block, 0, st, X, M, L.K, L.smooth_inv, l1, xq, xs, \
                          z, rp);                                                                            \
   } while (0)
-  switch (rp / 16) {
+  // one 16-column MFMA tile of the down factor per 16 of the rank
+  switch (L.rank / 16) {
     case 0: SVDQ_KA(0); break;
+    case 1: SVDQ_KA(1); break;
     case 2: SVDQ_KA(2); break;
+    case 3: SVDQ_KA(3); break;
     case 4: SVDQ_KA(4); break;
+    case 5: SVDQ_KA(5); break;
     case 6: SVDQ_KA(6); break;
+    case 7: SVDQ_KA(7); break;
     case 8: SVDQ_KA(8); break;
     default: return hipErrorInvalidValue;
   }

@@ -38,7 +38,7 @@ bool geometry(int32_t K, int32_t N, int32_t rank, int32_t fmt, Geometry* g) {
   g->ws_bytes = fmt == SVDQ_INT4_G64   ? int4_wscale_bytes(N, g->ks4)
                 : fmt == SVDQ_MXFP4_G32 ? scale_record_bytes(N, g->ks4)
                                         : (size_t)N * 4;
-  g->l1k_bytes = (size_t)K * g->rpad * 2;
+  g->l1k_bytes = (size_t)K * rank * 2;
   g->l2k_bytes = (size_t)N * g->rpad * 2;
   return true;
 }
@@ -624,7 +624,7 @@ svdq_status svdq_kernel_layout(int32_t K, int32_t N, int32_t rank, int32_t fmt, 
   // down factor: L1' (bf16) in the order of K-A's MFMA B operand,
   // [step][s 0..3][n-tile][lane 0..63][i 0..7] with
   // k = 128 step + 32 (lane / 16) + 8 s + i and n = 16 tile + lane % 16
-  const int32_t ntile = rp / 16;
+  const int32_t ntile = rank / 16;
   parallel_for(steps, default_threads(0), [&](int64_t lo, int64_t hi) {
     for (int64_t t = lo; t < hi; ++t)
       for (int s = 0; s < 4; ++s)
@@ -634,7 +634,7 @@ svdq_status svdq_kernel_layout(int32_t K, int32_t N, int32_t rank, int32_t fmt, 
               const int32_t k = (int32_t)t * kStep + 32 * (lane / 16) + 8 * s + i;
               const int32_t n = 16 * nt + lane % 16;
               const size_t idx = (((((size_t)t * 4 + s) * ntile + nt) * 64 + lane) * 8) + i;
-              l1k[idx] = n < rank ? l1[(size_t)k * rank + n] : (uint16_t)0;
+              l1k[idx] = l1[(size_t)k * rank + n];
             }
   });
   // up factor: L2'^T padded to rpad columns

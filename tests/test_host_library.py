@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = B.lib()
     for n in sorted(names):
         assert hasattr(lib, n), n
-    assert B.abi_version() == B.ABI_VERSION == 4
+    assert B.abi_version() == B.ABI_VERSION == 5
     assert B.status_str(0) == "ok"
 
 
@@ -290,6 +290,33 @@ def test_int4_kernel_layout_positions():
                 assert ws[i] == sc[n, 2 * t + G]
                 seen[i] = True
     assert np.all(ws[~seen] == 0)
+
+
+def test_lowrank_factor_layout_positions():
+    """Down factor: [step][s][16-column tile < rank/16][lane][i] holding
+    L1'[128 step + 32 (lane / 16) + 8 s + i][16 tile + lane % 16]; up factor:
+    L2'^T [N][rank rounded up to 32], zero past the rank."""
+    K, N = 256, 48
+    rng = np.random.default_rng(5)
+    for rank in (16, 48, 64):
+        l1 = rng.integers(1, 0x7F00, (K, rank)).astype(np.uint16)
+        l2 = rng.integers(1, 0x7F00, (rank, N)).astype(np.uint16)
+        prep = {"K": K, "N": N, "rank": rank, "fmt": 1, "smooth_inv": np.ones(K, np.float32),
+                "wq": np.zeros((N, K // 2), np.uint8), "ws": np.full((N, K // 32), 127, np.uint8),
+                "l1": l1, "l2": l2}
+        assert B.layer_sizes(K, N, rank, 1)["l1k_bytes"] == K * rank * 2
+        kl = B.kernel_layout(prep)
+        l1k, nt = kl["l1k"][:K * rank].reshape(K // 128, 4, rank // 16, 64, 8), rank // 16
+        for t in range(K // 128):
+            for s4 in range(4):
+                for tile in range(nt):
+                    for lane in range(0, 64, 5):
+                        for i in range(8):
+                            k = 128 * t + 32 * (lane // 16) + 8 * s4 + i
+                            assert l1k[t, s4, tile, lane, i] == l1[k, 16 * tile + lane % 16]
+        rp = (rank + 31) // 32 * 32
+        l2k = kl["l2k"][:N * rp].reshape(N, rp)
+        assert np.array_equal(l2k[:, :rank], l2.T) and np.all(l2k[:, rank:] == 0)
 
 
 def test_mxfp4_code_layout_positions():
