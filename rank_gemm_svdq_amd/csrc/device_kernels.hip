@@ -84,14 +84,16 @@ constexpr int KA_SL_MAX_K = 16384;   // 1/lambda is staged in LDS up to this K
 // smoothed x^ = x / lambda, split into bf16 hi + lo, by the bf16 factor
 // L1', so it runs on bf16 MFMA with fp32 accumulation.  ZONLY drops the
 // quantisation (the unfused baseline's separate down-projection pass).
-template <int FMT, int NT, bool SL, bool ZONLY = false>
+template <int FMT, int NT, bool SL, bool ZONLY = false, bool RING = true>
 __global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __restrict__ X, int M, int K,
                                                           const float* __restrict__ sinv,
                                                           const v8bf* __restrict__ l1k,
                                                           uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
                                                           float* __restrict__ zout, int rpad) {
   constexpr int NTZ = NT > 0 ? NT : 1;
-  constexpr bool WRING = NT > 0 && NT <= (SL ? 4 : 2);   // down-factor fragments in the ring
+  // down-factor fragments in the ring (RING: chosen when one block per
+  // compute unit runs; without them the kernel fits two blocks per unit)
+  constexpr bool WRING = RING && NT > 0 && NT <= (SL ? 4 : 2);
   constexpr int NW = WRING ? 4 * NT : 1;
   constexpr bool W8 = FMT == SVDQ_W8A8 && !ZONLY;
   __shared__ float zred[NT > 0 ? KA_WAVES * 16 * NT * 16 : 1];
@@ -1211,6 +1213,27 @@ __global__ __launch_bounds__(256) void kup_kernel(const uint16_t* __restrict__ z
 
 // ------------------------------------------------------------ dispatch
 
+// compute units of the current device, cached per device (write-once)
+static std::atomic<int> g_dev_cus[64];
+
+static int device_cus() {
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  v = g_dev_cus[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    g_dev_cus[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+template <int FMT, int NT, bool SL, bool ZONLY, bool RING>
+static void launch_ka_one(dim3 grid, dim3 block, size_t lds, hipStream_t st, const uint16_t* X, int M,
+                          const svdq_layer& L, const v8bf* l1, uint8_t* xq, uint8_t* xs, float* z, int rp) {
+  hipLaunchKernelGGL((ka_kernel<FMT, NT, SL, ZONLY, RING>), grid, block, lds, st, X, M, L.K, L.smooth_inv, l1, xq,
+                     xs, z, rp);
+}
+
 template <int FMT, bool ZONLY = false>
 static hipError_t launch_ka(const svdq_layer& L, const uint16_t* X, int M, uint8_t* ws, const svdq_ws_layout& W,
                             hipStream_t st) {
@@ -1220,14 +1243,31 @@ static hipError_t launch_ka(const svdq_layer& L, const uint16_t* X, int M, uint8
   uint8_t* xs = ws + W.xs_off;
   float* z = reinterpret_cast<float*>(ws + W.z_off);
   const v8bf* l1 = reinterpret_cast<const v8bf*>(L.l1k);
-#define SVDQ_KA(NTV)                                                                                        \
-  do {                                                                                                      \
-    if (L.K <= KA_SL_MAX_K)                                                                                 \
-      hipLaunchKernelGGL((ka_kernel<FMT, NTV, true, ZONLY>), grid, block, (size_t)L.K * 4, st, X, M, L.K, L.smooth_inv, \
-                         l1, xq, xs, z, rp);                                                                \
-    else                                                                                                    \
-      hipLaunchKernelGGL((ka_kernel<FMT, NTV, false, ZONLY>), grid, block, 0, st, X, M, L.K, L.smooth_inv, l1, xq, xs, \
-                         z, rp);                                                                            \
+  // With at most one block per compute unit the register ring of down-factor
+  // fragments hides their L2 latency; with more blocks than units the
+  // ring-free kernel (about 110 VGPRs) runs two blocks per unit, which
+  // hides it better.
+  const bool ring = (int)grid.x <= device_cus();
+#define SVDQ_KA(NTV)                                                                                      \
+  do {                                                                                                    \
+    if (L.K <= KA_SL_MAX_K) {                                                                             \
+      const size_t lds = (size_t)L.K * 4;                                                                 \
+      if constexpr (NTV > 0 && NTV <= 4) {                                                                \
+        if (!ring) {                                                                                      \
+          launch_ka_one<FMT, NTV, true, ZONLY, false>(grid, block, lds, st, X, M, L, l1, xq, xs, z, rp);  \
+          break;                                                                                          \
+        }                                                                                                 \
+      }                                                                                                   \
+      launch_ka_one<FMT, NTV, true, ZONLY, true>(grid, block, lds, st, X, M, L, l1, xq, xs, z, rp);       \
+    } else {                                                                                              \
+      if constexpr (NTV > 0 && NTV <= 2) {                                                                \
+        if (!ring) {                                                                                      \
+          launch_ka_one<FMT, NTV, false, ZONLY, false>(grid, block, 0, st, X, M, L, l1, xq, xs, z, rp);   \
+          break;                                                                                          \
+        }                                                                                                 \
+      }                                                                                                   \
+      launch_ka_one<FMT, NTV, false, ZONLY, true>(grid, block, 0, st, X, M, L, l1, xq, xs, z, rp);        \
+    }                                                                                                     \
   } while (0)
   // one 16-column MFMA tile of the down factor per 16 of the rank
   switch (L.rank / 16) {

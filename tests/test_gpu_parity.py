@@ -50,6 +50,7 @@ def test_tiny_layer(fmt, use_bias):
     (96, 640, 320, 32), (40, 1152, 272, 64), (33, 384, 160, 16),   # odd numbers of 128-wide K steps
     (70, 640, 384, 96), (257, 512, 400, 128),                      # ranks 96 and 128 (the maximum)
     (50, 512, 160, 80), (70, 384, 144, 112),                       # ranks 80 and 112 (odd 16-column tiles)
+    (4200, 256, 160, 48),                                          # more 16-row blocks than compute units
     (40, 16512, 64, 16),                                           # K above 16384: 1/lambda not staged in LDS
 ])
 def test_shapes_and_tails(fmt, M, K, N, rank):
