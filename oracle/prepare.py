@@ -29,8 +29,11 @@ O6 weight packing: the quantizer of the chosen format applied to R32^T
    ([N, K], grouped along K).
 
 O-RI residual iterations (AutoRound doc, "Residual iteration"): refit the
-   branch to W~ - Q(R_prev), keep the candidate with the smallest
-   ||W~ - L1b L2b - Q(R)||_F, optionally stop at the first worse one.
+   branch to W~ - Q(R_prev), keep the candidate with the smallest score,
+   optionally stop at the first worse one.  The doc scores candidates by
+   the weight reconstruction error ||W~ - L1b L2b - Q(R)||_F when smooth
+   search is off and by the calibration output error when it is on; the
+   second is passed in by the smooth search (oracle.search) as `score`.
 
 Pins (tests/test_oracle_prepare.py): Eq. (3) smoothing invariance (bit
 identical for power-of-two lambda), Eckart-Young tail energy, R = 0 at full
@@ -93,19 +96,22 @@ def _candidate(wt, target, rank, fmt):
     return {"l1": l1, "l2": l2, "sigma": sig, "l1b": l1b, "l2b": l2b, "r": r, "r32": r32, "q": q, "err": err}
 
 
-def residual_iterations(wt, rank, fmt, iters=1, early_stop=False, keep_all=False):
+def residual_iterations(wt, rank, fmt, iters=1, early_stop=False, keep_all=False, score=None):
     """Residual iteration (AutoRound doc, "Residual iteration"; Zhou notes
     sec. 5, the alternating update of the protected branch).
 
     Iteration 1 fits the rank-r branch to W~ itself.  Every further
     iteration fits it to W~ - Q(R_prev), Q the deployment RTN
     quantize-dequantize of the previous residual, then takes the new
-    residual R = W~ - L1b L2b.  A candidate's error is the weight
-    reconstruction error ||W~ - L1b L2b - Q(R)||_F (smoothed coordinates;
-    the pages use it when no calibration output is scored).  The candidate
-    with the smallest error is kept; with early_stop the loop ends at the
-    first iteration whose error is larger than the best so far.
-    Returns (best candidate, list of errors per iteration run, all
+    residual R = W~ - L1b L2b.  A candidate's score is score(candidate)
+    when a scoring function is given (the smooth search passes the
+    calibration output error), else its weight reconstruction error
+    ||W~ - L1b L2b - Q(R)||_F in smoothed coordinates (the doc's objective
+    without smooth search).  The candidate with the smallest score is kept
+    (the earlier on ties; a non-finite score never displaces a finite one);
+    with early_stop the loop ends at the first iteration whose score is
+    larger than the best so far.
+    Returns (best candidate, list of scores per iteration run, all
     candidates if keep_all).
     """
     cands, errors = [], []
@@ -114,30 +120,46 @@ def residual_iterations(wt, rank, fmt, iters=1, early_stop=False, keep_all=False
     for it in range(max(1, int(iters))):
         c = _candidate(wt, target, rank, fmt)
         c["iteration"] = it
-        errors.append(c["err"])
+        c["score"] = c["err"] if score is None else float(score(c))
+        errors.append(c["score"])
         if keep_all:
             cands.append(c)
-        if best is None or c["err"] < best["err"]:
+        if (best is None or c["score"] < best["score"]
+                or (not np.isfinite(best["score"]) and np.isfinite(c["score"]))):
             best = c
-        elif early_stop and c["err"] > best["err"]:
+        elif early_stop and c["score"] > best["score"]:
             break
         target = wt - c["q"]["deq"].T
     return best, errors, cands
 
 
-def prepare(w, act_amax, alpha, rank, fmt, lora=None, residual_iters=1, early_stop=False, beta=None):
+def candidate_layer(c, lam32, inv, fmt, rank, lora=None):
+    """The deployable layer (the dict oracle.forward reads) of one residual
+    iteration candidate."""
+    l1p, l2p = c["l1b"], c["l2b"]
+    if lora is not None:
+        l1p, l2p = attach_lora(l1p, l2p, lam32, lora["A"], lora["B"], lora.get("strength", 1.0))
+    return {"fmt": fmt, "rank": rank, "lam32": lam32, "inv_lambda": inv, "l1p": l1p, "l2p": l2p,
+            "wq_packed": c["q"]["packed"], "ws": c["q"]["scales"]}
+
+
+def prepare(w, act_amax, alpha, rank, fmt, lora=None, residual_iters=1, early_stop=False, beta=None,
+            score=None):
     """Prepare one layer.
 
     w: [K, N] weight values, act_amax: [K], alpha in [0, 1], rank r >= 0,
     fmt 'int4' | 'mxfp4', lora: optional dict(A=[K, k], B=[k, N], strength=s),
     residual_iters / early_stop: see residual_iterations (1 = one SVD),
-    beta: weight exponent of lambda (None: 1 - alpha).
+    beta: weight exponent of lambda (None: 1 - alpha), score: optional
+    function of a candidate's deployable layer (candidate_layer) that
+    scores residual iterations in place of the weight error.
     Returns a dict of every intermediate the pins and the forward need.
     """
     w = np.asarray(w, dtype=np.float64)
     lam32, inv = smoothing_factors(act_amax, w, alpha, beta)
     wt = smooth_weight(w, lam32)
-    c, errors, _ = residual_iterations(wt, rank, fmt, residual_iters, early_stop)
+    sc = None if score is None else (lambda c: score(candidate_layer(c, lam32, inv, fmt, rank, lora)))
+    c, errors, _ = residual_iterations(wt, rank, fmt, residual_iters, early_stop, score=sc)
     l1, l2, sig = c["l1"], c["l2"], c["sigma"]
     l1b, l2b = c["l1b"], c["l2b"]
     r_exact = wt - l1 @ l2

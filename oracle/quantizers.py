@@ -10,10 +10,15 @@ scale).  Per group of 64 values z (fp32):
     amax = max |z|
     s32  = fp32(amax / 7)                      (IEEE fp32 division)
     s16  = fp16(s32)                           (the stored 16-bit scale)
+    if s16 overflowed to +inf (s32 >= 65520): s16 = 65504, the largest
+           finite fp16 value, and the clamp below saturates the codes
     if s16 == 0: every code is 0
     else: rcp = fp32(1 / s16); q = clamp(rint(fp32(z * rcp)), -7, 7)
 Codes run -7..7 (the notes: symmetric coding, the extra negative code is
-not used).  The scale is rounded to fp16 before quantizing, so decoding is
+not used).  Eq. (1) assumes a scale the 16-bit format can hold; for a group
+whose amax / 7 lies beyond the fp16 range the reading taken is a saturated
+scale: s16 = 65504 and every |z| / s16 above 7.5 takes code +-7 (clipping,
+the only way a finite group stays finite under a 16-bit scale).  The scale is rounded to fp16 before quantizing, so decoding is
 exactly q * s16.  Dividing by the scale is done as one correctly rounded
 reciprocal per group and a multiply per element; this is the reading taken
 where Eq. (1) writes Z / s.
@@ -49,7 +54,8 @@ infinity: non-zero elements then take +-127 and zeros stay 0.
 Codes are stored one signed byte per element, K contiguous, row-major.
 
 Pins (tests/test_oracle_quantizers.py): the worked example of Zhou notes
-sec. 2.2 (range 7 gives step 1; range 1 gives step 1/7), brute-force argmin
+sec. 2.2 (range 7 gives step 1; range 1 gives step 1/7), the saturated
+scale on both sides of the fp16 overflow threshold, brute-force argmin
 over the 15 INT4 codes, the 255 8-bit codes and the 8 E2M1 magnitudes,
 brute-force search for e, the no-clipping property and the Eq. (9) per-group
 error bound (per row for 8-bit).
@@ -61,6 +67,7 @@ from .rounding import round_f16
 
 INT4_GROUP = 64
 MXFP4_GROUP = 32
+F16_MAX = 65504.0            # largest finite IEEE binary16 value
 E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
 
 
@@ -83,6 +90,7 @@ def quantize_int4(z):
     amax = np.max(np.abs(zg), axis=2)                       # fp32, exact
     s32 = (amax / np.float32(7.0)).astype(np.float32)       # fp32 division
     s16 = round_f16(s32)                                    # stored scale
+    s16 = np.where(np.isposinf(s16), F16_MAX, s16)          # saturated, not infinite
     s16_32 = s16.astype(np.float32)                         # exact
     with np.errstate(divide="ignore", invalid="ignore"):
         rcp = (np.float32(1.0) / s16_32).astype(np.float32)

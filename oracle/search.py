@@ -8,6 +8,11 @@ with it, and is scored by how far the layer's output on the calibration
 inputs lands from the floating-point output X W; the finite smallest score
 wins.
 
+With residual iteration on (the doc: "Residual iteration"), each
+candidate's iterations are scored by that same calibration output error,
+not by the weight error the doc names for runs without smooth search, and
+the candidate's score is that of its kept iteration.
+
 Readings (the pages leave these open):
 S1  x_span / w_span are the per-input-channel absolute maxima of the
     calibration activations and of the weight rows, the statistics Eq. (4)
@@ -96,17 +101,28 @@ def reservoir_select(n_calls, k, seed):
     return sorted(slots)
 
 
-def smooth_search(w, x_cal, rank, fmt, grids=20, residual_iters=1):
+def candidate_score(x, y_ref):
+    """S2 + S3 as a function of a deployable layer: the relative error of
+    its bf16-rounded output on the calibration rows."""
+    return lambda layer: output_error(round_bf16(F.forward(x, layer)["y"]), y_ref)
+
+
+def smooth_search(w, x_cal, rank, fmt, grids=20, residual_iters=1, early_stop=False, details=None):
     """Score every candidate on x_cal ([M, K] bf16 values); returns
-    (best index, list of (alpha, beta), list of scores)."""
+    (best index, list of (alpha, beta), list of scores).  `details`, if a
+    list, receives per candidate the prepared layer's kept iteration and its
+    per-iteration scores."""
     w = np.asarray(w, dtype=np.float64)
     x = np.asarray(x_cal, dtype=np.float64)
     amax = P.calib_amax(x)
     y_ref = x @ w
+    score = candidate_score(x, y_ref)
     pairs = candidates(grids)
     errors = []
     for alpha, beta in pairs:
-        layer = P.prepare(w, amax, alpha, rank, fmt, beta=beta, residual_iters=residual_iters)
-        y = F.forward(x, layer)["y"]
-        errors.append(output_error(round_bf16(y), y_ref))
+        layer = P.prepare(w, amax, alpha, rank, fmt, beta=beta, residual_iters=residual_iters,
+                          early_stop=early_stop, score=score)
+        errors.append(min(layer["iter_errors"]))
+        if details is not None:
+            details.append({"best_iter": layer["best_iter"], "iter_scores": list(layer["iter_errors"])})
     return select(errors), pairs, errors

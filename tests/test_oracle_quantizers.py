@@ -87,6 +87,33 @@ def test_int4_tiny_scale_clamps():
     assert q[0, 0] == 7 and q[0, 1] == -7
 
 
+def test_int4_scale_saturates_at_fp16_max():
+    """A group whose amax / 7 lies past the fp16 range keeps a finite
+    scale: 65504, the largest binary16 value, with codes clipped at +-7.
+    Both sides of the overflow threshold (amax / 7 = 65520, the midpoint
+    between 65504 and 2^16, which rounds to infinity under ties-to-even)
+    give that same scale, so the saturated scale is continuous with the
+    unsaturated one."""
+    z = np.zeros((4, 64), dtype=np.float32)
+    z[0, 0] = 7 * 65519.0            # s32 = 65519 rounds down to 65504: finite without saturation
+    z[1, 0] = 7 * 65520.0            # s32 = 65520 rounds to +inf in fp16: saturated
+    z[2, :8] = [1e30, -1e30, 65504 * 6.6, 65504 * 7.4, 65504 * 3.2, -65504 * 2.5, 65504 * 0.5, 65504 * 0.49]
+    z[3, 0] = 3.4e38                 # near the fp32 maximum
+    q, s = Q.quantize_int4(z)
+    assert np.all(s[:, 0] == 65504.0)
+    with np.errstate(over="ignore"):
+        assert np.float16(7 * 65519.0 / 7) == np.float16(65504.0) and np.isinf(np.float16(np.float32(65520.0)))
+    assert q[0, 0] == 7 and q[1, 0] == 7 and q[3, 0] == 7
+    # closed form under the saturated scale: clip(rint(z / 65504), -7, 7),
+    # ties to even (-2.5 -> -2, 0.5 -> 0)
+    assert list(q[2, :8]) == [7, -7, 7, 7, 3, -2, 0, 0]
+    deq = Q.decode_int4(q, s)
+    assert np.all(np.isfinite(deq))
+    # below the clipping point the Eq. (9) element bound |z - s q| <= s / 2 still holds
+    inside = np.abs(z.astype(np.float64)) <= 7.5 * 65504
+    assert np.all(np.abs(z.astype(np.float64) - deq)[inside] <= 65504 / 2)
+
+
 def test_int4_eq9_group_bound():
     rng = np.random.default_rng(11)
     z = (rng.standard_t(3, (32, 64 * 16)) * 0.05).astype(np.float32)

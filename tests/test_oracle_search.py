@@ -64,6 +64,61 @@ def test_outlier_activations_select_smoothing():
     assert all(np.isfinite(errs))
 
 
+def _plain_output_error(x, w, layer):
+    """The score written out from its definition: the layer's output on the
+    calibration rows (quantized main path plus low-rank branch, no bias),
+    rounded to bf16, against X W."""
+    from oracle.forward import forward
+    y_ref = x @ w
+    y = P.round_bf16(forward(x, layer)["y"])
+    return float(np.linalg.norm(y - y_ref) / np.linalg.norm(y_ref))
+
+
+def test_residual_iterations_under_search_score_the_output():
+    """AutoRound doc, "Residual iteration": with smooth search on, the
+    residual iterations are scored by the calibration output error.  Every
+    iterate is scored on its own (brute force over the iteration sequence),
+    the kept iteration is the first minimum of those scores, and on this
+    layer (16 calibration rows) it is not the iteration the weight error
+    would keep, so the reading is observable."""
+    s = S.spec("tiny", M=32, K=256, N=128, rank=16, fmt="int4")
+    d = S.make_layer(s)
+    x = d["X"][:16].astype(np.float64)
+    w = d["W"].astype(np.float64)
+    amax = P.calib_amax(x)
+    lam32, inv = P.smoothing_factors(amax, w, 0.5)
+    wt = P.smooth_weight(w, lam32)
+    _, weight_err, cands = P.residual_iterations(wt, 16, "int4", iters=8, keep_all=True)
+    brute = [_plain_output_error(x, w, P.candidate_layer(c, lam32, inv, "int4", 16)) for c in cands]
+    score = SR.candidate_score(x, x @ w)
+    lo = P.prepare(w, amax, 0.5, 16, "int4", residual_iters=8, score=score)
+    assert lo["iter_errors"] == pytest.approx(brute, rel=1e-12)
+    assert lo["best_iter"] == int(np.argmin(brute))
+    assert lo["best_iter"] != int(np.argmin(weight_err))
+    # the search itself reports that candidate's kept iteration and score
+    det = []
+    _, pairs, errs = SR.smooth_search(w, x, 16, "int4", grids=2, residual_iters=8, details=det)
+    k = pairs.index((0.5, 0.5))
+    assert det[k]["best_iter"] == lo["best_iter"]
+    assert errs[k] == pytest.approx(min(brute), rel=1e-12)
+    # early stop: the scored run cut at its first rise above the best so far
+    le = P.prepare(w, amax, 0.5, 16, "int4", residual_iters=8, score=score, early_stop=True)
+    stop = next((t for t in range(1, 8) if brute[t] > min(brute[:t])), 7)
+    assert le["iter_errors"][:stop + 1] == pytest.approx(brute[:stop + 1], rel=1e-12)
+    assert len(le["iter_errors"]) == stop + 1
+
+
+def test_search_without_residual_iteration_scores_the_prepared_layer():
+    s = S.spec("tiny", M=64, K=256, N=128, rank=16, fmt="mxfp4")
+    d = S.make_layer(s)
+    x = d["X"].astype(np.float64)
+    w = d["W"].astype(np.float64)
+    _, pairs, errs = SR.smooth_search(w, x, 16, "mxfp4", grids=2)
+    amax = P.calib_amax(x)
+    for (a, b), e in zip(pairs, errs):
+        assert e == pytest.approx(_plain_output_error(x, w, P.prepare(w, amax, a, 16, "mxfp4", beta=b)), rel=1e-12)
+
+
 def test_reservoir_small_cases():
     assert SR.reservoir_select(5, 8, 1) == [0, 1, 2, 3, 4]      # fewer calls than slots: all kept
     assert SR.reservoir_select(8, 8, 1) == list(range(8))
