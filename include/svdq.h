@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define SVDQ_ABI_VERSION 5   /* 5: the down factor's kernel layout holds rank / 16 column tiles */
+#define SVDQ_ABI_VERSION 6   /* 6: the search reports the winner's kept residual iteration */
 #define SVDQ_MAX_RANK 128   /* msModelSlim doc, svd_res: rank not above 128 recommended */
 
 typedef enum svdq_status {
@@ -225,6 +225,8 @@ typedef struct svdq_search_result {
   double  alpha, beta;            /* the winner's exponents */
   double* errors;                 /* host [count] scores, NaN where a candidate could not be
                                      prepared (optional, caller-allocated) */
+  int32_t best_iter;              /* the winner's kept residual iteration (0 without residual
+                                     iteration), -1 if none is finite */
 } svdq_search_result;
 
 /* Reservoir selection of calibration calls (AutoRound doc, "Smooth search":
@@ -243,11 +245,15 @@ size_t svdq_search_workspace_bytes(int32_t M, int32_t K, int32_t N, int32_t rank
 /* Smooth-factor grid search of one layer (AutoRound doc, "Smooth search").
  * lambda_i = x_span_i^alpha / w_span_i^beta with x_span the per-channel
  * absolute maximum of the calibration rows x_cal and w_span that of the
- * weight rows.  Every candidate is prepared as svdq_prepare does (with
- * opts' residual iteration), run through svdq_linear_forward on x_cal
- * (no bias) and scored by ||Y - x_cal W||_F / ||x_cal W||_F, with the
- * reference x_cal W computed on the device in fp32.  The finite smallest
- * score wins (the earlier candidate on ties).
+ * weight rows.  Every candidate is prepared as svdq_prepare does, run
+ * through svdq_linear_forward on x_cal (no bias) and scored by
+ * ||Y - x_cal W||_F / ||x_cal W||_F, with the reference x_cal W computed on
+ * the device in fp32.  With opts' residual iteration, every iteration of a
+ * candidate is scored by that output error (AutoRound doc, "Residual
+ * iteration": calibration output error when smooth is on, in place of the
+ * weight error svdq_prepare uses), the best iteration is kept (early stop
+ * at the first score above the best) and its score is the candidate's.
+ * The finite smallest score wins (the earlier candidate on ties).
  * W: host [K, N] fp32.  x_cal: device [M, K] bf16, 16-byte aligned.
  * ws: device workspace of svdq_search_workspace_bytes(), 256-byte aligned.
  * best (optional): receives the winner's lambda, smooth_inv, l1, l2, wq and

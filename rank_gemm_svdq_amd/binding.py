@@ -54,7 +54,11 @@ def _scales_view(a, f):
 
 class SvdqError(RuntimeError):
     def __init__(self, status, where):
-        super().__init__(f"{where}: {status_str(status)} (status {status})")
+        try:
+            text = status_str(status)
+        except Exception:           # the library itself may be what failed to load
+            text = "error"
+        super().__init__(f"{where}: {text} (status {status})")
         self.status = status
 
 
@@ -95,11 +99,11 @@ class SearchOpts(C.Structure):
 
 class SearchResult(C.Structure):
     _fields_ = [("count", C.c_int32), ("best", C.c_int32), ("alpha", C.c_double), ("beta", C.c_double),
-                ("errors", C.c_void_p)]
+                ("errors", C.c_void_p), ("best_iter", C.c_int32)]
 
 
 _lib = None
-ABI_VERSION = 5   # SVDQ_ABI_VERSION of include/svdq.h that these structures mirror
+ABI_VERSION = 6   # SVDQ_ABI_VERSION of include/svdq.h that these structures mirror
 
 
 def lib():
@@ -322,6 +326,44 @@ class DeviceLayer:
                            device=self.wq.device)
 
 
+_TWO_BYTE = ("torch.int16", "torch.bfloat16")
+
+
+def _check_tensor(t, what, where, layer, dtypes, shape=None):
+    """Reject a tensor the kernels cannot take: wrong dtype or shape, a
+    strided view, or memory that is not on the layer's GPU.  The C ABI gets
+    bare pointers and cannot see any of these."""
+    if str(t.dtype) not in dtypes:
+        raise SvdqError(1, f"{where}: {what} has dtype {t.dtype}, expected one of {', '.join(dtypes)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise SvdqError(2, f"{where}: {what} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise SvdqError(1, f"{where}: {what} is not contiguous")
+
+
+def _check_device(layer, where, **tensors):
+    for what, t in tensors.items():
+        if not t.is_cuda:
+            raise SvdqError(1, f"{where}: {what} is not in GPU memory")
+        if t.device != layer.wq.device:
+            raise SvdqError(1, f"{where}: {what} is on {t.device}, the layer on {layer.wq.device}")
+
+
+def _check_x(layer, X, where):
+    if X.dim() != 2 or X.shape[1] != layer.K:
+        raise SvdqError(2, f"{where}: X has shape {tuple(X.shape)}, expected (M, {layer.K})")
+    _check_tensor(X, "X", where, layer, _TWO_BYTE)
+    return X.shape[0]
+
+
+def _check_y(layer, Y, M, where):
+    _check_tensor(Y, "Y", where, layer, _TWO_BYTE, (M, layer.N))
+
+
+def _check_ws(layer, ws, where):
+    _check_tensor(ws, "workspace", where, layer, ("torch.uint8",))
+
+
 def _stream(stream):
     torch = _torch()
     s = torch.cuda.current_stream() if stream is None else stream
@@ -329,25 +371,36 @@ def _stream(stream):
 
 
 def quantize_lora_down(layer, X, ws, stream=None):
-    M = X.shape[0]
+    M = _check_x(layer, X, "svdq_quantize_lora_down")
+    _check_ws(layer, ws, "svdq_quantize_lora_down")
+    _check_device(layer, "svdq_quantize_lora_down", X=X, workspace=ws)
     _check(lib().svdq_quantize_lora_down(C.byref(layer.struct), X.data_ptr(), M, ws.data_ptr(), ws.numel(),
                                          _stream(stream)), "svdq_quantize_lora_down")
 
 
 def gemm_lora_up(layer, ws, M, Y, stream=None):
+    _check_ws(layer, ws, "svdq_gemm_lora_up")
+    _check_y(layer, Y, M, "svdq_gemm_lora_up")
+    _check_device(layer, "svdq_gemm_lora_up", workspace=ws, Y=Y)
     _check(lib().svdq_gemm_lora_up(C.byref(layer.struct), ws.data_ptr(), ws.numel(), M, Y.data_ptr(),
                                    _stream(stream)), "svdq_gemm_lora_up")
 
 
 def linear_forward(layer, X, Y, ws, stream=None):
-    M = X.shape[0]
+    M = _check_x(layer, X, "svdq_linear_forward")
+    _check_y(layer, Y, M, "svdq_linear_forward")
+    _check_ws(layer, ws, "svdq_linear_forward")
+    _check_device(layer, "svdq_linear_forward", X=X, Y=Y, workspace=ws)
     _check(lib().svdq_linear_forward(C.byref(layer.struct), X.data_ptr(), M, Y.data_ptr(), ws.data_ptr(),
                                      ws.numel(), _stream(stream)), "svdq_linear_forward")
 
 
 def linear_forward_unfused(layer, X, Y, ws, stream=None):
     """The same layer as four separate kernels (svdq_linear_forward_unfused)."""
-    M = X.shape[0]
+    M = _check_x(layer, X, "svdq_linear_forward_unfused")
+    _check_y(layer, Y, M, "svdq_linear_forward_unfused")
+    _check_ws(layer, ws, "svdq_linear_forward_unfused")
+    _check_device(layer, "svdq_linear_forward_unfused", X=X, Y=Y, workspace=ws)
     _check(lib().svdq_linear_forward_unfused(C.byref(layer.struct), X.data_ptr(), M, Y.data_ptr(), ws.data_ptr(),
                                              ws.numel(), _stream(stream)), "svdq_linear_forward_unfused")
 
@@ -374,6 +427,10 @@ def smooth_search(W, X_cal, rank, fmt, grids=20, residual_iters=1, early_stop=Fa
     torch = _torch()
     W = np.ascontiguousarray(W, dtype=np.float32)
     K, N = W.shape
+    if X_cal.dim() != 2 or X_cal.shape[1] != K:
+        raise SvdqError(2, f"svdq_smooth_search: X_cal has shape {tuple(X_cal.shape)}, expected (M, {K})")
+    if str(X_cal.dtype) not in _TWO_BYTE or not X_cal.is_contiguous() or not X_cal.is_cuda:
+        raise SvdqError(1, "svdq_smooth_search: X_cal must be a contiguous int16/bfloat16 GPU tensor")
     M = X_cal.shape[0]
     f = fmt_code(fmt)
     n = lib().svdq_smooth_candidates(int(grids), None, None)
@@ -392,13 +449,14 @@ def smooth_search(W, X_cal, rank, fmt, grids=20, residual_iters=1, early_stop=Fa
     pr = Prepared(_p(out["lambda"]).value, _p(out["smooth_inv"]).value,
                   _p(out["l1"]).value if rank else None, _p(out["l2"]).value if rank else None,
                   None, None, _p(out["wq"]).value, _p(out["ws"]).value, None, None)
-    res = SearchResult(0, -1, 0.0, 0.0, _p(errors).value)
+    res = SearchResult(0, -1, 0.0, 0.0, _p(errors).value, -1)
     opts = SearchOpts(int(grids), int(residual_iters), int(bool(early_stop)), int(threads))
     _check(lib().svdq_smooth_search(_p(W), K, N, rank, f, X_cal.data_ptr(), M, C.byref(opts), ws.data_ptr(),
                                     ws.numel(), _stream(stream), C.byref(res), C.byref(pr)), "svdq_smooth_search")
     out["ws"] = _scales_view(out["ws"], f)
     out.update(K=K, N=N, rank=rank, fmt=f)
-    return {"best": res.best, "alpha": res.alpha, "beta": res.beta, "errors": errors, "prepared": out}
+    return {"best": res.best, "alpha": res.alpha, "beta": res.beta, "errors": errors, "prepared": out,
+            "best_iter": res.best_iter}
 
 
 def reservoir_select(n_calls, k, seed):

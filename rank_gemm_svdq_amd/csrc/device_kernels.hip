@@ -215,7 +215,9 @@ __global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __res
       // INT4: the 64-element group spans lane groups g and g ^ 1
       const float amax64 = fmaxf(amax, __shfl_xor(amax, 16));
       const float s32 = amax64 / 7.0f;
-      const _Float16 s16 = (_Float16)s32;
+      // fp16 scale, saturated at 65504 instead of overflowing to infinity
+      _Float16 s16 = (_Float16)s32;
+      if (s32 >= 65520.0f) s16 = (_Float16)65504.0f;
       const float sf = (float)s16;
       uint32_t d[4] = {0u, 0u, 0u, 0u};
       if (sf != 0.f) {

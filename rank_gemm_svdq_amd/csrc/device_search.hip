@@ -1,7 +1,10 @@
 // Smooth-factor grid search of one layer (AutoRound doc, "Smooth search"):
 // every candidate (alpha, beta) is prepared on the host, copied into one
 // set of device layer buffers and scored by running the fused forward on
-// the calibration rows against the floating-point output X W.
+// the calibration rows against the floating-point output X W.  With
+// residual iteration, every iteration of a candidate is scored that way and
+// the best one kept (AutoRound doc, "Residual iteration": calibration
+// output error when smooth is on).
 //
 // Device work per search: the per-channel absolute maximum of the
 // calibration rows (the activation statistic of lambda), the fp32 reference
@@ -238,11 +241,40 @@ svdq_status svdq_smooth_search(const float* W, int32_t K, int32_t N, int32_t ran
   svdq_layer layer{K, N, rank, fmt, reinterpret_cast<const float*>(dev(SL.sinv)), dev(SL.wq), dev(SL.ws),
                    reinterpret_cast<const uint16_t*>(dev(SL.l1k)), reinterpret_cast<const uint16_t*>(dev(SL.l2k)),
                    nullptr};
-  int32_t best_i = -1;
+  // Scorer of one prepared candidate (a residual iteration of one (alpha,
+  // beta) pair): kernel layout, upload, the fused forward on the
+  // calibration rows, and the relative output error against X W.
+  Scorer scorer = [&](const CandidateView& v, double* score) -> svdq_status {
+    svdq_status ls = svdq_kernel_layout(K, N, rank, fmt, v.smooth_inv, v.wq, v.ws, v.l1b, v.l2b, wq_k.data(),
+                                        ws_k.data(), l1k.data(), l2k.data());
+    if (ls != SVDQ_OK) return ls;
+    if (!ok(hipMemcpyAsync(dev(SL.sinv), v.smooth_inv, (size_t)K * 4, hipMemcpyHostToDevice, st)) ||
+        !ok(hipMemcpyAsync(dev(SL.wq), wq_k.data(), g.wq_bytes, hipMemcpyHostToDevice, st)) ||
+        !ok(hipMemcpyAsync(dev(SL.ws), ws_k.data(), g.ws_bytes, hipMemcpyHostToDevice, st)) ||
+        (rank > 0 && (!ok(hipMemcpyAsync(dev(SL.l1k), l1k.data(), g.l1k_bytes, hipMemcpyHostToDevice, st)) ||
+                      !ok(hipMemcpyAsync(dev(SL.l2k), l2k.data(), g.l2k_bytes, hipMemcpyHostToDevice, st)))))
+      return SVDQ_ERR_DEVICE;
+    ls = svdq_linear_forward(&layer, x_cal, M, reinterpret_cast<uint16_t*>(dev(SL.y)), dev(SL.fws), SL.fws_bytes,
+                             stream);
+    if (ls != SVDQ_OK) return ls;
+    hipLaunchKernelGGL(sqdiff_kernel, dim3(SR_BLOCKS), dim3(256), 0, st,
+                       reinterpret_cast<const uint16_t*>(dev(SL.y)), reinterpret_cast<const float*>(dev(SL.yref)),
+                       (int64_t)M * N, reinterpret_cast<double*>(dev(SL.part)));
+    if (!ok(hipGetLastError()) ||
+        !ok(hipMemcpyAsync(part.data(), dev(SL.part), SR_BLOCKS * 8, hipMemcpyDeviceToHost, st)) ||
+        !ok(hipStreamSynchronize(st)))
+      return SVDQ_ERR_DEVICE;
+    *score = std::sqrt(sum_parts(part) / ref2);
+    return SVDQ_OK;
+  };
+  const int32_t iters = opts ? std::max(1, opts->residual_iters) : 1;
+  if (iters > SVDQ_MAX_RESIDUAL_ITERS) return SVDQ_ERR_ARG;
+  std::vector<double> iter_scores(iters);
+  int32_t best_i = -1, best_iter = 0, kept_iter = 0;
   for (int32_t c = 0; c < count; ++c) {
     svdq_prepare_opts po{};
     po.threads = opts ? opts->threads : 0;
-    po.residual_iters = opts ? opts->residual_iters : 1;
+    po.residual_iters = iters;
     po.residual_early_stop = opts ? opts->residual_early_stop : 0;
     po.has_beta = 1;
     po.beta = betas[c];
@@ -253,31 +285,17 @@ svdq_status svdq_smooth_search(const float* W, int32_t K, int32_t N, int32_t ran
     pr.l2 = rank ? l2.data() : nullptr;
     pr.wq = wq.data();
     pr.ws = wsc.data();
-    s = svdq_prepare(W, amax.data(), K, N, alphas[c], rank, fmt, &po, &pr);
+    pr.iter_errors = iter_scores.data();
+    pr.best_iter = &kept_iter;
+    // each residual iteration is scored by the calibration output error
+    // (AutoRound doc, "Residual iteration": output error when smooth is on)
+    s = prepare_layer(W, amax.data(), K, N, alphas[c], rank, fmt, &po, &pr, &scorer);
     if (s == SVDQ_ERR_NUMERIC) continue;          // a candidate lambda out of range scores NaN
     if (s != SVDQ_OK) return s;
-    s = svdq_kernel_layout(K, N, rank, fmt, sinv.data(), wq.data(), wsc.data(), rank ? l1.data() : nullptr,
-                           rank ? l2.data() : nullptr, wq_k.data(), ws_k.data(), l1k.data(), l2k.data());
-    if (s != SVDQ_OK) return s;
-    if (!ok(hipMemcpyAsync(dev(SL.sinv), sinv.data(), (size_t)K * 4, hipMemcpyHostToDevice, st)) ||
-        !ok(hipMemcpyAsync(dev(SL.wq), wq_k.data(), g.wq_bytes, hipMemcpyHostToDevice, st)) ||
-        !ok(hipMemcpyAsync(dev(SL.ws), ws_k.data(), g.ws_bytes, hipMemcpyHostToDevice, st)) ||
-        (rank > 0 && (!ok(hipMemcpyAsync(dev(SL.l1k), l1k.data(), g.l1k_bytes, hipMemcpyHostToDevice, st)) ||
-                      !ok(hipMemcpyAsync(dev(SL.l2k), l2k.data(), g.l2k_bytes, hipMemcpyHostToDevice, st)))))
-      return SVDQ_ERR_DEVICE;
-    s = svdq_linear_forward(&layer, x_cal, M, reinterpret_cast<uint16_t*>(dev(SL.y)), dev(SL.fws), SL.fws_bytes,
-                            stream);
-    if (s != SVDQ_OK) return s;
-    hipLaunchKernelGGL(sqdiff_kernel, dim3(SR_BLOCKS), dim3(256), 0, st,
-                       reinterpret_cast<const uint16_t*>(dev(SL.y)), reinterpret_cast<const float*>(dev(SL.yref)),
-                       (int64_t)M * N, reinterpret_cast<double*>(dev(SL.part)));
-    if (!ok(hipGetLastError()) ||
-        !ok(hipMemcpyAsync(part.data(), dev(SL.part), SR_BLOCKS * 8, hipMemcpyDeviceToHost, st)) ||
-        !ok(hipStreamSynchronize(st)))
-      return SVDQ_ERR_DEVICE;
-    errs[c] = std::sqrt(sum_parts(part) / ref2);
+    errs[c] = iter_scores[kept_iter];
     if (std::isfinite(errs[c]) && (best_i < 0 || errs[c] < errs[best_i])) {
       best_i = c;
+      best_iter = kept_iter;
       if (best) {
         std::memcpy(best->smooth_inv, sinv.data(), (size_t)K * 4);
         if (best->lambda) std::memcpy(best->lambda, lam.data(), (size_t)K * 4);
@@ -292,6 +310,7 @@ svdq_status svdq_smooth_search(const float* W, int32_t K, int32_t N, int32_t ran
   }
   res->count = count;
   res->best = best_i;
+  res->best_iter = best_i < 0 ? -1 : best_iter;
   if (res->errors)
     for (int32_t c = 0; c < count; ++c) res->errors[c] = errs[c];
   if (best_i < 0) return SVDQ_ERR_NUMERIC;

@@ -58,6 +58,24 @@ void quant_int4_group(const float* x, uint8_t* nib /*64 nibble values*/, uint16_
 void quant_mxfp4_group(const float* x, uint8_t* nib /*32 nibble values*/, uint8_t* scale_byte);
 void quant_w8_row(const float* x, int32_t K, int8_t* q, float* scale);
 
+// One residual-iteration candidate as a deployable layer (canonical host
+// buffers, valid during the call), and a function that scores it in place
+// of the weight reconstruction error (the smooth search's calibration
+// output error).
+struct CandidateView {
+  const float* lambda;
+  const float* smooth_inv;
+  const uint16_t* l1b;   // [K, rank] (NULL when rank == 0)
+  const uint16_t* l2b;   // [rank, N]
+  const uint8_t* wq;     // canonical codes
+  const uint8_t* ws;     // canonical scales
+};
+using Scorer = std::function<svdq_status(const CandidateView&, double* score)>;
+
+// svdq_prepare with an optional scorer of the residual iterations.
+svdq_status prepare_layer(const float* W, const float* act_amax, int32_t K, int32_t N, double alpha, int32_t rank,
+                          int32_t fmt, const svdq_prepare_opts* opts, svdq_prepared* out, const Scorer* scorer);
+
 void parallel_for(int64_t n, int threads, const std::function<void(int64_t, int64_t)>& fn);
 int default_threads(int requested);
 

@@ -142,12 +142,15 @@ float float_from_half(uint16_t h) {
 // ------------------------------------------------------------ quantizers
 
 // INT4 (Zhou notes sec. 2.2 Eq. (1); 64 elements, fp16 scale): s32 = amax/7
-// in fp32, s16 = fp16(s32), codes = clamp(rint(x * fp32(1/s16)), -7, 7).
+// in fp32, s16 = fp16(s32), codes = clamp(rint(x * fp32(1/s16)), -7, 7).  A
+// scale past the fp16 range saturates at 65504 (the largest finite binary16
+// value; the clamp then clips the codes) instead of becoming infinite.
 void quant_int4_group(const float* x, uint8_t* nib, uint16_t* scale_bits) {
   float amax = 0.0f;
   for (int i = 0; i < 64; ++i) amax = std::max(amax, std::fabs(x[i]));
   const float s32 = amax / 7.0f;
-  const uint16_t s16 = half_from_float(s32);
+  uint16_t s16 = half_from_float(s32);
+  if (s16 == 0x7C00) s16 = 0x7BFF;
   const float sf = float_from_half(s16);
   *scale_bits = s16;
   if (sf == 0.0f) {
@@ -454,8 +457,14 @@ static svdq_status fit_candidate(const std::vector<double>& wt, const double* ta
   return SVDQ_OK;
 }
 
-svdq_status svdq_prepare(const float* W, const float* act_amax, int32_t K, int32_t N, double alpha, int32_t rank,
-                         int32_t fmt, const svdq_prepare_opts* opts, svdq_prepared* out) {
+}  // extern "C"
+
+namespace svdq {
+
+// The offline preparation; `scorer` (optional) replaces the weight
+// reconstruction error as the residual iterations' score.
+svdq_status prepare_layer(const float* W, const float* act_amax, int32_t K, int32_t N, double alpha, int32_t rank,
+                          int32_t fmt, const svdq_prepare_opts* opts, svdq_prepared* out, const Scorer* scorer) {
   if (!W || !act_amax || !out || !out->smooth_inv || !out->wq || !out->ws) return SVDQ_ERR_ARG;
   if (!valid_fmt(fmt)) return SVDQ_ERR_UNSUPPORTED;
   if (!valid_kn(K, N) || !valid_rank(rank) || rank > std::min(K, N)) return SVDQ_ERR_SHAPE;
@@ -508,6 +517,12 @@ svdq_status svdq_prepare(const float* W, const float* act_amax, int32_t K, int32
                                          max_iters, cur);
     if (st != SVDQ_OK) return st;
     cur.iter = t;
+    if (scorer) {
+      const CandidateView v{lam.data(), inv.data(), rank ? cur.l1b.data() : nullptr, rank ? cur.l2b.data() : nullptr,
+                            cur.wq.data(), cur.ws.data()};
+      const svdq_status ss = (*scorer)(v, &cur.err);
+      if (ss != SVDQ_OK) return ss;
+    }
     if (out->iter_errors) out->iter_errors[t] = cur.err;
     if (t + 1 < iters) {
       target.resize((size_t)K * N);
@@ -515,7 +530,9 @@ svdq_status svdq_prepare(const float* W, const float* act_amax, int32_t K, int32
         for (size_t i = (size_t)lo * N; i < (size_t)hi * N; ++i) target[i] = wt[i] - cur.qr[i];
       });
     }
-    if (t == 0 || cur.err < best.err) {
+    // the smallest score wins, the earlier on ties; a non-finite score
+    // never displaces a finite one
+    if (t == 0 || cur.err < best.err || (!std::isfinite(best.err) && std::isfinite(cur.err))) {
       std::swap(best, cur);
     } else if (early_stop && cur.err > best.err) {
       break;
@@ -543,6 +560,15 @@ svdq_status svdq_prepare(const float* W, const float* act_amax, int32_t K, int32
     }
   }
   return SVDQ_OK;
+}
+
+}  // namespace svdq
+
+extern "C" {
+
+svdq_status svdq_prepare(const float* W, const float* act_amax, int32_t K, int32_t N, double alpha, int32_t rank,
+                         int32_t fmt, const svdq_prepare_opts* opts, svdq_prepared* out) {
+  return prepare_layer(W, act_amax, K, N, alpha, rank, fmt, opts, out, nullptr);
 }
 
 int64_t svdq_reservoir_select(int64_t n_calls, int64_t k, uint64_t seed, int64_t* out) {

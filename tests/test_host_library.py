@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = B.lib()
     for n in sorted(names):
         assert hasattr(lib, n), n
-    assert B.abi_version() == B.ABI_VERSION == 5
+    assert B.abi_version() == B.ABI_VERSION == 6
     assert B.status_str(0) == "ok"
 
 
@@ -49,6 +49,9 @@ def test_packer_bit_exact_against_oracle(fmt):
     x[7, :] = 0.0                                    # all-zero row (8-bit: one scale per row)
     x[8, :] = 0.0
     x[8, :8] = [127.0, -3.0, 2.5, -2.5, 0.5, 126.5, -0.5, 1.5]   # 8-bit exact ties at scale 1
+    x[9, :64] *= 1e30                                # INT4 scale past the fp16 range: saturated at 65504
+    x[9, 64] = 7 * 65520.0                           # exactly at the fp16 overflow threshold
+    x[9, 128] = 7 * 65519.0                          # just below it
     codes, scales = B.pack_host(x, fmt)
     q = Q.quantize(x, fmt)
     assert np.array_equal(codes, q["packed"])
@@ -416,3 +419,44 @@ def test_reservoir_select_matches_oracle():
     for n, k, seed in [(5, 8, 1), (1000, 128, 7), (300, 17, 2 ** 63 + 5), (129, 128, 0), (0, 3, 1), (3, 0, 1)]:
         assert B.reservoir_select(n, k, seed) == SR.reservoir_select(n, k, seed)
     assert B.lib().svdq_reservoir_select(10, 3, 1, None) == -1
+
+
+def test_binding_rejects_unusable_tensors_before_the_library(monkeypatch):
+    """The device entry points take bare pointers; the binding checks dtype,
+    shape, contiguity and device first and raises without calling into the
+    library (which is replaced here by a function that fails the test)."""
+    import types
+    import torch
+    from rank_gemm_svdq_amd import binding as BD
+
+    def no_call():
+        raise AssertionError("the library was called")
+
+    monkeypatch.setattr(BD, "lib", no_call)
+    monkeypatch.setattr(BD, "status_str", lambda s: "error")
+    lay = types.SimpleNamespace(K=256, N=128, rank=16, fmt=0, struct=None, wq=torch.empty(1, dtype=torch.uint8))
+    X = torch.zeros((8, 256), dtype=torch.int16)
+    Y = torch.zeros((8, 128), dtype=torch.int16)
+    ws = torch.zeros(4096, dtype=torch.uint8)
+    cases = [
+        (dict(X=X.float()), "dtype"),
+        (dict(X=torch.zeros((8, 255), dtype=torch.int16)), "shape"),
+        (dict(X=torch.zeros((256, 8), dtype=torch.int16).T), "contiguous"),
+        (dict(Y=torch.zeros((8, 127), dtype=torch.int16)), "shape"),
+        (dict(Y=torch.zeros((9, 128), dtype=torch.bfloat16)), "shape"),
+        (dict(ws=ws.view(torch.int8)), "dtype"),
+        (dict(), "GPU memory"),                       # everything right, but host tensors
+    ]
+    for over, msg in cases:
+        a = dict(X=X, Y=Y, ws=ws)
+        a.update(over)
+        for call in (lambda: BD.linear_forward(lay, a["X"], a["Y"], a["ws"]),
+                     lambda: BD.linear_forward_unfused(lay, a["X"], a["Y"], a["ws"])):
+            with pytest.raises(BD.SvdqError, match=msg):
+                call()
+    with pytest.raises(BD.SvdqError, match="dtype"):
+        BD.quantize_lora_down(lay, X.float(), ws)
+    with pytest.raises(BD.SvdqError, match="shape"):
+        BD.gemm_lora_up(lay, ws, 8, torch.zeros((8, 64), dtype=torch.int16))
+    with pytest.raises(BD.SvdqError, match="GPU memory"):
+        BD.gemm_lora_up(lay, ws, 8, Y)
