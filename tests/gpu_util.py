@@ -2,6 +2,9 @@
 produce the oracle's view of the same inputs."""
 import numpy as np
 
+from oracle import quantizers as Q
+from oracle.rounding import bf16_bits as _bf16_bits
+
 import rank_gemm_svdq_amd as B
 from rank_gemm_svdq_amd import synthetic as S
 from oracle import forward as F
@@ -57,3 +60,84 @@ def oracle_layer(d, fmt, rank, alpha, lora=None, **prep_kw):
 
 def oracle_scales_bits(xs, fmt):
     return np.float16(xs).view(np.uint16) if fmt == "int4" else xs
+
+
+def oracle_canonical(po):
+    """The oracle's prepared layer as the canonical host buffers the library's
+    kernel-layout conversion takes (the oracle's own lambda, factors, codes
+    and scales: the device then computes from exactly the oracle's operands)."""
+    fmt = po["fmt"]
+    K = po["inv_lambda"].shape[0]
+    N = po["wq_packed"].shape[0]
+    if fmt == "int4":
+        ws = np.float16(po["ws"]).view(np.uint16)
+    elif fmt == "w8a8":
+        ws = np.asarray(po["ws"], np.float32)
+    else:
+        ws = np.asarray(po["ws"], np.uint8)
+    rank = po["l1p"].shape[1]
+    return {"K": K, "N": N, "rank": rank, "fmt": B.fmt_code(fmt),
+            "smooth_inv": np.asarray(po["inv_lambda"], np.float32),
+            "wq": np.ascontiguousarray(po["wq_packed"], np.uint8), "ws": ws,
+            "l1": _bf16_bits(po["l1p"]).reshape(K, rank), "l2": _bf16_bits(po["l2p"]).reshape(rank, N)}
+
+
+# Element-wise bound of a device output against the exact (fp64) output of
+# the same operands.  The device forms every main-path partial product
+# exactly and sums them in fp32 (per MFMA step, per 64-group, or in int32
+# with the per-row scales applied after), so the accumulated rounding error
+# is at most (K/32 + 16) u32 times the sum of |products| (u32 = 2^-24;
+# generous for each format's summation order).  The low-rank branch carries
+# x^ and Z as bf16 hi + lo pairs (each within 2^-16 of the value) with fp32
+# accumulation: at most 2^-15 times the nested absolute product
+# (|x^| |L1'|) |L2'|.  Bias and the last additions add a few u32 of |y|;
+# the single bf16 store adds at most half an ulp, 2^-8 |y|.
+def elementwise_bound(x, po, bias=None):
+    fmt = po["fmt"]
+    K = po["inv_lambda"].shape[0]
+    xs = F.smooth_activations(x, po["inv_lambda"]).astype(np.float64)
+    a_q = F.quantize_activations(x, po["inv_lambda"], fmt)["deq"]
+    b_q = Q.dequantize_packed(po["wq_packed"], po["ws"], fmt)
+    a_main = np.abs(a_q) @ np.abs(b_q).T
+    a_lr = (np.abs(xs) @ np.abs(np.asarray(po["l1p"], np.float64))) @ np.abs(np.asarray(po["l2p"], np.float64))
+    y = a_q @ b_q.T + (xs.astype(np.float64) @ np.asarray(po["l1p"], np.float64)) @ np.asarray(po["l2p"], np.float64)
+    if bias is not None:
+        y = y + np.asarray(bias, np.float64)[None, :]
+    e = (K / 32 + 16) * 2.0**-24 * a_main + 2.0**-15 * a_lr + 4 * 2.0**-24 * np.abs(y)
+    return 2.0**-8 * (np.abs(y) + e) + e
+
+
+def assert_elementwise(y_dev, y_ref, bound, what):
+    """Every element within its bound; the report names the worst element."""
+    d = np.abs(np.asarray(y_dev, np.float64) - y_ref)
+    bad = d > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(d / np.maximum(bound, 1e-300)), d.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {d.size} elements outside the bound; worst at {i}: "
+                             f"dev {y_dev[i]!r} ref {y_ref[i]!r} |d| {d[i]:.3e} bound {bound[i]:.3e}")
+
+
+def run_on_oracle_layer(po, x, bias=None):
+    """Device forward (K-A + K-B through the C ABI) of the oracle's own
+    prepared layer on x; returns Y as fp64 and the run's workspace tensor."""
+    import torch
+    canon = oracle_canonical(po)
+    layer = B.DeviceLayer(canon, None if bias is None else S.bf16_bits_of(bias))
+    M = x.shape[0]
+    X = torch.from_numpy(S.bf16_bits_of(x).view(np.int16)).cuda()
+    Y = torch.empty((M, canon["N"]), dtype=torch.int16, device="cuda")
+    ws = layer.workspace(M)
+    B.linear_forward(layer, X, Y, ws)
+    torch.cuda.synchronize()
+    return bf16_to_f64(Y.cpu().numpy())
+
+
+def check_elementwise_on_oracle_layer(po, x, bias, what):
+    """Kernel-isolated parity: the device computes from the oracle's
+    operands, and every element of Y lies within elementwise_bound of the
+    oracle's fp64 forward."""
+    y_dev = run_on_oracle_layer(po, x, bias)
+    assert np.all(np.isfinite(y_dev)), f"{what}: non-finite output"
+    ref = F.forward(x, po, bias)["y"]
+    assert_elementwise(y_dev, ref, elementwise_bound(x, po, bias), what)
+    return y_dev

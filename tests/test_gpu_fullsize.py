@@ -12,8 +12,15 @@ depend on the SVD) must match bit for bit.
 Every row is then checked through a property that holds at any size: Y is
 the bf16 rounding of the exact product of the decoded 4-bit operands the
 device wrote (codes decoded by the oracle's decoders, multiplied in fp32 on
-the GPU by torch) plus Z L2' plus bias, so the whole output lies within bf16
-rounding (2^-9 relative) of that reference.
+the GPU by torch) plus Z L2' plus bias, so every element lies within half a
+bf16 ulp plus the fp32 accumulation slack of that reference.
+
+Kernel-isolated parity: the same kernels then run on the oracle's own
+prepared layer (its lambda, bf16 factors, codes and scales, laid out by the
+library's kernel-layout conversion), and every element of the sampled rows
+must lie within the element-wise bound of the oracle's fp64 forward of those
+rows (tests/gpu_util.elementwise_bound: half a bf16 ulp plus the fp32
+accumulation slack of the main and low-rank sums).
 """
 import numpy as np
 import pytest
@@ -21,7 +28,8 @@ import pytest
 from rank_gemm_svdq_amd import synthetic as S
 from oracle import forward as F
 from oracle import quantizers as Q
-from tests.gpu_util import GpuRun, bf16_to_f64, oracle_layer, oracle_scales_bits, rel_fro
+from tests.gpu_util import (GpuRun, assert_elementwise, bf16_to_f64, elementwise_bound, oracle_layer,
+                            oracle_scales_bits, rel_fro, run_on_oracle_layer)
 
 pytestmark = pytest.mark.gpu
 Y_TOL = 5e-3
@@ -61,12 +69,24 @@ def _check(name, fmt, alpha=None, lora=False):
     torch.backends.cuda.matmul.allow_tf32 = False
     try:
         ref = xd @ wd.T + zt @ l2 + bias
+        # the reference's own fp32 sums carry the same slack as the device's
+        e = (2 * (s.K / 32 + 16) * 2.0**-24) * (xd.abs() @ wd.abs().T) + 2.0**-15 * (zt.abs() @ l2.abs())
+        e += 8 * 2.0**-24 * ref.abs()
     finally:
         torch.backends.cuda.matmul.allow_tf32 = prev
     ydev = (run.Y.to(torch.int32) << 16).view(torch.float32)
     assert bool(torch.isfinite(ydev).all())
     full_err = float(torch.linalg.norm(ydev - ref) / torch.linalg.norm(ref))
     assert full_err <= 2.5e-3, f"{name}/{fmt}: all-row rel_fro {full_err:.3e} against the decoded-operand product"
+    bound = 2.0**-8 * (ref.abs() + e) + e
+    over = (ydev - ref).abs() > bound
+    n_over = int(over.sum())
+    assert n_over == 0, f"{name}/{fmt}: {n_over} elements outside the element-wise bound (first {over.nonzero()[:4].tolist()})"
+    del xd, wd, ref, e, bound, over, ydev
+    # kernel-isolated: the oracle's own layer through the same kernels
+    y_iso = run_on_oracle_layer(po, d["X"], d["bias"])
+    assert_elementwise(y_iso[rows], of["y"], elementwise_bound(d["X"][rows], po, d["bias"]),
+                       f"{name}/{fmt} oracle layer, sampled rows")
     return err
 
 

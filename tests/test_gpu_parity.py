@@ -10,7 +10,8 @@ from rank_gemm_svdq_amd import synthetic as S
 from oracle import forward as F
 from oracle import prepare as P
 from oracle import quantizers as Q
-from tests.gpu_util import GpuRun, bf16_to_f64, oracle_layer, oracle_scales_bits, rel_fro
+from tests.gpu_util import (GpuRun, bf16_to_f64, check_elementwise_on_oracle_layer, oracle_layer,
+                            oracle_scales_bits, rel_fro)
 
 pytestmark = pytest.mark.gpu
 Y_TOL = 5e-3
@@ -28,6 +29,9 @@ def _check_full(run, po, x, bias, z_tol=2e-5):
         assert rel_fro(zl2, of["z"] @ po["l2p"]) <= z_tol
     err = rel_fro(run.y(), of["y"])
     assert err <= Y_TOL, err
+    # kernel-isolated: the same kernels on the oracle's own prepared layer,
+    # every element of Y within its bf16 + fp32-accumulation bound
+    check_elementwise_on_oracle_layer(po, x, bias, f"{run.fmt} M={run.M} K={run.K} N={run.N} rank={run.rank}")
     return err
 
 
@@ -74,8 +78,9 @@ def test_lora_rank48(fmt):
 @pytest.mark.parametrize("fmt", ["int4", "mxfp4", "w8a8"])
 def test_quantizer_edge_values(fmt):
     """Zero rows, bf16 subnormals (MXFP4 scale clamped at 2^-127; 8-bit
-    scale below 2^-128), huge values and exact ties go through K-A; codes
-    and scales bit-exact."""
+    scale below 2^-128), huge values (an INT4 scale past the fp16 range,
+    saturated at 65504) and exact ties go through K-A; codes and scales
+    bit-exact, and Y finite and within its element-wise bound."""
     M, K, N = 48, 512, 64
     x = S.random_bf16(5, (M, K), 2.0)
     x[0] = 0.0
@@ -93,6 +98,10 @@ def test_quantizer_edge_values(fmt):
     xq, xs, _ = run.activations()
     assert np.array_equal(xq, of["xq"])
     assert np.array_equal(xs, oracle_scales_bits(of["xs"], fmt))
+    if fmt == "int4":
+        assert np.any(of["xs"] == 65504.0)           # the huge row's groups saturate
+    assert np.all(np.isfinite(of["y"])) and np.all(np.isfinite(run.y()))
+    check_elementwise_on_oracle_layer(po, x, d["bias"], f"edge values {fmt}")
 
 
 def test_workspace_reuse_and_determinism():
