@@ -321,6 +321,21 @@ svdq_status svdq_gemm_lora_up(const svdq_layer* layer, const void* ws, size_t ws
 svdq_status svdq_linear_forward(const svdq_layer* layer, const uint16_t* X, int32_t M, uint16_t* Y,
                                 void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * forward as svdq_linear_forward without a workspace argument.  The
+ * workspace is a file-scope device array of SVDQ_NOALLOC_MAX_WORKSPACE bytes
+ * in the library, one per GPU, held until the process ends; its device
+ * address is looked up on the first call on each device.  The call
+ * allocates nothing.  Layers whose svdq_workspace_bytes(M, K, rank, fmt)
+ * exceeds the maximum return SVDQ_ERR_WORKSPACE.  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (on
+ * different streams or threads) race and must be serialized by the caller.
+ * Errors: ARG, SHAPE, ALIGN, WORKSPACE, UNSUPPORTED, DEVICE. */
+#define SVDQ_NOALLOC_MAX_WORKSPACE (32u << 20)
+svdq_status svdq_linear_forward_noalloc(const svdq_layer* layer, const uint16_t* X, int32_t M, uint16_t* Y,
+                                        void* stream);
+
 /* The same layer computed by four separate kernels, the arrangement whose
  * cost the notes weigh against the fused kernels (Zhou notes, sec. 6.1: run
  * unfused, the low-rank branch adds a large share of the 4-bit layer's time,

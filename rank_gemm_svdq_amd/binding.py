@@ -16,7 +16,8 @@ __all__ = [
     "INT4", "MXFP4", "SvdqError", "lib", "status_str", "abi_version", "device_check",
     "layer_sizes", "workspace_layout", "workspace_bytes", "calib_absmax", "pack_host",
     "prepare", "attach_lora", "kernel_layout", "unpack_activations", "DeviceLayer",
-    "quantize_lora_down", "gemm_lora_up", "linear_forward", "linear_forward_unfused", "fmt_code", "LIB_PATH",
+    "quantize_lora_down", "gemm_lora_up", "linear_forward", "linear_forward_unfused", "linear_forward_noalloc",
+    "NOALLOC_MAX_WORKSPACE", "fmt_code", "LIB_PATH",
     "ABI_VERSION", "reservoir_select", "smooth_candidates", "search_workspace_bytes", "smooth_search", "SearchOpts", "SearchResult",
 ]
 
@@ -135,6 +136,7 @@ def lib():
     L.svdq_gemm_lora_up.argtypes = [C.POINTER(Layer), vp, sz, i32, vp, vp]
     L.svdq_linear_forward.argtypes = [C.POINTER(Layer), vp, i32, vp, vp, sz, vp]
     L.svdq_linear_forward_unfused.argtypes = [C.POINTER(Layer), vp, i32, vp, vp, sz, vp]
+    L.svdq_linear_forward_noalloc.argtypes = [C.POINTER(Layer), vp, i32, vp, vp]
     L.svdq_reservoir_select.restype = C.c_int64
     L.svdq_reservoir_select.argtypes = [C.c_int64, C.c_int64, C.c_uint64, vp]
     L.svdq_smooth_candidates.restype = i32
@@ -146,7 +148,8 @@ def lib():
     for name in ("svdq_device_check", "svdq_layer_sizes", "svdq_workspace_layout", "svdq_calib_absmax",
                  "svdq_pack_host", "svdq_prepare", "svdq_attach_lora", "svdq_kernel_layout",
                  "svdq_unpack_activations", "svdq_quantize_lora_down", "svdq_gemm_lora_up",
-                 "svdq_linear_forward", "svdq_linear_forward_unfused", "svdq_smooth_search"):
+                 "svdq_linear_forward", "svdq_linear_forward_unfused", "svdq_linear_forward_noalloc",
+                 "svdq_smooth_search"):
         getattr(L, name).restype = C.c_int
     _lib = L
     return L
@@ -393,6 +396,19 @@ def linear_forward(layer, X, Y, ws, stream=None):
     _check_device(layer, "svdq_linear_forward", X=X, Y=Y, workspace=ws)
     _check(lib().svdq_linear_forward(C.byref(layer.struct), X.data_ptr(), M, Y.data_ptr(), ws.data_ptr(),
                                      ws.numel(), _stream(stream)), "svdq_linear_forward")
+
+
+NOALLOC_MAX_WORKSPACE = 32 << 20   # SVDQ_NOALLOC_MAX_WORKSPACE
+
+
+def linear_forward_noalloc(layer, X, Y, stream=None):
+    """svdq_linear_forward with the library's own per-GPU scratch array as
+    the workspace (no allocation; calls overlapping on one GPU race)."""
+    M = _check_x(layer, X, "svdq_linear_forward_noalloc")
+    _check_y(layer, Y, M, "svdq_linear_forward_noalloc")
+    _check_device(layer, "svdq_linear_forward_noalloc", X=X, Y=Y)
+    _check(lib().svdq_linear_forward_noalloc(C.byref(layer.struct), X.data_ptr(), M, Y.data_ptr(), _stream(stream)),
+           "svdq_linear_forward_noalloc")
 
 
 def linear_forward_unfused(layer, X, Y, ws, stream=None):

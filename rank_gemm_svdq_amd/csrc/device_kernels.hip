@@ -1378,6 +1378,29 @@ static svdq_status device_ok() {
   return v == 1 ? SVDQ_OK : SVDQ_ERR_UNSUPPORTED;
 }
 
+// Workspace of svdq_linear_forward_noalloc: one file-scope device array per
+// GPU (the runtime places a copy on every device the library runs on, held
+// until the process ends).  Its name is only a host-side stand-in: host code
+// uses the device address hipGetSymbolAddress returns, looked up once per
+// device with that device current and kept here.
+static __device__ __align__(256) uint8_t scratch[SVDQ_NOALLOC_MAX_WORKSPACE];
+static std::atomic<uint8_t*> g_scratch[64];
+
+static svdq_status scratch_of_current_device(uint8_t** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SVDQ_ERR_DEVICE;
+  if (dev < 0 || dev >= 64) return SVDQ_ERR_UNSUPPORTED;
+  uint8_t* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return SVDQ_ERR_DEVICE;
+    p = static_cast<uint8_t*>(q);
+    g_scratch[dev].store(p, std::memory_order_release);   // racing first calls store the same address
+  }
+  *out = p;
+  return SVDQ_OK;
+}
+
 }  // namespace svdq
 
 using namespace svdq;
@@ -1438,6 +1461,36 @@ svdq_status svdq_linear_forward(const svdq_layer* layer, const uint16_t* X, int3
   if (!aligned16(X) || !aligned16(Y) || !aligned16(ws)) return SVDQ_ERR_ALIGN;
   if ((s = svdq_quantize_lora_down(layer, X, M, ws, ws_bytes, stream)) != SVDQ_OK) return s;
   return svdq_gemm_lora_up(layer, ws, ws_bytes, M, Y, stream);
+}
+
+svdq_status svdq_linear_forward_noalloc(const svdq_layer* layer, const uint16_t* X, int32_t M, uint16_t* Y,
+                                        void* stream) {
+  svdq_status s = check_layer(layer, M);
+  if (s != SVDQ_OK) return s;
+  if (!X || !Y) return SVDQ_ERR_ARG;
+  if (!aligned16(X) || !aligned16(Y)) return SVDQ_ERR_ALIGN;
+  svdq_ws_layout W;
+  if ((s = svdq_workspace_layout(M, layer->K, layer->rank, layer->fmt, &W)) != SVDQ_OK) return s;
+  if (W.total > (size_t)SVDQ_NOALLOC_MAX_WORKSPACE) return SVDQ_ERR_WORKSPACE;
+  if ((s = device_ok()) != SVDQ_OK) return s;
+  uint8_t* ws = nullptr;
+  if ((s = scratch_of_current_device(&ws)) != SVDQ_OK) return s;
+  // the same kernels as svdq_linear_forward, with the scratch array as the
+  // workspace (nothing in it needs clearing: K-A writes every byte K-B reads
+  // for the M rows, and rows past M are never stored)
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (layer->fmt == SVDQ_MXFP4_G32) {
+    e = launch_ka<SVDQ_MXFP4_G32>(*layer, X, M, ws, W, st);
+    if (e == hipSuccess) e = launch_kb<SVDQ_MXFP4_G32>(*layer, ws, W, M, Y, st);
+  } else if (layer->fmt == SVDQ_W8A8) {
+    e = launch_ka<SVDQ_W8A8>(*layer, X, M, ws, W, st);
+    if (e == hipSuccess) e = launch_kb<SVDQ_W8A8>(*layer, ws, W, M, Y, st);
+  } else {
+    e = launch_ka<SVDQ_INT4_G64>(*layer, X, M, ws, W, st);
+    if (e == hipSuccess) e = launch_kb<SVDQ_INT4_G64>(*layer, ws, W, M, Y, st);
+  }
+  return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_DEVICE;
 }
 
 svdq_status svdq_linear_forward_unfused(const svdq_layer* layer, const uint16_t* X, int32_t M, uint16_t* Y,

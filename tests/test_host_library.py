@@ -460,3 +460,19 @@ def test_binding_rejects_unusable_tensors_before_the_library(monkeypatch):
         BD.gemm_lora_up(lay, ws, 8, torch.zeros((8, 64), dtype=torch.int16))
     with pytest.raises(BD.SvdqError, match="GPU memory"):
         BD.gemm_lora_up(lay, ws, 8, Y)
+
+
+def test_noalloc_forward_rejects_oversize_before_any_device_call():
+    """svdq_linear_forward_noalloc validates the layer and the workspace
+    size against its fixed maximum before it touches the device, so the
+    rejections below return on a machine without a GPU (the pointers are
+    never dereferenced)."""
+    lib = B.lib()
+    L = B.binding.Layer(3072, 12288, 32, B.MXFP4, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, None)
+    M = 40000
+    assert B.workspace_bytes(M, 3072, 32, "mxfp4") > B.NOALLOC_MAX_WORKSPACE
+    assert lib.svdq_linear_forward_noalloc(C.byref(L), C.c_void_p(0x2000), M, C.c_void_p(0x3000), None) == 5
+    assert lib.svdq_linear_forward_noalloc(C.byref(L), None, 16, C.c_void_p(0x3000), None) == 1
+    assert lib.svdq_linear_forward_noalloc(C.byref(L), C.c_void_p(0x2008), 16, C.c_void_p(0x3000), None) == 3
+    L.rank = 20
+    assert lib.svdq_linear_forward_noalloc(C.byref(L), C.c_void_p(0x2000), 16, C.c_void_p(0x3000), None) == 2
