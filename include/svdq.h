@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define SVDQ_ABI_VERSION 6   /* 6: the search reports the winner's kept residual iteration */
+#define SVDQ_ABI_VERSION 7   /* 7: INT4 codes travel as FP6 E2M3 values (main parts + tails) */
 #define SVDQ_MAX_RANK 128   /* msModelSlim doc, svd_res: rank not above 128 recommended */
 
 typedef enum svdq_status {
@@ -93,27 +93,34 @@ typedef struct svdq_sizes {
 /* Byte sizes of the kernel-layout and canonical buffers of a layer.
  * Errors: SVDQ_ERR_ARG (out NULL), SVDQ_ERR_SHAPE, SVDQ_ERR_UNSUPPORTED (fmt).
  *
- * Kernel layouts (K in steps of 128 elements = 64 code bytes per row; the
- * byte order of a row-step is canonical for MXFP4, and for INT4 element k
- * of the step sits at byte 16 ((k % 64) / 16) + 8 (k / 64) + (k % 16) / 2,
- * nibble k % 2):
- *   codes   1 KB units of 16 rows x one step, ordered [row / 16][step];
+ * Kernel layouts (K in steps of 128 elements):
+ *   MXFP4 codes: 64 bytes per row-step in canonical byte order, in 1 KB
+ *           units of 16 rows x one step, ordered [row / 16][step];
  *           16-byte slot 4 (row % 16) + q of a unit holds chunk
  *           q ^ (((r >> 1) & 1) | ((r >> 2) & 2)) of the row-step, r = row;
  *           rows are padded to a multiple of 16
- *   scale records (MXFP4 weights and both formats' activations): 16 bytes
- *           per row and 4 steps (4 dwords), in 1 KB units of 64 rows
- *           ordered [row / 64][4-step group]; dword d of row r at unit
- *           dword 64 (r % 64 / 16) + 16 d + r % 16; MXFP4 weight rows are
- *           first permuted inside each 64-row block, row 32 p + 8 j + 4 h +
- *           i (i, j < 4, h < 2) taking the place of row 16 (2 p + h) + 4 j + i;
- *           MXFP4: block b = 4t + g (32 elements) at record byte 4 g + t % 4;
- *           INT4: the fp16 scales of step t (groups 2t, 2t+1) at record
- *           bytes 4 (t % 4) and 4 (t % 4) + 2
- *   INT4 weight scales: 2 KB units of 128 rows x 4 steps ordered
- *           [row / 128][4-step group]; inside a unit fp16 index
- *           32 ((row % 128) / 4) + 8 (t % 4) + 2 (row % 4) + (group of the step)
- *   W8A8: codes in the same 1 KB units with 64 elements per step (byte b
+ *   MXFP4 scale records (weights and activations): 16 bytes per row and 4
+ *           steps (4 dwords), in 1 KB units of 64 rows ordered
+ *           [row / 64][4-step group]; dword d of row r at unit dword
+ *           64 (r % 64 / 16) + 16 d + r % 16; weight rows are first permuted
+ *           inside each 64-row block, row 32 p + 8 j + 4 h + i (i, j < 4,
+ *           h < 2) taking the place of row 16 (2 p + h) + 4 j + i; block
+ *           b = 4t + g (32 elements) at record byte 4 g + t % 4
+ *   INT4 codes: each code q (-7..7) is the FP6 E2M3 value q (sign bit 5,
+ *           exponent bits 3-4 biased by 1, mantissa bits 0-2; exact for
+ *           these integers), the operand type of the scaled 32x32x64 MFMA.
+ *           A row-step holds 4 slices s = 2 G + h (elements 64 G + 32 h ..
+ *           +32), each 32 six-bit codes packed in 6 dwords (element j at
+ *           bits 6 j).  Dwords 0-3 of every slice (the main part) are stored
+ *           in 1 KB units of 16 rows x one step ordered [row / 16][step],
+ *           slot 4 (row % 16) + (s ^ ((row >> 2) & 3)); dwords 4-5 (the
+ *           tail) follow all main parts, in 1 KB units of 32 rows x one step
+ *           ordered [row / 32][step], at unit byte 256 s + 8 (row % 32)
+ *   INT4 scales: 512-byte units of 128 rows x one step ordered
+ *           [row / 128][step]; activations: dword row % 128 holds the fp16
+ *           scales of the step's groups 2t (low half) and 2t + 1; weights:
+ *           fp16 index 128 G + row % 128 holds group 2t + G
+ *   W8A8: codes in the MXFP4 code layout with 64 elements per step (byte b
  *           of step t is element 64 t + b, canonical order), so a row has
  *           K/64 steps; weight scales are the canonical fp32 [N]
  * Padding rows, steps and records hold zero codes, scale 127 (MXFP4) or 0 (INT4). */
@@ -123,11 +130,12 @@ svdq_status svdq_layer_sizes(int32_t K, int32_t N, int32_t rank, int32_t fmt, sv
 
 /* Per-call device workspace.  Regions, each 256-byte aligned:
  *   xq   activation codes in the codes layout above (rows padded to 16;
- *        ceil(M/16) * 16 * K/2 bytes, K bytes per row for W8A8; padding
- *        rows are not written)
- *   xs   activation scale records in the scale-record layout above
- *        (ceil(M/64) * 64 * ceil(K/512) * 16 bytes); W8A8: fp32 [M] per
- *        token scales (ceil(M/16) * 64 bytes)
+ *        ceil(M/16) * 16 * K/2 bytes, K bytes per row for W8A8; INT4: the
+ *        main parts, ceil(M/16) * 16 * K/2 bytes, then the tails,
+ *        ceil(M/32) * 32 * K/4 bytes; padding rows are not written)
+ *   xs   activation scales: MXFP4 scale records (ceil(M/64) * 64 *
+ *        ceil(K/512) * 16 bytes); INT4 scale units (ceil(M/128) * K/128 *
+ *        512 bytes); W8A8 fp32 [M] per token scales (ceil(M/16) * 64 bytes)
  *   z    down projection Z: per row and 32-column chunk of the rank
  *        (rounded up to 32), 32 bf16 values hi then 32 bf16 values lo with
  *        hi + lo = Z to about 2^-17 relative (M * rank_pad * 4 bytes)

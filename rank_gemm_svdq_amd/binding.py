@@ -104,7 +104,7 @@ class SearchResult(C.Structure):
 
 
 _lib = None
-ABI_VERSION = 6   # SVDQ_ABI_VERSION of include/svdq.h that these structures mirror
+ABI_VERSION = 7   # SVDQ_ABI_VERSION of include/svdq.h that these structures mirror
 
 
 def lib():

@@ -58,6 +58,8 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v6i __attribute__((ext_vector_type(6)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -108,6 +110,7 @@ __global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __res
   const bool live = row < M;
   const int steps = K / 128;
   const int ks4 = (steps + 3) / 4;
+  const size_t i4_tail = code_bytes(M, steps);   // INT4: the code tails follow the main parts
   const int spw = (steps + KA_WAVES - 1) / KA_WAVES;
   const int t0 = wave * spw;
   const int t1 = min(steps, t0 + spw);
@@ -219,26 +222,27 @@ __global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __res
       _Float16 s16 = (_Float16)s32;
       if (s32 >= 65520.0f) s16 = (_Float16)65504.0f;
       const float sf = (float)s16;
-      uint32_t d[4] = {0u, 0u, 0u, 0u};
-      if (sf != 0.f) {
-        const float rcp = 1.0f / sf;
+      // codes -7..7 as floats, then FP6 E2M3 (exact for them): the
+      // convert takes two 16-value operands and interleaves them, so the
+      // even elements go in the first and the odd in the second to give
+      // the dense order (element j at bits 6 j) the MFMA reads
+      v16f qa, qb;
+      const float rcp = sf != 0.f ? 1.0f / sf : 0.f;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          float q = __builtin_rintf(xh[i] * rcp);
-          q = fminf(fmaxf(q, -7.f), 7.f);
-          d[i >> 3] |= ((uint32_t)(int)q & 0xFu) << (4 * (i & 7));
-        }
+      for (int j = 0; j < 16; ++j) {
+        qa[j] = sf != 0.f ? fminf(fmaxf(__builtin_rintf(xh[2 * j] * rcp), -7.f), 7.f) : 0.f;
+        qb[j] = sf != 0.f ? fminf(fmaxf(__builtin_rintf(xh[2 * j + 1] * rcp), -7.f), 7.f) : 0.f;
       }
+      const v6i d = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(qa, qb, 1.0f);
       if (live) {
-        // bytes 32 half + 8 G + (0..7) and the same + 16 of the step (the
-        // INT4 step permutation), each inside one 16-byte chunk
-        const int G = g >> 1, half = g & 1;
-        *reinterpret_cast<uint2*>(xq + code_offset(row, t, 32 * half + 8 * G, steps)) = make_uint2(d[0], d[1]);
-        *reinterpret_cast<uint2*>(xq + code_offset(row, t, 32 * half + 16 + 8 * G, steps)) = make_uint2(d[2], d[3]);
-        if (half == 0) {
+        // slice g of the step: dwords 0-3 to the main part, 4-5 to the tail
+        *reinterpret_cast<v4i*>(xq + i4_main_offset(row, t, g, steps)) = (v4i){d[0], d[1], d[2], d[3]};
+        *reinterpret_cast<uint2*>(xq + i4_tail + i4_tail_offset(row, t, g, steps)) =
+            make_uint2((uint32_t)d[4], (uint32_t)d[5]);
+        if ((g & 1) == 0) {
           uint16_t sb;
           __builtin_memcpy(&sb, &s16, 2);
-          *reinterpret_cast<uint16_t*>(xs + scale_record_offset(row, t >> 2, 4 * (t & 3) + 2 * G, ks4)) = sb;
+          *reinterpret_cast<uint16_t*>(xs + i4_xscale_offset(row, t, g >> 1, steps)) = sb;
         }
       }
     }
@@ -892,53 +896,54 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
 //
 // 128 (tokens) x 128 (out-features) per block of 4 waves, three blocks per
 // compute unit, so each SIMD runs three waves of different blocks: one
-// block's barrier or load wait is covered by the others' VALU work, and
-// the tile count of a layer splits evenly over the compute units more
-// often than with larger tiles.  Wave w owns tokens 64 (w & 1) .. +64 and
-// out-features 64 (w >> 1) .. +64, i.e. 4 x 4 MFMA tiles of 16 x 16 (64
-// fp32 accumulators per lane).  Codes travel global -> LDS by direct-to-LDS
-// loads into a ring of two 16 KB step buffers, one step ahead; the scale
-// records of 4 steps (token rows: one dword per step; weights: 4 rows x one
-// dword per step, 64 bytes per 4-row block) are double buffered the same
-// way.
+// block's barrier or load wait is covered by the others' VALU work.  Wave w
+// owns tokens 64 (w & 1) .. +64 and out-features 64 (w >> 1) .. +64, i.e.
+// 2 x 2 MFMA tiles of 32 x 32 (64 fp32 accumulators per lane).
 //
-// Each 16-byte fragment holds 16 codes of each of the step's two 64-element
-// groups.  Nibbles become bytes 16 q, the int8 MFMA operand, so one MFMA per
-// group gives 2^8 times the exact integer dot product I; the accumulator
-// takes float(I) * (sx * sw), the fp16 scale product formed exactly in fp32,
-// and the 2^8 is removed once after the K loop.
+// The codes are FP6 E2M3 values (INT4 -7..7 exactly), the operands of the
+// scaled 32x32x64 MFMA (unit E8M0 scales), whose K extent is one 64-element
+// group: one MFMA gives the group's exact integer dot product I as fp32, and
+// the accumulator takes I * (sx * sw), the fp16 scale product formed exactly
+// in fp32 by one mixed-precision FMA.  Two VALU operations per output and
+// group: the per-group fp16 scales are not powers of two, so they cannot
+// ride in the MFMA's block scales.
 //
-// After the K loop the two step buffers take the low-rank chunks (Z and
-// L2'); weight rows are permuted inside tile pairs as in the MXFP4 kernel
-// for 16-byte stores.
+// Each step (128 elements = 2 groups) travels global -> LDS by direct-to-LDS
+// loads into a ring of two 25 KB step buffers, one step ahead: the code main
+// parts (16 + 16 units of 1 KB), the code tails (4 + 4 units) and the
+// step's scales (512 B of token rows, 512 B of weight rows).
+//
+// Weight rows are read in a permuted order inside each 32-row tile: MFMA row
+// q holds out-feature i4_nrow(q), so the 16 accumulators a lane holds for a
+// tile are 16 consecutive out-features of one token (two 16-byte stores).
 
 constexpr int I4_BM = 128, I4_BN = 128, I4_WAVES = 4, I4_THREADS = 64 * I4_WAVES;
-constexpr int I4_STEP_BYTES = (I4_BM + I4_BN) * 64;   // codes of one step, both operands
-constexpr int I4_NBUF = 2;
-constexpr int I4_SC_BYTES = (I4_BM + I4_BN) * 16;     // scale records of one 4-step group
-constexpr int I4_SC0 = I4_NBUF * I4_STEP_BYTES;
-constexpr int I4_LDS = I4_SC0 + 2 * I4_SC_BYTES;
-// after the K loop the step buffers hold a low-rank chunk: Z (128 rows x 32
-// fp32) in buffer 0, L2' (128 rows x 32 bf16) in buffer 1
+// step buffer: token main | weight main | token tails | weight tails | token scales | weight scales
+constexpr int I4_BMAIN = 0, I4_AMAIN = 8192, I4_BTAIL = 16384, I4_ATAIL = 20480, I4_BSC = 24576, I4_ASC = 25088;
+constexpr int I4_STEP_BYTES = 25600;
+constexpr int I4_LDS = 2 * I4_STEP_BYTES;
+// after the K loop: Z (128 rows x 32 hi + 32 lo bf16) in buffer 0, L2' (128 rows x 32 bf16) in buffer 1
 constexpr int I4_Z0 = 0, I4_L20 = I4_STEP_BYTES;
 
-// product of the fp16 halves G of a and b, formed exactly in fp32 by one
-// mixed-precision FMA (the fp16 inputs are widened inside it, addend 0)
-template <int G>
-__device__ __forceinline__ float f16_product(uint32_t a, uint32_t b) {
+// out-feature (within a 32-row tile) of MFMA row q: the 32x32 result puts
+// rows 8 a + 4 h + b (a, b < 4) in lane half h, register 4 a + b, so out-feature
+// 16 h + 4 a + b makes register i of a lane out-feature 16 h + i
+__device__ __forceinline__ int i4_nrow(int q) { return 16 * ((q >> 2) & 1) + 4 * (q >> 3) + (q & 3); }
+
+// exact product of fp16 half HA of a and half HB of b in fp32 (one
+// mixed-precision FMA, addend 0)
+template <int HA, int HB>
+__device__ __forceinline__ float f16_mul(uint32_t a, uint32_t b) {
   float d;
-  if constexpr (G == 0)
+  if constexpr (HA == 0 && HB == 0)
     asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,1,0]" : "=v"(d) : "v"(a), "v"(b));
+  else if constexpr (HA == 0 && HB == 1)
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[1,1,0]" : "=v"(d) : "v"(a), "v"(b));
+  else if constexpr (HA == 1 && HB == 0)
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,1,0]" : "=v"(d) : "v"(a), "v"(b));
   else
     asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[1,1,0] op_sel_hi:[1,1,0]" : "=v"(d) : "v"(a), "v"(b));
   return d;
-}
-
-// int8 MFMA operand of group G from a 16-byte INT4 fragment: bytes 16 q
-__device__ __forceinline__ v4i i4_unpack(const v4i f, int G) {
-  const uint32_t MSK = 0xF0F0F0F0u;
-  const uint32_t d0 = (uint32_t)f[2 * G], d1 = (uint32_t)f[2 * G + 1];
-  return (v4i){(int)((d0 << 4) & MSK), (int)(d0 & MSK), (int)((d1 << 4) & MSK), (int)(d1 & MSK)};
 }
 
 template <int NTR>
@@ -951,47 +956,58 @@ __global__ __launch_bounds__(I4_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
-  const int l16 = lane & 15, g = lane >> 4;
+  const int l32 = lane & 31, h = lane >> 5;
   const int tiles_m = (M + I4_BM - 1) / I4_BM, tiles_n = (N + I4_BN - 1) / I4_BN;
   int tm, tn;
   mx_tile_of(blockIdx.x, tiles_m, tiles_n, &tm, &tn);
   const int tile_m = tm * I4_BM, tile_n = tn * I4_BN;
   const int steps = K / 128;
-  const int ks4 = (steps + 3) / 4;
   const int m_base = tile_m + 64 * wm, n_base = tile_n + 64 * wn;
 
-  // ---- DMA plan.  Codes: 16 contiguous 1 KB units per step (units 0-7:
-  // token row groups, 8-15: weight row groups); wave w moves units 4w ..
-  // 4w+3, lane i 16 bytes.  Units past the last row group repeat it.
-  const bool tokw = wave < 2;
-  const uint8_t* cbase = tokw ? xq : wq;
-  uint32_t coff[4];
+  // ---- DMA plan.  24 code units of 1 KB per step (0-7 token main row
+  // groups of 16, 8-15 weight main, 16-19 token tails of 32 rows, 20-23
+  // weight tails); wave w moves units 6 w .. 6 w + 5, lane i 16 bytes.  Row
+  // groups past the last repeat it (their outputs are never stored).
+  // Consecutive steps of a row group are 1 KB apart in every part.
+  const uint8_t* xtail = xq + code_bytes(M, steps);
+  const uint8_t* wtail = wq + code_bytes(N, steps);
+  const uint8_t* ubase[6];
+  uint32_t udst[6];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int u = 4 * (wave & 1) + j;
-    const int grp16 = tokw ? min((tile_m >> 4) + u, (M + 15) / 16 - 1) : min((tile_n >> 4) + u, N / 16 - 1);
-    coff[j] = (uint32_t)grp16 * (uint32_t)steps * 1024u + 16u * lane;
+  for (int j = 0; j < 6; ++j) {
+    const int u = 6 * wave + j;
+    const uint8_t* b;
+    uint32_t dst;
+    if (u < 8) {
+      b = xq + (size_t)min((tile_m >> 4) + u, (M + 15) / 16 - 1) * steps * 1024;
+      dst = I4_BMAIN + 1024u * u;
+    } else if (u < 16) {
+      b = wq + (size_t)min((tile_n >> 4) + u - 8, N / 16 - 1) * steps * 1024;
+      dst = I4_AMAIN + 1024u * (u - 8);
+    } else if (u < 20) {
+      b = xtail + (size_t)min((tile_m >> 5) + u - 16, (M + 31) / 32 - 1) * steps * 1024;
+      dst = I4_BTAIL + 1024u * (u - 16);
+    } else {
+      b = wtail + (size_t)min((tile_n >> 5) + u - 20, (N + 31) / 32 - 1) * steps * 1024;
+      dst = I4_ATAIL + 1024u * (u - 20);
+    }
+    ubase[j] = b;
+    udst[j] = dst;
   }
-  // Scales of 4-step group grp: waves 0-1 move the 1 KB records of token
-  // rows 64 w .., waves 2-3 the two halves of the 2 KB weight-scale unit of
-  // the block's 128 out-features (32 blocks of 4 rows x 4 steps).
-  const uint8_t* sbase = tokw ? xs : ws;
-  uint32_t soff, sstride;
-  if (tokw) {
-    soff = (uint32_t)min((tile_m >> 6) + wave, (M + 63) / 64 - 1) * (uint32_t)ks4 * 1024u + 16u * lane;
-    sstride = 1024;
-  } else {
-    soff = (uint32_t)(tile_n >> 7) * (uint32_t)ks4 * 2048u + 1024u * (uint32_t)(wave & 1) + 16u * lane;
-    sstride = 2048;
-  }
-  auto issue_codes = [&](int t) __attribute__((always_inline)) {
-    const uint32_t b = lds_u32 + (uint32_t)(t % I4_NBUF) * I4_STEP_BYTES + (uint32_t)wave * 4096u;
+  // the step's scales: 512 B of token rows (lanes 0-31) and 512 B of weight
+  // rows (lanes 32-63), both moved by wave 0
+  const uint8_t* sx_base = xs + (size_t)tm * steps * 512;
+  const uint8_t* sw_base = ws + (size_t)tn * steps * 512;
+  auto issue_step = [&](int t) __attribute__((always_inline)) {
+    const uint32_t b = lds_u32 + (uint32_t)(t & 1) * I4_STEP_BYTES;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(cbase + (size_t)t * 1024, coff[j], b + 1024u * j);
-  };
-  auto issue_scales = [&](int grp) __attribute__((always_inline)) {
-    dma16(sbase + (size_t)grp * sstride, soff,
-          lds_u32 + I4_SC0 + (uint32_t)(grp & 1) * I4_SC_BYTES + (uint32_t)wave * 1024u);
+    for (int j = 0; j < 6; ++j) dma16(ubase[j] + (size_t)t * 1024, 16u * lane, b + udst[j]);
+    if (wave == 0) {
+      if (lane < 32)
+        dma16(sx_base + (size_t)t * 512, 16u * lane, b + I4_BSC);
+      else
+        dma16(sw_base + (size_t)t * 512, 16u * (lane - 32), b + I4_BSC);
+    }
   };
   // Z (128 rows x 128 B, 16 units of 8 rows) and L2' (128 rows x 64 B, 8
   // units of 16 rows) chunk u into step buffers 0 and 1
@@ -1014,154 +1030,147 @@ __global__ __launch_bounds__(I4_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
     }
   };
 
-  // fragment addresses inside a step buffer: token fragment q reads row
-  // 64 wm + 16 q + l16 (the swizzle repeats every 32 rows), weight fragment
-  // nt the permuted row 64 wn + mx_nrow(nt, l16)
-  uint32_t boff[2], aoff[4];
+  // fragment offsets inside a step buffer, per tile and group G: the main
+  // part of slice 2 G + h of the row, and its tail
+  uint32_t amain[2][2], atail[2], bmain[2][2], btail[2];
 #pragma unroll
-  for (int par = 0; par < 2; ++par) boff[par] = (uint32_t)swz(64 * wm + 16 * par + l16, g) - 1024u * par;
+  for (int i = 0; i < 2; ++i) {
+    const int ra = 64 * wn + 32 * i + i4_nrow(l32), rb = 64 * wm + 32 * i + l32;
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) aoff[nt] = (uint32_t)(I4_BM * 64 + swz(64 * wn + mx_nrow(nt, l16), g));
+    for (int G = 0; G < 2; ++G) {
+      amain[i][G] = I4_AMAIN + 64 * ra + 16 * ((2 * G + h) ^ i4_swz(ra));
+      bmain[i][G] = I4_BMAIN + 64 * rb + 16 * ((2 * G + h) ^ i4_swz(rb));
+    }
+    atail[i] = I4_ATAIL + 1024 * (ra >> 5) + 256 * h + 8 * (ra & 31);
+    btail[i] = I4_BTAIL + 1024 * (rb >> 5) + 256 * h + 8 * (rb & 31);
+  }
   auto buf_of = [&](int t) __attribute__((always_inline)) -> uint32_t {
-    uint32_t bo = (uint32_t)(t % I4_NBUF) * I4_STEP_BYTES;
+    uint32_t bo = (uint32_t)(t & 1) * I4_STEP_BYTES;
     asm volatile("" : "+s"(bo));
     return bo;
   };
-  auto read_b = [&](uint32_t bo, int q) __attribute__((always_inline)) -> v4i {
-    return *reinterpret_cast<const v4i*>(lds + bo + boff[q & 1] + 1024 * q);
-  };
-  auto read_a = [&](uint32_t bo, int nt) __attribute__((always_inline)) -> v4i {
-    return *reinterpret_cast<const v4i*>(lds + bo + aoff[nt]);
-  };
-  // scales of step t: token row dword (groups 2t, 2t+1) per mt; 4 weight
-  // rows x dword per nt (the lane's 4 consecutive out-features)
-  uint32_t sx[4];
-  v4i sw[4];
-  auto read_scales = [&](int t) __attribute__((always_inline)) {
-    uint32_t so = (uint32_t)(I4_SC0 + ((t >> 2) & 1) * I4_SC_BYTES);
-    asm volatile("" : "+s"(so));
-    const uint8_t* sc = lds + so;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-      sx[mt] = *reinterpret_cast<const uint32_t*>(sc + 1024 * wm + 4 * (64 * mt + 16 * (t & 3) + l16));
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int blk = 16 * wn + 8 * (nt >> 1) + 2 * g + (nt & 1);
-      sw[nt] = *reinterpret_cast<const v4i*>(sc + I4_BM * 16 + blk * 64 + 16 * (t & 3));
-    }
+  auto frag = [&](uint32_t bo, uint32_t mo, uint32_t to) __attribute__((always_inline)) -> v8i {
+    const v4i m4 = *reinterpret_cast<const v4i*>(lds + bo + mo);
+    const uint2 t2 = *reinterpret_cast<const uint2*>(lds + bo + to);
+    return (v8i){m4[0], m4[1], m4[2], m4[3], (int)t2.x, (int)t2.y, 0, 0};
   };
 
-  // Ring of two step buffers: the top of step t waits for step t's loads
-  // and a barrier, after which step t-1's buffer (every wave is past it)
-  // receives step t+1; steps 0 and 1 are issued before the loop.
-  issue_scales(0);
-  issue_codes(0);
-  if (steps > 1) issue_codes(1);
-
-  v4f acc[4][4];   // [weight tile][token tile]
+  issue_step(0);
+  v16f acc[2][2];   // [weight tile][token tile]
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
+  for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[nt][mt] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[nt][mt][i] = 0.f;
 
   for (int t = 0; t < steps; ++t) {
-    if (t == 0 && steps > 1)
-      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // step t has landed; every wave is past step t - 1, whose buffer now
+    // receives step t + 1
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (t >= 1 && t + 1 < steps) issue_codes(t + 1);
-    if ((t & 3) == 0 && (t >> 2) + 1 < ks4) issue_scales((t >> 2) + 1);
-    read_scales(t);
-    const uint32_t bc = buf_of(t);
-    v4i wu[4][2], tk[4];
+    if (t + 1 < steps) issue_step(t + 1);
+    const uint32_t bo = buf_of(t);
+    // token scales: the fp16 pair (group 0, group 1) of the lane's token per tile
+    uint32_t sx[2];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const v4i wp = read_a(bc, nt);
-      wu[nt][0] = i4_unpack(wp, 0);
-      wu[nt][1] = i4_unpack(wp, 1);
-    }
+    for (int mt = 0; mt < 2; ++mt)
+      sx[mt] = *reinterpret_cast<const uint32_t*>(lds + bo + I4_BSC + 4 * (64 * wm + 32 * mt + l32));
 #pragma unroll
-    for (int q = 0; q < 4; ++q) tk[q] = read_b(bc, q);
+    for (int G = 0; G < 2; ++G) {
+      v8i af[2], bf[2];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-      for (int G = 0; G < 2; ++G) {
-        // the group's 4 MFMAs first, then their scaling
-        const v4i b8 = i4_unpack(tk[mt], G);
-        v4i I[4];
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          I[nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wu[nt][G], b8, (v4i){0, 0, 0, 0}, 0, 0, 0);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p = G == 0 ? f16_product<0>(sx[mt], (uint32_t)sw[nt][i])
-                                   : f16_product<1>(sx[mt], (uint32_t)sw[nt][i]);
-            acc[nt][mt][i] = __builtin_fmaf((float)I[nt][i], p, acc[nt][mt][i]);
-          }
+      for (int i = 0; i < 2; ++i) {
+        af[i] = frag(bo, amain[i][G], atail[i] + 512 * G);
+        bf[i] = frag(bo, bmain[i][G], btail[i] + 512 * G);
       }
+      // weight scales of group G: the lane's 16 consecutive out-features per tile
+      v4i sw[2][2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          sw[nt][c] = *reinterpret_cast<const v4i*>(lds + bo + I4_ASC + 256 * G + 2 * (64 * wn + 32 * nt + 16 * h) +
+                                                    16 * c);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const v16f I = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[nt], bf[mt], (v16f){}, 2, 2, 0, 127, 0,
+                                                                          127);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const uint32_t w2 = (uint32_t)sw[nt][i >> 3][(i >> 1) & 3];
+            const float p = G == 0 ? ((i & 1) ? f16_mul<0, 1>(sx[mt], w2) : f16_mul<0, 0>(sx[mt], w2))
+                                   : ((i & 1) ? f16_mul<1, 1>(sx[mt], w2) : f16_mul<1, 0>(sx[mt], w2));
+            acc[nt][mt][i] = __builtin_fmaf(I[i], p, acc[nt][mt][i]);
+          }
+        }
     }
   }
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[nt][mt][i] *= 1.0f / 256.0f;
 
-  // ---- low-rank up projection and bias, then one 16-byte store per pair
+  // ---- low-rank up projection and bias, then two 16-byte stores per tile
   if constexpr (NTR > 0) {
     for (int u = 0; u < NTR; ++u) {
       __syncthreads();   // every wave is done with the step buffers (or chunk u-1)
       issue_lowrank(u);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      v8bf bh[4], bl[4];
+      // bf16 32x32x16 MFMAs: lane l supplies row l % 32 and the 8 values
+      // k = 16 j + 8 (l / 32) .. +8 of the chunk's K half j; Z as hi and lo
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int zrow = 64 * wm + 16 * mt + l16;
-        bh[mt] = *reinterpret_cast<const v8bf*>(lds + I4_Z0 + zrow * 128 + 16 * (g ^ zswz(zrow)));
-        bl[mt] = *reinterpret_cast<const v8bf*>(lds + I4_Z0 + zrow * 128 + 16 * ((4 + g) ^ zswz(zrow)));
-      }
+      for (int j = 0; j < 2; ++j) {
+        const int c = 2 * j + h;
+        v8bf zh[2], zl[2];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int lrow = 64 * wn + mx_nrow(nt, l16);
-        const v8bf af = *reinterpret_cast<const v8bf*>(lds + I4_L20 + lrow * 64 + 16 * (g ^ lswz(lrow)));
+        for (int mt = 0; mt < 2; ++mt) {
+          const int zrow = 64 * wm + 32 * mt + l32;
+          zh[mt] = *reinterpret_cast<const v8bf*>(lds + I4_Z0 + zrow * 128 + 16 * (c ^ zswz(zrow)));
+          zl[mt] = *reinterpret_cast<const v8bf*>(lds + I4_Z0 + zrow * 128 + 16 * ((4 + c) ^ zswz(zrow)));
+        }
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bh[mt], acc[nt][mt], 0, 0, 0);
-          acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bl[mt], acc[nt][mt], 0, 0, 0);
+        for (int nt = 0; nt < 2; ++nt) {
+          const int lrow = 64 * wn + 32 * nt + i4_nrow(l32);
+          const v8bf lf = *reinterpret_cast<const v8bf*>(lds + I4_L20 + lrow * 64 + 16 * (c ^ lswz(lrow)));
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) {
+            acc[nt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lf, zh[mt], acc[nt][mt], 0, 0, 0);
+            acc[nt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lf, zl[mt], acc[nt][mt], 0, 0, 0);
+          }
         }
       }
     }
   }
 #pragma unroll
-  for (int p2 = 0; p2 < 2; ++p2) {
-    const int n0 = n_base + 32 * p2 + 8 * g;
-    float bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (bias != nullptr && n0 < N) {
-      const v4i braw = *reinterpret_cast<const v4i*>(bias + n0);
+  for (int nt = 0; nt < 2; ++nt) {
+    const int n0 = n_base + 32 * nt + 16 * h;
+    float bv[16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        bv[2 * i] = bf16_lo((uint32_t)braw[i]);
-        bv[2 * i + 1] = bf16_hi((uint32_t)braw[i]);
+    for (int i = 0; i < 16; ++i) bv[i] = 0.f;
+    if (bias != nullptr && n0 < N) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const v4i braw = *reinterpret_cast<const v4i*>(bias + n0 + 8 * c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          bv[8 * c + 2 * i] = bf16_lo((uint32_t)braw[i]);
+          bv[8 * c + 2 * i + 1] = bf16_hi((uint32_t)braw[i]);
+        }
       }
     }
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int m = m_base + 16 * mt + l16;
+    for (int mt = 0; mt < 2; ++mt) {
+      const int m = m_base + 32 * mt + l32;
       if (m >= M || n0 >= N) continue;
-      v4i o;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        o[i] = (int)(bf16_rne(acc[2 * p2][mt][2 * i] + bv[2 * i]) |
-                     (bf16_rne(acc[2 * p2][mt][2 * i + 1] + bv[2 * i + 1]) << 16));
-        o[2 + i] = (int)(bf16_rne(acc[2 * p2 + 1][mt][2 * i] + bv[4 + 2 * i]) |
-                         (bf16_rne(acc[2 * p2 + 1][mt][2 * i + 1] + bv[4 + 2 * i + 1]) << 16));
+      for (int c = 0; c < 2; ++c) {
+        v4i o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          o[i] = (int)(bf16_rne(acc[nt][mt][8 * c + 2 * i] + bv[8 * c + 2 * i]) |
+                       (bf16_rne(acc[nt][mt][8 * c + 2 * i + 1] + bv[8 * c + 2 * i + 1]) << 16));
+        *reinterpret_cast<v4i*>(Y + (size_t)m * N + n0 + 8 * c) = o;
       }
-      *reinterpret_cast<v4i*>(Y + (size_t)m * N + n0) = o;
     }
   }
 }

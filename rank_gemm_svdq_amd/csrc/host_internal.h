@@ -34,6 +34,7 @@ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 struct Geometry {
   int32_t K, N, rank, rpad, fmt, steps, ks4, csteps;   // csteps: 64-byte code steps per row
   size_t wq_bytes, ws_bytes, l1k_bytes, l2k_bytes;
+  size_t wq_tail_off;                                  // INT4: start of the code tails inside wq
 };
 bool geometry(int32_t K, int32_t N, int32_t rank, int32_t fmt, Geometry* g);
 bool valid_kn(int32_t K, int32_t N);
@@ -41,10 +42,37 @@ bool valid_rank(int32_t rank);
 bool valid_fmt(int32_t fmt);
 int32_t choose_zsplit(int32_t M, int32_t K);
 
-// Byte position of canonical element k (0..127) inside a 64-byte INT4 step.
-inline int int4_step_byte(int k) {
-  const int G = k >> 6, r = k & 63, g = r >> 4, j = r & 15;
-  return 16 * g + 8 * G + (j >> 1);
+// INT4 codes on the device: 32 six-bit FP6 codes of a slice packed into 6
+// dwords, element j at bits 6 j, and back.
+inline void pack6(const uint8_t* c32, uint32_t* d6) {
+  for (int i = 0; i < 6; ++i) d6[i] = 0;
+  for (int j = 0; j < 32; ++j) {
+    const int bit = 6 * j;
+    const uint64_t v = (uint64_t)(c32[j] & 63) << (bit & 31);
+    d6[bit >> 5] |= (uint32_t)v;
+    if ((bit & 31) + 6 > 32) d6[(bit >> 5) + 1] |= (uint32_t)(v >> 32);
+  }
+}
+inline void unpack6(const uint32_t* d6, uint8_t* c32) {
+  for (int j = 0; j < 32; ++j) {
+    const int bit = 6 * j;
+    uint64_t v = d6[bit >> 5] >> (bit & 31);
+    if ((bit & 31) + 6 > 32) v |= (uint64_t)d6[(bit >> 5) + 1] << (32 - (bit & 31));
+    c32[j] = (uint8_t)(v & 63);
+  }
+}
+// INT4 value of an FP6 E2M3 code the packers write; 8 (an INT4 nibble the
+// quantizers never produce) for any other code.
+struct E2m3Inverse {
+  int8_t q[64];
+  E2m3Inverse() {
+    for (int c = 0; c < 64; ++c) q[c] = c == 0x20 ? 0 : 8;
+    for (int v = -7; v <= 7; ++v) q[e2m3_of_int4(v)] = (int8_t)v;
+  }
+};
+inline int int4_of_e2m3(uint8_t c) {
+  static const E2m3Inverse inv;
+  return inv.q[c & 63];
 }
 
 // Scalar conversions (round to nearest even).

@@ -35,7 +35,9 @@ bool geometry(int32_t K, int32_t N, int32_t rank, int32_t fmt, Geometry* g) {
   g->ks4 = (g->steps + 3) / 4;
   g->csteps = code_steps(K, fmt);
   g->wq_bytes = code_bytes(N, g->csteps);   // N % 16 == 0: exactly the canonical size
-  g->ws_bytes = fmt == SVDQ_INT4_G64   ? int4_wscale_bytes(N, g->ks4)
+  g->wq_tail_off = g->wq_bytes;
+  if (fmt == SVDQ_INT4_G64) g->wq_bytes += i4_tail_bytes(N, g->steps);   // FP6 codes: main parts, then tails
+  g->ws_bytes = fmt == SVDQ_INT4_G64   ? i4_scale_bytes(N, g->steps)
                 : fmt == SVDQ_MXFP4_G32 ? scale_record_bytes(N, g->ks4)
                                         : (size_t)N * 4;
   g->l1k_bytes = (size_t)K * rank * 2;
@@ -262,8 +264,11 @@ svdq_status svdq_workspace_layout(int32_t M, int32_t K, int32_t rank, int32_t fm
   out->zsplit = rank > 0 ? choose_zsplit(M, K) : 0;
   out->xq_off = 0;
   out->xq_bytes = code_bytes(M, code_steps(K, fmt));
+  if (fmt == SVDQ_INT4_G64) out->xq_bytes += i4_tail_bytes(M, steps);   // main parts, then tails
   out->xs_off = align256(out->xq_bytes);
-  out->xs_bytes = is_w8(fmt) ? (size_t)(M + 15) / 16 * 64 : scale_record_bytes(M, ks4);
+  out->xs_bytes = is_w8(fmt)                ? (size_t)(M + 15) / 16 * 64
+                  : fmt == SVDQ_INT4_G64 ? i4_scale_bytes(M, steps)
+                                            : scale_record_bytes(M, ks4);
   out->z_off = align256(out->xs_off + out->xs_bytes);
   out->z_bytes = rank > 0 ? (size_t)out->zsplit * M * rank_pad(rank) * 4 : 0;
   out->total = align256(out->z_off + out->z_bytes);
@@ -609,28 +614,16 @@ svdq_status svdq_kernel_layout(int32_t K, int32_t N, int32_t rank, int32_t fmt, 
         for (int32_t k = 0; k < K; ++k) wq_k[code_offset((int)n, k >> 6, k & 63, cs)] = wq[(size_t)n * K + k];
     });
     std::memcpy(ws_k, ws, (size_t)N * 4);
-  } else {
-  // codes: tiled 1 KB units (INT4 bytes first permuted inside each step)
-  parallel_for(N, default_threads(0), [&](int64_t lo, int64_t hi) {
-    for (int64_t n = lo; n < hi; ++n)
-      for (int32_t t = 0; t < steps; ++t) {
-        const uint8_t* src = wq + (size_t)n * (K / 2) + (size_t)t * 64;
-        if (fmt == SVDQ_MXFP4_G32) {
+  } else if (fmt == SVDQ_MXFP4_G32) {
+    // codes: tiled 1 KB units
+    parallel_for(N, default_threads(0), [&](int64_t lo, int64_t hi) {
+      for (int64_t n = lo; n < hi; ++n)
+        for (int32_t t = 0; t < steps; ++t) {
+          const uint8_t* src = wq + (size_t)n * (K / 2) + (size_t)t * 64;
           for (int b = 0; b < 64; ++b) wq_k[code_offset((int)n, t, b, steps)] = src[b];
-        } else {
-          uint8_t step[64];
-          std::memset(step, 0, 64);
-          for (int k = 0; k < kStep; ++k) {
-            const uint8_t v = (src[k >> 1] >> ((k & 1) * 4)) & 0xF;
-            const int j = (k & 63) & 15;
-            step[int4_step_byte(k)] |= (uint8_t)(v << ((j & 1) * 4));
-          }
-          for (int b = 0; b < 64; ++b) wq_k[code_offset((int)n, t, b, steps)] = step[b];
         }
-      }
-  });
-  // scales
-  if (fmt == SVDQ_MXFP4_G32) {
+    });
+    // scales
     std::memset(ws_k, 127, g.ws_bytes);
     for (int32_t n = 0; n < N; ++n)
       for (int32_t b = 0; b < K / 32; ++b) {
@@ -638,13 +631,32 @@ svdq_status svdq_kernel_layout(int32_t K, int32_t N, int32_t rank, int32_t fmt, 
         ws_k[scale_record_offset(wrec_row(n), t / 4, 4 * gq + t % 4, g.ks4)] = ws[(size_t)n * (K / 32) + b];
       }
   } else {
-    const uint16_t* s = reinterpret_cast<const uint16_t*>(ws);
-    uint16_t* d = reinterpret_cast<uint16_t*>(ws_k);
+    // INT4: FP6 E2M3 codes, per slice dwords 0-3 in the main part and 4-5 in
+    // the tail part (padding rows of the last 32-row tail unit stay zero)
+    std::memset(wq_k, 0, g.wq_bytes);
+    uint8_t* tail = wq_k + g.wq_tail_off;
+    parallel_for(N, default_threads(0), [&](int64_t lo, int64_t hi) {
+      for (int64_t n = lo; n < hi; ++n)
+        for (int32_t t = 0; t < steps; ++t)
+          for (int sl = 0; sl < 4; ++sl) {
+            uint8_t c[32];
+            for (int j = 0; j < 32; ++j) {
+              const int32_t k = t * kStep + 32 * sl + j;
+              const int nib = (wq[(size_t)n * (K / 2) + k / 2] >> ((k & 1) * 4)) & 0xF;
+              c[j] = e2m3_of_int4(nib >= 8 ? nib - 16 : nib);
+            }
+            uint32_t d[6];
+            pack6(c, d);
+            std::memcpy(wq_k + i4_main_offset((int)n, t, sl, steps), d, 16);
+            std::memcpy(tail + i4_tail_offset((int)n, t, sl, steps), d + 4, 8);
+          }
+    });
+    const uint16_t* s16 = reinterpret_cast<const uint16_t*>(ws);
     std::memset(ws_k, 0, g.ws_bytes);
     for (int32_t n = 0; n < N; ++n)
       for (int32_t t = 0; t < steps; ++t)
-        for (int G = 0; G < 2; ++G) d[int4_wscale_index(n, t, G, g.ks4)] = s[(size_t)n * (K / 64) + 2 * t + G];
-  }
+        for (int G = 0; G < 2; ++G)
+          std::memcpy(ws_k + i4_wscale_offset(n, t, G, steps), s16 + (size_t)n * (K / 64) + 2 * t + G, 2);
   }
   if (rank == 0) return SVDQ_OK;
   // down factor: L1' (bf16) in the order of K-A's MFMA B operand,
@@ -683,38 +695,39 @@ svdq_status svdq_unpack_activations(const void* ws_host, int32_t M, int32_t K, i
     for (int32_t m = 0; m < M; ++m)
       for (int32_t k = 0; k < K; ++k) xq[(size_t)m * K + k] = q[code_offset(m, k >> 6, k & 63, cs)];
     std::memcpy(xs, base + L.xs_off, (size_t)M * 4);
-  } else {
-  for (int32_t m = 0; m < M; ++m) {
-    for (int32_t t = 0; t < steps; ++t) {
-      uint8_t src[64];
-      for (int b = 0; b < 64; ++b) src[b] = q[code_offset(m, t, b, steps)];
-      uint8_t* dst = xq + (size_t)m * (K / 2) + (size_t)t * 64;
-      if (fmt == SVDQ_MXFP4_G32) {
-        std::memcpy(dst, src, 64);
-      } else {
-        std::memset(dst, 0, 64);
-        for (int k = 0; k < kStep; ++k) {
-          const int j = (k & 63) & 15;
-          const uint8_t v = (src[int4_step_byte(k)] >> ((j & 1) * 4)) & 0xF;
-          dst[k >> 1] |= (uint8_t)(v << ((k & 1) * 4));
-        }
-      }
-    }
-  }
-  const uint8_t* s = base + L.xs_off;
-  if (fmt == SVDQ_MXFP4_G32) {
+  } else if (fmt == SVDQ_MXFP4_G32) {
+    for (int32_t m = 0; m < M; ++m)
+      for (int32_t t = 0; t < steps; ++t)
+        for (int b = 0; b < 64; ++b) xq[(size_t)m * (K / 2) + (size_t)t * 64 + b] = q[code_offset(m, t, b, steps)];
+    const uint8_t* s = base + L.xs_off;
     for (int32_t m = 0; m < M; ++m)
       for (int32_t b = 0; b < K / 32; ++b) {
         const int32_t t = b / 4, gq = b % 4;
         xs[(size_t)m * (K / 32) + b] = s[scale_record_offset(m, t / 4, 4 * gq + t % 4, ks4)];
       }
   } else {
+    // INT4: FP6 codes back to canonical nibbles
+    const uint8_t* tail = q + code_bytes(M, steps);
+    std::memset(xq, 0, (size_t)M * (K / 2));
+    for (int32_t m = 0; m < M; ++m)
+      for (int32_t t = 0; t < steps; ++t)
+        for (int sl = 0; sl < 4; ++sl) {
+          uint32_t d[6];
+          std::memcpy(d, q + i4_main_offset(m, t, sl, steps), 16);
+          std::memcpy(d + 4, tail + i4_tail_offset(m, t, sl, steps), 8);
+          uint8_t c[32];
+          unpack6(d, c);
+          for (int j = 0; j < 32; ++j) {
+            const int32_t k = t * kStep + 32 * sl + j;
+            xq[(size_t)m * (K / 2) + k / 2] |= (uint8_t)((int4_of_e2m3(c[j]) & 0xF) << ((k & 1) * 4));
+          }
+        }
+    const uint8_t* s = base + L.xs_off;
     uint16_t* xs16 = reinterpret_cast<uint16_t*>(xs);
     for (int32_t m = 0; m < M; ++m)
       for (int32_t t = 0; t < steps; ++t)
         for (int G = 0; G < 2; ++G)
-          std::memcpy(xs16 + (size_t)m * (K / 64) + 2 * t + G, s + scale_record_offset(m, t / 4, 4 * (t % 4) + 2 * G, ks4), 2);
-  }
+          std::memcpy(xs16 + (size_t)m * (K / 64) + 2 * t + G, s + i4_xscale_offset(m, t, G, steps), 2);
   }
   if (z && rank > 0) {
     const int32_t rp = rank_pad(rank);

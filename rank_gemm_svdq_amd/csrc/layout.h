@@ -6,10 +6,9 @@
 // a unit, 16-byte slot p = 4 (row % 16) + q holds chunk q ^ chunk_swz(row)
 // of that row's 64 bytes: the XOR swizzle the GEMM kernels read LDS with.
 //
-// Scale records (16 bytes per row and 4 steps) are stored in 1 KB units of
-// 64 rows, ordered [row / 64][4-step group].  INT4 weight scales are stored
-// in 2 KB units of 128 rows x 4 steps, ordered [row / 128][4-step group];
-// inside a unit [4-row block][step % 4][row % 4][group of 64] fp16.
+// Scale records (16 bytes per row and 4 steps; MXFP4) are stored in 1 KB
+// units of 64 rows, ordered [row / 64][4-step group].  INT4 codes and scales
+// have layouts of their own (below).
 #ifndef SVDQ_LAYOUT_H
 #define SVDQ_LAYOUT_H
 
@@ -56,11 +55,44 @@ SVDQ_HD inline int wrec_row(int row) {
 }
 SVDQ_HD inline size_t scale_record_bytes(int rows, int ks4) { return (size_t)((rows + 63) / 64) * ks4 * 1024; }
 
-// fp16 index of the INT4 weight scale of row n, step t, 64-group G (0, 1) of the step
-SVDQ_HD inline size_t int4_wscale_index(int n, int t, int G, int ks4) {
-  return ((size_t)(n >> 7) * ks4 + (t >> 2)) * 1024 + (size_t)((n & 127) >> 2) * 32 + (t & 3) * 8 + (n & 3) * 2 + G;
+// ---- INT4 on the device.  Codes -7..7 are stored as FP6 E2M3 values (exact
+// for these integers), the operand type of the scaled 32x32x64 MFMA, whose
+// K extent is one 64-element group.  A 128-element step of a row holds four
+// 32-element slices s = 2 G + h (elements 64 G + 32 h .. +32); a slice is 32
+// six-bit codes packed in 6 dwords, element j at bits 6 j.  Dwords 0-3 of
+// slice s ("main") sit in the codes layout above, 16-byte slot
+// 4 (row % 16) + (s ^ i4_swz(row)); dwords 4-5 ("tail") in 1 KB units of 32
+// rows x one step ordered [row / 32][step], at unit byte 256 s + 8 (row % 32).
+//
+// i4_swz(row) = row bits 2-3: the 32x32 MFMA's fragment read (lane l: row
+// l % 32, or its out-feature permutation, at slot 2 G + l / 32) then gives
+// every 16-lane LDS group 16 distinct 16-byte slots.
+SVDQ_HD inline int i4_swz(int row) { return (row >> 2) & 3; }
+SVDQ_HD inline size_t i4_main_offset(int row, int t, int s, int steps) {
+  return ((size_t)(row >> 4) * steps + t) * 1024 + (size_t)(4 * (row & 15) + (s ^ i4_swz(row))) * 16;
 }
-SVDQ_HD inline size_t int4_wscale_bytes(int rows, int ks4) { return (size_t)((rows + 127) / 128) * ks4 * 2048; }
+SVDQ_HD inline size_t i4_tail_offset(int row, int t, int s, int steps) {
+  return ((size_t)(row >> 5) * steps + t) * 1024 + (size_t)256 * s + 8 * (row & 31);
+}
+SVDQ_HD inline size_t i4_tail_bytes(int rows, int steps) { return (size_t)((rows + 31) / 32) * steps * 1024; }
+// INT4 scales: 512-byte units of 128 rows x one step ordered [row / 128][step].
+// Activations: dword row % 128 is the fp16 pair of the step's groups 2t
+// (low half) and 2t + 1; weights: fp16 index 128 G + row % 128.
+SVDQ_HD inline size_t i4_scale_bytes(int rows, int steps) { return (size_t)((rows + 127) / 128) * steps * 512; }
+SVDQ_HD inline size_t i4_xscale_offset(int row, int t, int G, int steps) {
+  return ((size_t)(row >> 7) * steps + t) * 512 + 4 * (row & 127) + 2 * G;
+}
+SVDQ_HD inline size_t i4_wscale_offset(int row, int t, int G, int steps) {
+  return ((size_t)(row >> 7) * steps + t) * 512 + 2 * (128 * G + (row & 127));
+}
+// FP6 E2M3 code of an INT4 value (sign bit 5, exponent bits 3-4 with bias
+// 1, mantissa bits 0-2): 1 = 1.0 x 2^0, 3 = 1.5 x 2^1, 5 = 1.25 x 2^2, ...
+SVDQ_HD inline uint8_t e2m3_of_int4(int q) {
+  const int a = q < 0 ? -q : q;
+  const uint8_t mag = a == 0 ? 0 : a == 1 ? 0x08 : a == 2 ? 0x10 : a == 3 ? 0x14 : a == 4 ? 0x18 : a == 5 ? 0x1A
+                    : a == 6 ? 0x1C : 0x1E;
+  return (uint8_t)((q < 0 ? 0x20 : 0) | mag);
+}
 
 }  // namespace svdq
 

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = B.lib()
     for n in sorted(names):
         assert hasattr(lib, n), n
-    assert B.abi_version() == B.ABI_VERSION == 6
+    assert B.abi_version() == B.ABI_VERSION == 7
     assert B.status_str(0) == "ok"
 
 
@@ -254,6 +254,10 @@ def test_workspace_layout_regions():
         if f == 2:
             assert w["xq_bytes"] == (M + 15) // 16 * 16 * K
             assert w["xs_bytes"] == (M + 15) // 16 * 16 * 4
+        elif f == 0:
+            # FP6 codes: main parts (16 bytes per slice) then tails (8 bytes per slice)
+            assert w["xq_bytes"] == (M + 15) // 16 * 16 * K // 2 + (M + 31) // 32 * 32 * K // 4
+            assert w["xs_bytes"] == (M + 127) // 128 * (K // 128) * 512
         else:
             assert w["xq_bytes"] == (M + 15) // 16 * 16 * K // 2
             assert w["xs_bytes"] == (M + 63) // 64 * 64 * ks4 * 16
@@ -264,32 +268,77 @@ def test_workspace_layout_regions():
             assert w["z_bytes"] == w["zsplit"] * M * ((r + 31) // 32 * 32) * 4
 
 
+E2M3_OF_INT4 = {0: 0x00, 1: 0x08, 2: 0x10, 3: 0x14, 4: 0x18, 5: 0x1A, 6: 0x1C, 7: 0x1E}
+
+
+def _e2m3(q):
+    """FP6 E2M3 code of an integer -7..7, from the format's definition
+    (sign bit 5, exponent bits 3-4 with bias 1, mantissa bits 0-2)."""
+    return (0x20 if q < 0 else 0) | E2M3_OF_INT4[abs(q)]
+
+
+def test_e2m3_table_is_the_format():
+    def value(c):
+        e, m = (c >> 3) & 3, c & 7
+        v = m / 8 if e == 0 else 2.0 ** (e - 1) * (1 + m / 8)
+        return -v if c & 0x20 else v
+    for q in range(-7, 8):
+        assert value(_e2m3(q)) == q
+
+
+def _i4_main_off(row, t, s, steps):
+    return ((row // 16) * steps + t) * 1024 + (4 * (row % 16) + (s ^ ((row >> 2) & 3))) * 16
+
+
+def _i4_tail_off(row, t, s, steps):
+    return ((row // 32) * steps + t) * 1024 + 256 * s + 8 * (row % 32)
+
+
+def _slice_codes(main16, tail8):
+    """32 six-bit codes of a slice: dwords 0-3 from the main part, 4-5 from
+    the tail, element j at bits 6 j of the 192-bit string."""
+    bits = int.from_bytes(bytes(main16) + bytes(tail8), "little")
+    return [(bits >> (6 * j)) & 63 for j in range(32)]
+
+
 def test_int4_kernel_layout_positions():
-    """INT4 element k of a step sits at step byte 16 g + 8 G + j/2 (nibble
-    j % 2), G = k // 64, g = (k % 64) // 16, j = k % 16, and the step bytes
-    are tiled as documented; weight scales in 2 KB units of 128 rows."""
+    """INT4 weights as documented in svdq.h: FP6 E2M3 codes of slice
+    s = 2 G + h of each step, dwords 0-3 in 16-row main units with slot
+    4 (row % 16) + (s ^ row bits 2-3), dwords 4-5 in 32-row tail units after
+    all main parts; scales in 512-byte units of 128 rows x one step."""
     K, N = 640, 144
-    steps, ks4 = K // 128, (K // 128 + 3) // 4
+    steps = K // 128
     rng = np.random.default_rng(0)
-    nib = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    q = rng.integers(-7, 8, (N, K))
     sc = rng.integers(1, 30000, (N, K // 64)).astype(np.uint16)
     prep = {"K": K, "N": N, "rank": 0, "fmt": 0, "smooth_inv": np.ones(K, np.float32),
-            "wq": Q.pack_nibbles(nib), "ws": sc}
+            "wq": Q.pack_nibbles(Q.int4_nibbles(q)), "ws": sc}
+    sizes = B.layer_sizes(K, N, 0, "int4")
+    main_bytes = (N + 15) // 16 * steps * 1024
+    assert sizes["wq_bytes"] == main_bytes + (N + 31) // 32 * steps * 1024
     kl = B.kernel_layout(prep)
     wk = kl["wq_k"].reshape(-1)
-    for n in range(0, N, 7):
-        for k in range(K):
-            t, kk = divmod(k, 128)
-            G, g, j = kk // 64, (kk % 64) // 16, kk % 16
-            byte = wk[_code_off(n, t, 16 * g + 8 * G + j // 2, steps)]
-            assert (byte >> (4 * (j % 2))) & 0xF == nib[n, k]
+    for n in list(range(0, N, 5)) + [N - 1]:
+        for t in range(steps):
+            for s_ in range(4):
+                a = _i4_main_off(n, t, s_, steps)
+                b = main_bytes + _i4_tail_off(n, t, s_, steps)
+                codes = _slice_codes(wk[a:a + 16], wk[b:b + 8])
+                want = [_e2m3(int(v)) for v in q[n, 128 * t + 32 * s_: 128 * t + 32 * s_ + 32]]
+                assert codes == want, (n, t, s_)
+    # rows 144..159 of the last tail unit are padding: zero codes
+    for t in range(steps):
+        for s_ in range(4):
+            for n in range(N, (N + 31) // 32 * 32):
+                b = main_bytes + _i4_tail_off(n, t, s_, steps)
+                assert not wk[b:b + 8].any()
     ws = kl["ws_k"].view(np.uint16).reshape(-1)
-    assert ws.size == (N + 127) // 128 * ks4 * 1024
+    assert ws.size * 2 == sizes["ws_bytes"] == (N + 127) // 128 * steps * 512
     seen = np.zeros(ws.size, bool)
     for n in range(N):
         for t in range(steps):
             for G in range(2):
-                i = ((n // 128) * ks4 + t // 4) * 1024 + ((n % 128) // 4) * 32 + (t % 4) * 8 + (n % 4) * 2 + G
+                i = ((n // 128) * steps + t) * 256 + 128 * G + n % 128
                 assert ws[i] == sc[n, 2 * t + G]
                 seen[i] = True
     assert np.all(ws[~seen] == 0)
