@@ -60,6 +60,7 @@ typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v6i __attribute__((ext_vector_type(6)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -902,11 +903,12 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
 //
 // The codes are FP6 E2M3 values (INT4 -7..7 exactly), the operands of the
 // scaled 32x32x64 MFMA (unit E8M0 scales), whose K extent is one 64-element
-// group: one MFMA gives the group's exact integer dot product I as fp32, and
-// the accumulator takes I * (sx * sw), the fp16 scale product formed exactly
-// in fp32 by one mixed-precision FMA.  Two VALU operations per output and
-// group: the per-group fp16 scales are not powers of two, so they cannot
-// ride in the MFMA's block scales.
+// group: one MFMA gives the group's exact integer dot product I as fp32.  A
+// second MFMA (32x32x16 f16 with one non-zero K slot) gives the outer
+// product P = sw x sx of the group's fp16 scales, exact in fp32 and in the
+// same register layout, and the accumulator takes fma(I, P, acc): one VALU
+// operation per output and group.  (The per-group fp16 scales are not
+// powers of two, so they cannot ride in the MFMA's block scales.)
 //
 // Each step (128 elements = 2 groups) travels global -> LDS by direct-to-LDS
 // loads into a ring of two 25 KB step buffers, one step ahead: the code main
@@ -929,22 +931,6 @@ constexpr int I4_Z0 = 0, I4_L20 = I4_STEP_BYTES;
 // rows 8 a + 4 h + b (a, b < 4) in lane half h, register 4 a + b, so out-feature
 // 16 h + 4 a + b makes register i of a lane out-feature 16 h + i
 __device__ __forceinline__ int i4_nrow(int q) { return 16 * ((q >> 2) & 1) + 4 * (q >> 3) + (q & 3); }
-
-// exact product of fp16 half HA of a and half HB of b in fp32 (one
-// mixed-precision FMA, addend 0)
-template <int HA, int HB>
-__device__ __forceinline__ float f16_mul(uint32_t a, uint32_t b) {
-  float d;
-  if constexpr (HA == 0 && HB == 0)
-    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,1,0]" : "=v"(d) : "v"(a), "v"(b));
-  else if constexpr (HA == 0 && HB == 1)
-    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[1,1,0]" : "=v"(d) : "v"(a), "v"(b));
-  else if constexpr (HA == 1 && HB == 0)
-    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,1,0]" : "=v"(d) : "v"(a), "v"(b));
-  else
-    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[1,1,0] op_sel_hi:[1,1,0]" : "=v"(d) : "v"(a), "v"(b));
-  return d;
-}
 
 template <int NTR>
 __global__ __launch_bounds__(I4_THREADS) __attribute__((amdgpu_waves_per_eu(3))) void kb_i4_kernel(
@@ -1084,27 +1070,30 @@ __global__ __launch_bounds__(I4_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
         af[i] = frag(bo, amain[i][G], atail[i] + 512 * G);
         bf[i] = frag(bo, bmain[i][G], btail[i] + 512 * G);
       }
-      // weight scales of group G: the lane's 16 consecutive out-features per tile
-      v4i sw[2][2];
+      // operands of the scale-product MFMA (32x32x16 f16, K slot 0 only):
+      // lanes 0-31 hold the fp16 scale of their weight row (MFMA row order)
+      // or token in element 0, every other element is zero, so the product
+      // is the outer product sw x sx, exact in fp32
+      v8h pa[2], pb[2];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < 2; ++nt) {
+        const uint32_t w = *reinterpret_cast<const uint16_t*>(lds + bo + I4_ASC + 256 * G + 2 * (64 * wn + 32 * nt + i4_nrow(l32)));
+        pa[nt] = __builtin_bit_cast(v8h, (v4i){(int)(h == 0 ? w : 0u), 0, 0, 0});
+      }
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
-          sw[nt][c] = *reinterpret_cast<const v4i*>(lds + bo + I4_ASC + 256 * G + 2 * (64 * wn + 32 * nt + 16 * h) +
-                                                    16 * c);
+      for (int mt = 0; mt < 2; ++mt) {
+        const uint32_t x = G == 0 ? (sx[mt] & 0xFFFFu) : (sx[mt] >> 16);
+        pb[mt] = __builtin_bit_cast(v8h, (v4i){(int)(h == 0 ? x : 0u), 0, 0, 0});
+      }
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
           const v16f I = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[nt], bf[mt], (v16f){}, 2, 2, 0, 127, 0,
                                                                           127);
+          const v16f P = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[nt], pb[mt], (v16f){}, 0, 0, 0);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const uint32_t w2 = (uint32_t)sw[nt][i >> 3][(i >> 1) & 3];
-            const float p = G == 0 ? ((i & 1) ? f16_mul<0, 1>(sx[mt], w2) : f16_mul<0, 0>(sx[mt], w2))
-                                   : ((i & 1) ? f16_mul<1, 1>(sx[mt], w2) : f16_mul<1, 0>(sx[mt], w2));
-            acc[nt][mt][i] = __builtin_fmaf(I[i], p, acc[nt][mt][i]);
-          }
+          for (int i = 0; i < 16; ++i) acc[nt][mt][i] = __builtin_fmaf(I[i], P[i], acc[nt][mt][i]);
         }
     }
   }
