@@ -36,21 +36,53 @@ def _run(cmd):
     return out
 
 
-def build(verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
-    os.makedirs(LIBDIR, exist_ok=True)
+# Host-code sanitizer configuration (CPU testing only): the host units with
+# AddressSanitizer and UndefinedBehaviorSanitizer (g++), the device units as
+# usual, linked by g++ into a separate library.  Python is not instrumented,
+# so a process that loads it preloads the sanitizer runtimes (see
+# sanitizer_env()).
+ASAN_LIB = os.path.join(HERE, "lib_asan", "libsvdq.so")
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
+
+
+def sanitizer_env():
+    """Environment for a process that loads the sanitized library."""
+    rt = [subprocess.run(["g++", f"-print-file-name={n}"], stdout=subprocess.PIPE, text=True).stdout.strip()
+          for n in ("libasan.so", "libubsan.so")]
+    return {"LD_PRELOAD": ":".join(rt), "ASAN_OPTIONS": "detect_leaks=0:abort_on_error=1",
+            "UBSAN_OPTIONS": "print_stacktrace=1:halt_on_error=1"}
+
+
+def build(verbose=False, sanitize=False, reuse_device_objects=False):
+    """Compile and link the library.  sanitize: the host-sanitizer
+    configuration above; reuse_device_objects (with sanitize): take the
+    device objects of the last plain build instead of compiling them again."""
+    bdir = BUILD + ("_asan" if sanitize else "")
+    lib = ASAN_LIB if sanitize else LIB
+    os.makedirs(bdir, exist_ok=True)
+    os.makedirs(os.path.dirname(lib), exist_ok=True)
     objs = []
     for src, cc in UNITS:
-        obj = os.path.join(BUILD, src + ".o")
-        out = _run(cc + ["-c", os.path.join(CSRC, src), "-o", obj])
+        if sanitize and reuse_device_objects and cc[0] != "g++":
+            prev = os.path.join(BUILD, src + ".o")
+            if os.path.exists(prev):
+                objs.append(prev)
+                continue
+        obj = os.path.join(bdir, src + ".o")
+        flags = cc + (SANITIZE_FLAGS if sanitize and cc[0] == "g++" else [])
+        out = _run(flags + ["-c", os.path.join(CSRC, src), "-o", obj])
         if verbose and out:
             print(out)
         objs.append(obj)
-    tmp = LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs + ["-lpthread"])
-    os.replace(tmp, LIB)
-    return LIB
+    tmp = lib + ".tmp"
+    if sanitize:
+        _run(["g++", "-shared", "-fPIC"] + SANITIZE_FLAGS + ["-o", tmp] + objs +
+             ["-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib", "-lpthread"])
+    else:
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs + ["-lpthread"])
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, sanitize="--sanitize" in sys.argv))

@@ -1168,19 +1168,22 @@ __global__ __launch_bounds__(I4_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
 // ------------------------------------------------- unfused baseline: up + add
 //
 // Y += Z L2' as its own pass over Y, for measuring what fusing the branch
-// into the GEMM epilogue saves.  One wave per 16 tokens x 64 out-features;
-// bf16 MFMA on the Z hi/lo halves and L2'^T rows, then a read-modify-write
-// of the bf16 output.
+// into the GEMM epilogue saves.  A block of 4 waves covers 64 tokens x 64
+// out-features: wave w forms tokens 16 w .. +16 on bf16 MFMA (Z hi and lo
+// against L2'^T rows), the fp32 products pass through LDS, and the
+// read-modify-write of Y runs with 8 consecutive bf16 per lane, so every
+// load and store instruction covers whole 128-byte lines of Y rows.
+constexpr int KUP_LD = 68;   // LDS row stride (floats) of the 64 x 64 product tile
+
 template <int NTR>
 __global__ __launch_bounds__(256) void kup_kernel(const uint16_t* __restrict__ zp, const uint16_t* __restrict__ l2k,
                                                   uint16_t* __restrict__ Y, int M, int N, int rpad) {
+  __shared__ float tile[64 * KUP_LD];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int tiles_n = (N + 63) / 64, tiles = ((M + 15) / 16) * tiles_n;
-  const int tile = blockIdx.x * 4 + wave;
-  if (tile >= tiles) return;   // whole wave; no barriers in this kernel
-  const int m0 = (tile / tiles_n) * 16, n0 = (tile % tiles_n) * 64;
-  const int m = min(m0 + l16, M - 1);
+  const int tiles_n = (N + 63) / 64;
+  const int m0 = (blockIdx.x / tiles_n) * 64, n0 = (blockIdx.x % tiles_n) * 64;
+  const int m = min(m0 + 16 * wave + l16, M - 1);
   v4f acc[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) acc[nt] = (v4f){0.f, 0.f, 0.f, 0.f};
@@ -1197,17 +1200,25 @@ __global__ __launch_bounds__(256) void kup_kernel(const uint16_t* __restrict__ z
       acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bl, acc[nt], 0, 0, 0);
     }
   }
-  // lane holds out-features n0 + 16 nt + 4 g + 0..3 of token m0 + l16
-  if (m0 + l16 >= M) return;
+  // lane holds out-features 16 nt + 4 g + i of token 16 wave + l16
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int nn = n0 + 16 * nt + 4 * g;
-    if (nn >= N) continue;
-    uint2* yp = reinterpret_cast<uint2*>(Y + (size_t)(m0 + l16) * N + nn);
-    const uint2 y = *yp;
-    const uint32_t lo = bf16_rne(bf16_lo(y.x) + acc[nt][0]) | (bf16_rne(bf16_hi(y.x) + acc[nt][1]) << 16);
-    const uint32_t hi = bf16_rne(bf16_lo(y.y) + acc[nt][2]) | (bf16_rne(bf16_hi(y.y) + acc[nt][3]) << 16);
-    *yp = make_uint2(lo, hi);
+  for (int nt = 0; nt < 4; ++nt)
+    *reinterpret_cast<v4f*>(&tile[(16 * wave + l16) * KUP_LD + 16 * nt + 4 * g]) = acc[nt];
+  __syncthreads();
+  // 512 pieces of 8 outputs: row c / 8, columns 8 (c % 8) .. +8
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = (int)threadIdx.x + 256 * j, row = c >> 3, col = 8 * (c & 7);
+    const int mm = m0 + row, nn = n0 + col;
+    if (mm >= M || nn >= N) continue;
+    v4i* yp = reinterpret_cast<v4i*>(Y + (size_t)mm * N + nn);
+    const v4i y = *yp;
+    const float* a = &tile[row * KUP_LD + col];
+    v4i o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = (int)(bf16_rne(bf16_lo((uint32_t)y[i]) + a[2 * i]) | (bf16_rne(bf16_hi((uint32_t)y[i]) + a[2 * i + 1]) << 16));
+    *yp = o;
   }
 }
 
@@ -1521,13 +1532,13 @@ svdq_status svdq_linear_forward_unfused(const svdq_layer* layer, const uint16_t*
                             : launch_kb<SVDQ_INT4_G64>(plain, w8, W, M, Y, st);
   if (e == hipSuccess && layer->rank > 0) {
     const int rp = rank_pad(layer->rank);
-    const int tiles = ((M + 15) / 16) * ((layer->N + 63) / 64);
+    const int tiles = ((M + 63) / 64) * ((layer->N + 63) / 64);
     const uint16_t* zp = reinterpret_cast<const uint16_t*>(w8 + W.z_off);
     switch (rp / 32) {
-      case 1: hipLaunchKernelGGL(kup_kernel<1>, dim3((tiles + 3) / 4), dim3(256), 0, st, zp, layer->l2k, Y, M, layer->N, rp); break;
-      case 2: hipLaunchKernelGGL(kup_kernel<2>, dim3((tiles + 3) / 4), dim3(256), 0, st, zp, layer->l2k, Y, M, layer->N, rp); break;
-      case 3: hipLaunchKernelGGL(kup_kernel<3>, dim3((tiles + 3) / 4), dim3(256), 0, st, zp, layer->l2k, Y, M, layer->N, rp); break;
-      case 4: hipLaunchKernelGGL(kup_kernel<4>, dim3((tiles + 3) / 4), dim3(256), 0, st, zp, layer->l2k, Y, M, layer->N, rp); break;
+      case 1: hipLaunchKernelGGL(kup_kernel<1>, dim3(tiles), dim3(256), 0, st, zp, layer->l2k, Y, M, layer->N, rp); break;
+      case 2: hipLaunchKernelGGL(kup_kernel<2>, dim3(tiles), dim3(256), 0, st, zp, layer->l2k, Y, M, layer->N, rp); break;
+      case 3: hipLaunchKernelGGL(kup_kernel<3>, dim3(tiles), dim3(256), 0, st, zp, layer->l2k, Y, M, layer->N, rp); break;
+      case 4: hipLaunchKernelGGL(kup_kernel<4>, dim3(tiles), dim3(256), 0, st, zp, layer->l2k, Y, M, layer->N, rp); break;
       default: return SVDQ_ERR_SHAPE;
     }
     e = hipGetLastError();

@@ -9,6 +9,12 @@ if ROOT not in sys.path:
 
 GOLDEN = os.path.join(ROOT, "tests", "golden")
 
+# The host-sanitizer run (rank_gemm_svdq_amd/build.py --sanitize) points the
+# binding at the instrumented library through SVDQ_TEST_LIB.
+if os.environ.get("SVDQ_TEST_LIB"):
+    import rank_gemm_svdq_amd.binding as _binding
+    _binding.LIB_PATH = os.path.abspath(os.environ["SVDQ_TEST_LIB"])
+
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
