@@ -36,6 +36,17 @@ clipping):
            mantissa; bit 3 is the sign bit of z (fp32 sign, -0 included)
 E2M1 magnitudes by code 0..7: 0, 0.5, 1, 1.5, 2, 3, 4, 6.
 
+MXFP4 with the OCP rule ("mxfp4_ocp"; the msModelSlim doc names MXFP4
+blocks without a scale rule, and the OCP Microscaling Formats v1.0
+specification fixes one): the shared exponent is
+    e    = floor(log2(amax)) - 2           (2 = the exponent of E2M1's
+                                            largest normal value, 6 = 1.5 x 2^2)
+           clamped to [-127, 127]; amax == 0 gives e = -127
+and the elements are the nearest E2M1 values of z * 2**-e saturated at +-6
+(magnitudes from 6 up to below 8 can occur and take code 7).  It equals the
+default rule's e whenever amax <= 6 * 2**e and is one smaller otherwise,
+trading the largest values' clipping for a finer step.
+
 Packing: two codes per byte (Zhou notes, Eq. (12) counts mn/2 bytes);
 element 2j goes to the low nibble of byte j, K contiguous, row-major.
 
@@ -55,7 +66,8 @@ Codes are stored one signed byte per element, K contiguous, row-major.
 
 Pins (tests/test_oracle_quantizers.py): the worked example of Zhou notes
 sec. 2.2 (range 7 gives step 1; range 1 gives step 1/7), the saturated
-scale on both sides of the fp16 overflow threshold, brute-force argmin
+scale on both sides of the fp16 overflow threshold, the OCP exponent by
+brute-force search and its relation to the default rule, brute-force argmin
 over the 15 INT4 codes, the 255 8-bit codes and the 8 E2M1 magnitudes,
 brute-force search for e, the no-clipping property and the Eq. (9) per-group
 error bound (per row for 8-bit).
@@ -153,16 +165,31 @@ def e2m1_nearest_code(a):
     return np.argmax(choose, axis=-1).astype(np.int64)
 
 
-def quantize_mxfp4(z):
+def mxfp4_ocp_block_exponent(amax):
+    """OCP shared exponent floor(log2(amax)) - 2, clamped to [-127, 127].
+
+    amax: fp32 array.  With amax = f * 2**E (0.5 <= f < 1), floor(log2(amax))
+    is E - 1, so e = E - 3; amax == 0 gives -127.
+    """
+    amax = np.asarray(amax, dtype=np.float64)
+    _, E = np.frexp(amax)
+    e = np.where(amax == 0, -127, E - 3)
+    return np.clip(e, -127, 127).astype(np.int64)
+
+
+def quantize_mxfp4(z, rule="ceil"):
     """MXFP4 (E2M1 codes, E8M0 scale per 32 elements).
 
-    z: [rows, K] fp32.  Returns (codes uint8 [rows, K] in 0..15 with bit 3 the
-    sign, scale bytes uint8 [rows, K/32], exponents int64 [rows, K/32]).
+    z: [rows, K] fp32; rule 'ceil' (the default: no clipping) or 'ocp' (the
+    OCP floor rule with saturation).  Returns (codes uint8 [rows, K] in 0..15
+    with bit 3 the sign, scale bytes uint8 [rows, K/32], exponents int64
+    [rows, K/32]).
     """
     zg = _groups(z, MXFP4_GROUP)
     amax = np.max(np.abs(zg), axis=2)
-    e = mxfp4_block_exponent(amax)
+    e = mxfp4_block_exponent(amax) if rule == "ceil" else mxfp4_ocp_block_exponent(amax)
     scaled = np.abs(zg.astype(np.float64)) * np.ldexp(1.0, -e)[:, :, None]
+    scaled = np.minimum(scaled, 6.0)                        # saturation (only the ocp rule reaches it)
     mag = e2m1_nearest_code(scaled)
     sign = np.signbit(zg).astype(np.int64)
     codes = (sign << 3) | mag
@@ -231,8 +258,8 @@ def quantize(z, fmt):
         q, s = quantize_int4(z)
         return {"packed": pack_nibbles(int4_nibbles(q)), "scales": s,
                 "codes": q, "deq": decode_int4(q, s)}
-    if fmt == "mxfp4":
-        c, b, _ = quantize_mxfp4(z)
+    if fmt in ("mxfp4", "mxfp4_ocp"):
+        c, b, _ = quantize_mxfp4(z, "ceil" if fmt == "mxfp4" else "ocp")
         return {"packed": pack_nibbles(c), "scales": b, "codes": c,
                 "deq": decode_mxfp4(c, b)}
     raise ValueError(f"unknown format {fmt!r}")
@@ -245,6 +272,6 @@ def dequantize_packed(packed, scales, fmt):
     nib = unpack_nibbles(packed)
     if fmt == "int4":
         return decode_int4(nibble_to_int4(nib), scales)
-    if fmt == "mxfp4":
+    if fmt in ("mxfp4", "mxfp4_ocp"):
         return decode_mxfp4(nib, scales)
     raise ValueError(f"unknown format {fmt!r}")

@@ -272,3 +272,60 @@ def test_w8_row_error_bound_and_roundtrip():
     # |z - q s| <= s / 2 (times the fp32 reciprocal's relative error) per element
     bound = d["scales"].astype(np.float64)[:, None] * (0.5 + 1e-6)
     assert np.all(np.abs(z - d["deq"]) <= bound)
+
+
+def test_mxfp4_ocp_exponent_brute_force_and_relation():
+    """OCP rule: e = floor(log2(amax)) - 2, i.e. the largest integer e with
+    4 * 2**e <= amax (brute force), clamped to [-127, 127]; it equals the
+    default (no clipping) exponent when amax <= 6 * 2**e and is one below
+    it otherwise."""
+    rng = np.random.default_rng(21)
+    amax = np.concatenate([
+        np.exp(rng.uniform(-80, 80, 2000)),
+        4.0 * np.ldexp(1.0, np.arange(-20, 20)),                    # exact powers of two times 4
+        6.0 * np.ldexp(1.0, np.arange(-20, 20)),
+        np.nextafter(6.0 * np.ldexp(1.0, np.arange(-20, 20)), np.inf),
+        np.nextafter(8.0 * np.ldexp(1.0, np.arange(-20, 20)), 0),
+        [0.0, 1e-45, 3e38]]).astype(np.float32)
+    e = Q.mxfp4_ocp_block_exponent(amax)
+    ec = Q.mxfp4_block_exponent(amax)
+    for a, ei, eci in zip(amax.astype(np.float64), e, ec):
+        if a == 0:
+            assert ei == -127
+            continue
+        want = 127
+        while want > -127 and 4.0 * 2.0**want > a:
+            want -= 1
+        assert ei == want, (a, ei, want)
+        if -126 < ei < 126:
+            assert eci == (ei if a <= 6.0 * 2.0**ei else ei + 1), (a, ei, eci)
+
+
+def test_mxfp4_ocp_saturates_and_keeps_the_grid():
+    rng = np.random.default_rng(22)
+    z = (rng.standard_t(3, (16, 32 * 16)) * 2.0).astype(np.float32)
+    z[0, :32] = 0.0
+    z[1, :32] = np.float32(7.0)                # amax 7: e = 0, every element saturates to 6
+    z[1, 5] = -7.9
+    z[2, :32] = np.linspace(-5.9, 5.9, 32)     # amax 5.9: e = 0, nothing saturates
+    codes, b, e = Q.quantize_mxfp4(z, "ocp")
+    assert b[0, 0] == 0 and np.all(codes[0, :32] == 0)
+    assert e[1, 0] == 0 and np.all(codes[1, :32] & 7 == 7) and codes[1, 5] == 15
+    amax = np.abs(z.astype(np.float64)).reshape(16, 16, 32).max(-1)
+    scaled_max = amax * np.ldexp(1.0, -e)
+    nz = amax > 0
+    assert np.all((scaled_max[nz] >= 4.0) & (scaled_max[nz] < 8.0))
+    # below the saturation point every element is the nearest E2M1 value;
+    # above it, 6
+    deq = Q.decode_mxfp4(codes, b)
+    s = np.repeat(np.ldexp(1.0, e), 32, axis=1)
+    x = np.abs(z.astype(np.float64)) / s
+    d = np.abs(deq) / s
+    inside = x <= 6.0
+    cand = Q.E2M1_VALUES
+    nearest = np.min(np.abs(x[inside][:, None] - cand[None, :]), axis=1)
+    assert np.all(np.abs(x[inside] - d[inside]) == nearest)
+    assert np.all(d[~inside] == 6.0)
+    # the default rule never clips: same data, no element saturated
+    c2, b2, e2 = Q.quantize_mxfp4(z)
+    assert np.all(amax * np.ldexp(1.0, -e2) <= 6.0)
