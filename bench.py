@@ -29,9 +29,9 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK = {"mxfp4": 10.1e15, "int4": 5.0e15, "w8a8": 5.0e15}   # dense MFMA peaks: FP4 / int8 (MI355X datasheet)
-PEAK_NAME = {"mxfp4": "fp4 MFMA", "int4": "int8 MFMA", "w8a8": "int8 MFMA"}
-DTYPE = {"mxfp4": "fp4", "int4": "int4", "w8a8": "int8"}   # operand type of the main contraction
+PEAK = {"mxfp4": 10.1e15, "mxfp4_ocp": 10.1e15, "int4": 5.0e15, "w8a8": 5.0e15}   # dense MFMA peaks: FP4 / int8
+PEAK_NAME = {"mxfp4": "fp4 MFMA", "mxfp4_ocp": "fp4 MFMA", "int4": "int8 MFMA", "w8a8": "int8 MFMA"}
+DTYPE = {"mxfp4": "fp4", "mxfp4_ocp": "fp4", "int4": "int4", "w8a8": "int8"}   # operand type of the main contraction
 
 
 # Algorithmic work of one layer (what the kernels must at least move or
@@ -104,7 +104,7 @@ def measured_traffic(config):
 def kb_kernel_names(fmt, K, rank):
     """Demangled and mangled names of the K-B instantiation a layer launches."""
     ntr = ((rank + 31) // 32 * 32) // 32
-    if fmt == "mxfp4":
+    if fmt in ("mxfp4", "mxfp4_ocp"):
         odd = (K // 128) % 2
         return (f"kb_mx_kernel<{ntr}, {'true' if odd else 'false'}, 8, false>",
                 f"kb_mx_kernelILi{ntr}ELb{odd}ELi8ELb0E")
@@ -423,7 +423,7 @@ def rotated_run(args, torch, B, prep, bias_bits, X, M, N, stream):
     out = {"sets": n, "bytes_per_set": int(per_set), "steps": steps, "ms_per_step": ms,
            "TOPS": ops / (ms * 1e-3) / 1e12, "ka_us_median": float(np.median(ka)) * 1e3,
            "kb_us_median": float(np.median(kb)) * 1e3,
-           "ka_GB_per_s": ka_bytes(M, prep["K"], prep["rank"], {0: "int4", 1: "mxfp4", 2: "w8a8"}[prep["fmt"]])
+           "ka_GB_per_s": ka_bytes(M, prep["K"], prep["rank"], {0: "int4", 1: "mxfp4", 2: "w8a8", 3: "mxfp4_ocp"}[prep["fmt"]])
            / (float(np.median(ka)) * 1e-3) / 1e9}
     del sets
     torch.cuda.synchronize()
@@ -654,7 +654,7 @@ def summarize_profiles(d, config, fmt_override=None):
     rp = (r + 31) // 32 * 32 if r else 0
     kb_names = kb_kernel_names(fmt, K, r)
     ka_names = ("ka_kernel",)
-    short = {"mxfp4": "kb_mx", "int4": "kb_int4", "w8a8": "kb_w8a8"}[fmt]
+    short = {"mxfp4": "kb_mx", "mxfp4_ocp": "kb_mx", "int4": "kb_int4", "w8a8": "kb_w8a8"}[fmt]
     key = s.name if not fmt_override else f"{s.name}_{fmt}"
     cmds = profile_commands("gpurun_out/prof_" + key, config + (f" --fmt {fmt_override}" if fmt_override else ""))
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define SVDQ_ABI_VERSION 7   /* 7: INT4 codes travel as FP6 E2M3 values (main parts + tails) */
+#define SVDQ_ABI_VERSION 8   /* 8: MXFP4 with the OCP shared-exponent rule as a format */
 #define SVDQ_MAX_RANK 128   /* msModelSlim doc, svd_res: rank not above 128 recommended */
 
 typedef enum svdq_status {
@@ -56,8 +56,15 @@ typedef enum svdq_status {
 
 /* SVDQ_W8A8: 8-bit codes -127..127 with one fp32 scale per row, i.e. per
  * token for activations (dynamic) and per out-feature for weights (Zhou
- * notes sec. 8, the 8-bit setting). */
-typedef enum svdq_format { SVDQ_INT4_G64 = 0, SVDQ_MXFP4_G32 = 1, SVDQ_W8A8 = 2 } svdq_format;
+ * notes sec. 8, the 8-bit setting).
+ * SVDQ_MXFP4_G32_OCP: MXFP4 with the OCP Microscaling v1.0 shared-exponent
+ * rule, e = floor(log2(amax)) - 2 clamped to [-127, 127], elements rounded
+ * to E2M1 and saturated at +-6 (the pages name MXFP4 blocks without a scale
+ * rule: msModelSlim doc, "per_block mxfp4 minmax").  SVDQ_MXFP4_G32 takes the
+ * smallest e with amax <= 6 * 2^e (no clipping).  Both share every layout. */
+typedef enum svdq_format {
+  SVDQ_INT4_G64 = 0, SVDQ_MXFP4_G32 = 1, SVDQ_W8A8 = 2, SVDQ_MXFP4_G32_OCP = 3
+} svdq_format;
 
 /* ------------------------------------------------------------------------
  * Shape rules (checked by every entry point):

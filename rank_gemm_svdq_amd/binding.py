@@ -13,7 +13,7 @@ import os
 import numpy as np
 
 __all__ = [
-    "INT4", "MXFP4", "SvdqError", "lib", "status_str", "abi_version", "device_check",
+    "INT4", "MXFP4", "W8A8", "MXFP4_OCP", "SvdqError", "lib", "status_str", "abi_version", "device_check",
     "layer_sizes", "workspace_layout", "workspace_bytes", "calib_absmax", "pack_host",
     "prepare", "attach_lora", "kernel_layout", "unpack_activations", "DeviceLayer",
     "quantize_lora_down", "gemm_lora_up", "linear_forward", "linear_forward_unfused", "linear_forward_noalloc",
@@ -24,6 +24,7 @@ __all__ = [
 INT4 = 0
 MXFP4 = 1
 W8A8 = 2
+MXFP4_OCP = 3   # MXFP4 with the OCP shared-exponent rule (floor(log2 amax) - 2, saturated elements)
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libsvdq.so")
 
 
@@ -34,6 +35,8 @@ def fmt_code(fmt):
         return MXFP4
     if fmt in (W8A8, "w8a8"):
         return W8A8
+    if fmt in (MXFP4_OCP, "mxfp4_ocp"):
+        return MXFP4_OCP
     raise ValueError(f"unknown format {fmt!r}")
 
 
@@ -104,7 +107,7 @@ class SearchResult(C.Structure):
 
 
 _lib = None
-ABI_VERSION = 7   # SVDQ_ABI_VERSION of include/svdq.h that these structures mirror
+ABI_VERSION = 8   # SVDQ_ABI_VERSION of include/svdq.h that these structures mirror
 
 
 def lib():

@@ -175,22 +175,28 @@ __global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __res
       // per-token scale: the whole row's maximum is needed first; the codes
       // are written in a second pass below
       rmax = fmaxf(rmax, amax);
-    } else if constexpr (FMT == SVDQ_MXFP4_G32) {
-      // smallest e with amax <= 6 * 2^e, clamped to [-127, 127]
+    } else if constexpr (FMT == SVDQ_MXFP4_G32 || FMT == SVDQ_MXFP4_G32_OCP) {
+      // smallest e with amax <= 6 * 2^e, or with the OCP rule
+      // floor(log2(amax)) - 2; clamped to [-127, 127]
+      constexpr bool OCP = FMT == SVDQ_MXFP4_G32_OCP;
       const uint32_t ab = __float_as_uint(amax);
       const int ex = (int)(ab >> 23);
-      int e = ex == 0 ? -127 : ex - 129 + ((ab & 0x7FFFFFu) > 0x400000u ? 1 : 0);
+      int e = ex == 0 ? -127 : ex - 129 + (!OCP && (ab & 0x7FFFFFu) > 0x400000u ? 1 : 0);
       e = e < -127 ? -127 : (e > 127 ? 127 : e);
       v4i packed;
       if (e >= -126) {
         const float scale = __uint_as_float((uint32_t)(e + 127) << 23);
+        // the OCP rule saturates at 6 2^e before the convert (exact: a
+        // power-of-two multiple); x^ itself stays for the down projection
+        const float lim = 6.0f * scale;
+        auto sat = [&](float v) __attribute__((always_inline)) { return OCP ? fminf(fmaxf(v, -lim), lim) : v; };
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           uint32_t d = 0;
-          d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, xh[8 * w + 0], xh[8 * w + 1], scale, 0);
-          d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, xh[8 * w + 2], xh[8 * w + 3], scale, 1);
-          d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, xh[8 * w + 4], xh[8 * w + 5], scale, 2);
-          d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, xh[8 * w + 6], xh[8 * w + 7], scale, 3);
+          d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, sat(xh[8 * w + 0]), sat(xh[8 * w + 1]), scale, 0);
+          d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, sat(xh[8 * w + 2]), sat(xh[8 * w + 3]), scale, 1);
+          d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, sat(xh[8 * w + 4]), sat(xh[8 * w + 5]), scale, 2);
+          d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, sat(xh[8 * w + 6]), sat(xh[8 * w + 7]), scale, 3);
           packed[w] = (int)d;
         }
       } else {
@@ -1323,7 +1329,7 @@ template <int FMT>
 static hipError_t launch_kb(const svdq_layer& L, const uint8_t* ws, const svdq_ws_layout& W, int M, uint16_t* Y,
                             hipStream_t st) {
   const int rp = rank_pad(L.rank);
-  if constexpr (FMT == SVDQ_MXFP4_G32 || FMT == SVDQ_W8A8) {
+  if constexpr (FMT == SVDQ_MXFP4_G32 || FMT == SVDQ_MXFP4_G32_OCP || FMT == SVDQ_W8A8) {
     constexpr bool W8 = FMT == SVDQ_W8A8;
     switch (rp / 32) {
       case 0: launch_kb_mx<0, W8>(L, ws, W, M, Y, st); break;
@@ -1368,6 +1374,18 @@ static svdq_status check_layer(const svdq_layer* L, int32_t M) {
       (L->rank > 0 && (!aligned16(L->l1k) || !aligned16(L->l2k))) || (L->bias && !aligned16(L->bias)))
     return SVDQ_ERR_ALIGN;
   return SVDQ_OK;
+}
+
+// call fn with the format as a compile-time constant
+template <class Fn>
+static hipError_t by_format(int fmt, Fn&& fn) {
+  switch (fmt) {
+    case SVDQ_INT4_G64: return fn(std::integral_constant<int, SVDQ_INT4_G64>{});
+    case SVDQ_MXFP4_G32: return fn(std::integral_constant<int, SVDQ_MXFP4_G32>{});
+    case SVDQ_MXFP4_G32_OCP: return fn(std::integral_constant<int, SVDQ_MXFP4_G32_OCP>{});
+    case SVDQ_W8A8: return fn(std::integral_constant<int, SVDQ_W8A8>{});
+  }
+  return hipErrorInvalidValue;
 }
 
 // gfx950 check, cached per device (write-once flags)
@@ -1436,10 +1454,9 @@ svdq_status svdq_quantize_lora_down(const svdq_layer* layer, const uint16_t* X, 
   if (ws_bytes < W.total) return SVDQ_ERR_WORKSPACE;
   if ((s = device_ok()) != SVDQ_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = layer->fmt == SVDQ_MXFP4_G32
-                     ? launch_ka<SVDQ_MXFP4_G32>(*layer, X, M, static_cast<uint8_t*>(ws), W, st)
-                 : layer->fmt == SVDQ_W8A8 ? launch_ka<SVDQ_W8A8>(*layer, X, M, static_cast<uint8_t*>(ws), W, st)
-                                           : launch_ka<SVDQ_INT4_G64>(*layer, X, M, static_cast<uint8_t*>(ws), W, st);
+  const hipError_t e = by_format(layer->fmt, [&](auto f) {
+    return launch_ka<decltype(f)::value>(*layer, X, M, static_cast<uint8_t*>(ws), W, st);
+  });
   return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_DEVICE;
 }
 
@@ -1454,10 +1471,9 @@ svdq_status svdq_gemm_lora_up(const svdq_layer* layer, const void* ws, size_t ws
   if (ws_bytes < W.total) return SVDQ_ERR_WORKSPACE;
   if ((s = device_ok()) != SVDQ_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = layer->fmt == SVDQ_MXFP4_G32
-                     ? launch_kb<SVDQ_MXFP4_G32>(*layer, static_cast<const uint8_t*>(ws), W, M, Y, st)
-                 : layer->fmt == SVDQ_W8A8 ? launch_kb<SVDQ_W8A8>(*layer, static_cast<const uint8_t*>(ws), W, M, Y, st)
-                                           : launch_kb<SVDQ_INT4_G64>(*layer, static_cast<const uint8_t*>(ws), W, M, Y, st);
+  const hipError_t e = by_format(layer->fmt, [&](auto f) {
+    return launch_kb<decltype(f)::value>(*layer, static_cast<const uint8_t*>(ws), W, M, Y, st);
+  });
   return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_DEVICE;
 }
 
@@ -1488,17 +1504,11 @@ svdq_status svdq_linear_forward_noalloc(const svdq_layer* layer, const uint16_t*
   // workspace (nothing in it needs clearing: K-A writes every byte K-B reads
   // for the M rows, and rows past M are never stored)
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  if (layer->fmt == SVDQ_MXFP4_G32) {
-    e = launch_ka<SVDQ_MXFP4_G32>(*layer, X, M, ws, W, st);
-    if (e == hipSuccess) e = launch_kb<SVDQ_MXFP4_G32>(*layer, ws, W, M, Y, st);
-  } else if (layer->fmt == SVDQ_W8A8) {
-    e = launch_ka<SVDQ_W8A8>(*layer, X, M, ws, W, st);
-    if (e == hipSuccess) e = launch_kb<SVDQ_W8A8>(*layer, ws, W, M, Y, st);
-  } else {
-    e = launch_ka<SVDQ_INT4_G64>(*layer, X, M, ws, W, st);
-    if (e == hipSuccess) e = launch_kb<SVDQ_INT4_G64>(*layer, ws, W, M, Y, st);
-  }
+  const hipError_t e = by_format(layer->fmt, [&](auto f) {
+    constexpr int F = decltype(f)::value;
+    const hipError_t ea = launch_ka<F>(*layer, X, M, ws, W, st);
+    return ea == hipSuccess ? launch_kb<F>(*layer, ws, W, M, Y, st) : ea;
+  });
   return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_DEVICE;
 }
 
@@ -1516,20 +1526,13 @@ svdq_status svdq_linear_forward_unfused(const svdq_layer* layer, const uint16_t*
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   svdq_layer plain = *layer;   // the same kernels with the low-rank branch left out
   plain.rank = 0;
-  const int f = layer->fmt;
-  auto ka = [&](const svdq_layer& L, bool zonly) {
-    if (f == SVDQ_MXFP4_G32)
-      return zonly ? launch_ka<SVDQ_MXFP4_G32, true>(L, X, M, w8, W, st) : launch_ka<SVDQ_MXFP4_G32>(L, X, M, w8, W, st);
-    if (f == SVDQ_W8A8)
-      return zonly ? launch_ka<SVDQ_W8A8, true>(L, X, M, w8, W, st) : launch_ka<SVDQ_W8A8>(L, X, M, w8, W, st);
-    return zonly ? launch_ka<SVDQ_INT4_G64, true>(L, X, M, w8, W, st) : launch_ka<SVDQ_INT4_G64>(L, X, M, w8, W, st);
-  };
-  hipError_t e = ka(plain, false);
-  if (e == hipSuccess && layer->rank > 0) e = ka(*layer, true);
-  if (e == hipSuccess)
-    e = f == SVDQ_MXFP4_G32 ? launch_kb<SVDQ_MXFP4_G32>(plain, w8, W, M, Y, st)
-        : f == SVDQ_W8A8    ? launch_kb<SVDQ_W8A8>(plain, w8, W, M, Y, st)
-                            : launch_kb<SVDQ_INT4_G64>(plain, w8, W, M, Y, st);
+  hipError_t e = by_format(layer->fmt, [&](auto f) {
+    constexpr int F = decltype(f)::value;
+    hipError_t r = launch_ka<F>(plain, X, M, w8, W, st);                    // quantize only
+    if (r == hipSuccess && layer->rank > 0) r = launch_ka<F, true>(*layer, X, M, w8, W, st);   // down projection
+    if (r == hipSuccess) r = launch_kb<F>(plain, w8, W, M, Y, st);           // GEMM + bias, Y stored
+    return r;
+  });
   if (e == hipSuccess && layer->rank > 0) {
     const int rp = rank_pad(layer->rank);
     const int tiles = ((M + 63) / 64) * ((layer->N + 63) / 64);

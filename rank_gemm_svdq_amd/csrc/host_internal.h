@@ -16,6 +16,7 @@ constexpr int kStep = 128;  // K elements per main-loop step of both kernels
 
 inline int group_size(int fmt) { return fmt == SVDQ_INT4_G64 ? 64 : 32; }   // the 4-bit formats
 inline bool is_w8(int fmt) { return fmt == SVDQ_W8A8; }
+inline bool is_mx(int fmt) { return fmt == SVDQ_MXFP4_G32 || fmt == SVDQ_MXFP4_G32_OCP; }   // same layouts
 // code steps of 64 bytes per row: 128 elements (4-bit) or 64 (8-bit)
 inline int32_t code_steps(int32_t K, int fmt) { return is_w8(fmt) ? K / 64 : K / 128; }
 // canonical buffers: codes [rows, K/2] (4-bit) or [rows, K] (8-bit); scales
@@ -24,7 +25,7 @@ inline size_t canon_code_bytes(int64_t rows, int32_t K, int fmt) {
   return is_w8(fmt) ? (size_t)rows * K : (size_t)rows * (K / 2);
 }
 inline size_t canon_scale_bytes(int64_t rows, int32_t K, int fmt) {
-  return fmt == SVDQ_INT4_G64 ? (size_t)rows * (K / 64) * 2 : fmt == SVDQ_MXFP4_G32 ? (size_t)rows * (K / 32)
+  return fmt == SVDQ_INT4_G64 ? (size_t)rows * (K / 64) * 2 : is_mx(fmt) ? (size_t)rows * (K / 32)
                                                                                    : (size_t)rows * 4;
 }
 inline int32_t rank_pad(int32_t rank) { return (rank + 31) / 32 * 32; }
@@ -83,7 +84,7 @@ float float_from_half(uint16_t h);
 
 // Quantizers of one group, shared by the weight packer and the unpack helper.
 void quant_int4_group(const float* x, uint8_t* nib /*64 nibble values*/, uint16_t* scale_bits);
-void quant_mxfp4_group(const float* x, uint8_t* nib /*32 nibble values*/, uint8_t* scale_byte);
+void quant_mxfp4_group(const float* x, uint8_t* nib /*32 nibble values*/, uint8_t* scale_byte, bool ocp_rule);
 void quant_w8_row(const float* x, int32_t K, int8_t* q, float* scale);
 
 // One residual-iteration candidate as a deployable layer (canonical host

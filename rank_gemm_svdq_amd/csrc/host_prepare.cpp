@@ -26,7 +26,7 @@ bool valid_kn(int32_t K, int32_t N) {
   return K >= kStep && K <= 65536 && K % kStep == 0 && N >= 16 && N <= 262144 && N % 16 == 0;
 }
 bool valid_rank(int32_t rank) { return rank >= 0 && rank <= SVDQ_MAX_RANK && rank % 16 == 0; }
-bool valid_fmt(int32_t fmt) { return fmt == SVDQ_INT4_G64 || fmt == SVDQ_MXFP4_G32 || fmt == SVDQ_W8A8; }
+bool valid_fmt(int32_t fmt) { return fmt == SVDQ_INT4_G64 || is_mx(fmt) || fmt == SVDQ_W8A8; }
 
 bool geometry(int32_t K, int32_t N, int32_t rank, int32_t fmt, Geometry* g) {
   if (!valid_kn(K, N) || !valid_rank(rank) || !valid_fmt(fmt)) return false;
@@ -38,7 +38,7 @@ bool geometry(int32_t K, int32_t N, int32_t rank, int32_t fmt, Geometry* g) {
   g->wq_tail_off = g->wq_bytes;
   if (fmt == SVDQ_INT4_G64) g->wq_bytes += i4_tail_bytes(N, g->steps);   // FP6 codes: main parts, then tails
   g->ws_bytes = fmt == SVDQ_INT4_G64   ? i4_scale_bytes(N, g->steps)
-                : fmt == SVDQ_MXFP4_G32 ? scale_record_bytes(N, g->ks4)
+                : is_mx(fmt)            ? scale_record_bytes(N, g->ks4)
                                         : (size_t)N * 4;
   g->l1k_bytes = (size_t)K * rank * 2;
   g->l2k_bytes = (size_t)N * g->rpad * 2;
@@ -169,9 +169,11 @@ void quant_int4_group(const float* x, uint8_t* nib, uint16_t* scale_bits) {
 }
 
 // MXFP4 (E2M1, 32 elements, E8M0 scale): e = smallest integer with
-// amax <= 6 * 2^e (clamped to [-127, 127]); code = nearest E2M1 magnitude of
-// |x| 2^-e with ties to the even mantissa; bit 3 = sign of x.
-void quant_mxfp4_group(const float* x, uint8_t* nib, uint8_t* scale_byte) {
+// amax <= 6 * 2^e (clamped to [-127, 127]), or with the OCP rule
+// e = floor(log2(amax)) - 2; code = nearest E2M1 magnitude of |x| 2^-e with
+// ties to the even mantissa, saturated at 6 (only the OCP rule reaches it);
+// bit 3 = sign of x.
+void quant_mxfp4_group(const float* x, uint8_t* nib, uint8_t* scale_byte, bool ocp_rule) {
   float amax = 0.0f;
   for (int i = 0; i < 32; ++i) amax = std::max(amax, std::fabs(x[i]));
   int e;
@@ -179,8 +181,8 @@ void quant_mxfp4_group(const float* x, uint8_t* nib, uint8_t* scale_byte) {
     e = -127;
   } else {
     int E;
-    const float f = std::frexp(amax, &E);
-    e = f <= 0.75f ? E - 3 : E - 2;
+    const float f = std::frexp(amax, &E);   // amax = f 2^E, 0.5 <= f < 1
+    e = ocp_rule ? E - 3 : (f <= 0.75f ? E - 3 : E - 2);
     e = std::min(127, std::max(-127, e));
   }
   *scale_byte = (uint8_t)(e + 127);
@@ -320,7 +322,7 @@ svdq_status svdq_pack_host(const float* x, int32_t rows, int32_t K, int32_t fmt,
           quant_int4_group(src, nib, &sb);
           std::memcpy(scales + ((size_t)r * (K / 64) + g) * 2, &sb, 2);
         } else {
-          quant_mxfp4_group(src, nib, scales + (size_t)r * (K / 32) + g);
+          quant_mxfp4_group(src, nib, scales + (size_t)r * (K / 32) + g, fmt == SVDQ_MXFP4_G32_OCP);
         }
         uint8_t* dst = codes + (size_t)r * (K / 2) + (size_t)g * (G / 2);
         for (int i = 0; i < G / 2; ++i) dst[i] = (uint8_t)(nib[2 * i] | (nib[2 * i + 1] << 4));
@@ -614,7 +616,7 @@ svdq_status svdq_kernel_layout(int32_t K, int32_t N, int32_t rank, int32_t fmt, 
         for (int32_t k = 0; k < K; ++k) wq_k[code_offset((int)n, k >> 6, k & 63, cs)] = wq[(size_t)n * K + k];
     });
     std::memcpy(ws_k, ws, (size_t)N * 4);
-  } else if (fmt == SVDQ_MXFP4_G32) {
+  } else if (is_mx(fmt)) {
     // codes: tiled 1 KB units
     parallel_for(N, default_threads(0), [&](int64_t lo, int64_t hi) {
       for (int64_t n = lo; n < hi; ++n)
@@ -695,7 +697,7 @@ svdq_status svdq_unpack_activations(const void* ws_host, int32_t M, int32_t K, i
     for (int32_t m = 0; m < M; ++m)
       for (int32_t k = 0; k < K; ++k) xq[(size_t)m * K + k] = q[code_offset(m, k >> 6, k & 63, cs)];
     std::memcpy(xs, base + L.xs_off, (size_t)M * 4);
-  } else if (fmt == SVDQ_MXFP4_G32) {
+  } else if (is_mx(fmt)) {
     for (int32_t m = 0; m < M; ++m)
       for (int32_t t = 0; t < steps; ++t)
         for (int b = 0; b < 64; ++b) xq[(size_t)m * (K / 2) + (size_t)t * 64 + b] = q[code_offset(m, t, b, steps)];

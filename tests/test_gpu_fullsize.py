@@ -98,6 +98,11 @@ def test_flux_mlp_up_mxfp4():
     _check("flux_mlp_up", "mxfp4")
 
 
+def test_flux_mlp_up_mxfp4_ocp_rule():
+    # the OCP shared-exponent rule (saturating) on the same layer
+    _check("flux_mlp_up", "mxfp4_ocp")
+
+
 @pytest.mark.parametrize("alpha", [0.3, 0.5, 0.7])
 def test_flux_mlp_down_int4_alpha(alpha):
     _check("flux_mlp_down", "int4", alpha=alpha)

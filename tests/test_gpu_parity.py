@@ -35,7 +35,7 @@ def _check_full(run, po, x, bias, z_tol=2e-5):
     return err
 
 
-@pytest.mark.parametrize("fmt", ["int4", "mxfp4", "w8a8"])
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4", "w8a8", "mxfp4_ocp"])
 @pytest.mark.parametrize("use_bias", [True, False])
 def test_tiny_layer(fmt, use_bias):
     s = S.spec("tiny", fmt=fmt)
@@ -65,7 +65,7 @@ def test_shapes_and_tails(fmt, M, K, N, rank):
     _check_full(run, po, d["X"], d["bias"])
 
 
-@pytest.mark.parametrize("fmt", ["int4", "mxfp4", "w8a8"])
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4", "w8a8", "mxfp4_ocp"])
 def test_lora_rank48(fmt):
     s = S.spec("flux_lora", M=200, K=512, N=640, fmt=fmt)
     d = S.make_layer(s)
@@ -75,7 +75,7 @@ def test_lora_rank48(fmt):
     _check_full(run, po, d["X"], d["bias"])
 
 
-@pytest.mark.parametrize("fmt", ["int4", "mxfp4", "w8a8"])
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4", "w8a8", "mxfp4_ocp"])
 def test_quantizer_edge_values(fmt):
     """Zero rows, bf16 subnormals (MXFP4 scale clamped at 2^-127; 8-bit
     scale below 2^-128), huge values (an INT4 scale past the fp16 range,
@@ -90,6 +90,8 @@ def test_quantizer_edge_values(fmt):
     x[4, :32] = S.to_bf16_values(np.array([7.0, 2.5, -2.5, 0.5, -0.5, 1.5, 3.5, -6.5] * 4))
     x[5] = S.to_bf16_values(S.random_bf16(6, (K,), 1.0) * 1e30)
     x[6, :] = S.to_bf16_values(np.full(K, 1e-36))
+    x[7, :32] = 7.0                                                 # OCP rule: a saturated block
+    x[7, 32:64] = S.to_bf16_values(np.linspace(-7.9, 7.9, 32))
     d = {"spec": S.spec("tiny"), "X": x, "X_cal": np.abs(x) + 1.0,
          "W": S.random_bf16(7, (K, N), 0.05), "bias": S.random_bf16(8, (N,), 0.1)}
     run = GpuRun(d, fmt, 0, 0.5).forward()
@@ -114,7 +116,7 @@ def test_workspace_reuse_and_determinism():
     assert bool((run.Y == y1).all())
 
 
-@pytest.mark.parametrize("fmt", ["int4", "mxfp4", "w8a8"])
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4", "w8a8", "mxfp4_ocp"])
 @pytest.mark.parametrize("M,K,N,rank", [(300, 1024, 400, 32), (17, 512, 272, 48), (130, 640, 144, 0)])
 def test_unfused_baseline(fmt, M, K, N, rank):
     """The four-kernel baseline computes the same layer: within the

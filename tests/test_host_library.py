@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = B.lib()
     for n in sorted(names):
         assert hasattr(lib, n), n
-    assert B.abi_version() == B.ABI_VERSION == 7
+    assert B.abi_version() == B.ABI_VERSION == 8
     assert B.status_str(0) == "ok"
 
 
@@ -34,7 +34,7 @@ def _oracle_scales(ws, fmt):
     return np.float16(ws).view(np.uint16) if fmt == "int4" else ws
 
 
-@pytest.mark.parametrize("fmt", ["int4", "mxfp4", "w8a8"])
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4", "w8a8", "mxfp4_ocp"])
 def test_packer_bit_exact_against_oracle(fmt):
     rng = np.random.default_rng(3)
     x = (rng.standard_t(3, (64, 1024)) * 0.7).astype(np.float32)
@@ -52,6 +52,9 @@ def test_packer_bit_exact_against_oracle(fmt):
     x[9, :64] *= 1e30                                # INT4 scale past the fp16 range: saturated at 65504
     x[9, 64] = 7 * 65520.0                           # exactly at the fp16 overflow threshold
     x[9, 128] = 7 * 65519.0                          # just below it
+    x[10, :32] = 7.0                                 # OCP rule: e = 0, every element saturates to 6
+    x[10, 32:64] = np.linspace(-6.0, 6.0, 32)        # amax exactly 6: e = 0 under both rules
+    x[10, 64:96] = np.float32(7.99)                  # just below 8
     codes, scales = B.pack_host(x, fmt)
     q = Q.quantize(x, fmt)
     assert np.array_equal(codes, q["packed"])
@@ -215,7 +218,7 @@ def test_error_codes_device_entry_points_validate_before_hip():
     assert uf(C.byref(L), 0x1000, 64, 0x2000, 0x3000, ws - 1, None) == 5
     bad = B.binding.Layer(256, 256, 40, 1, 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, None)
     assert lib.svdq_quantize_lora_down(C.byref(bad), 0x1000, 64, 0x3000, ws, None) == 2
-    badf = B.binding.Layer(256, 256, 32, 3, 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, None)
+    badf = B.binding.Layer(256, 256, 32, 4, 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, None)
     assert lib.svdq_gemm_lora_up(C.byref(badf), 0x3000, ws, 64, 0x2000, None) == 4
     mis = B.binding.Layer(256, 256, 32, 1, 0x1004, 0x2000, 0x3000, 0x4000, 0x5000, None)
     assert lib.svdq_gemm_lora_up(C.byref(mis), 0x3000, ws, 64, 0x2000, None) == 3
