@@ -441,6 +441,11 @@ PROFILE_STEPS = {
              "python -u bench.py --config {config} --steps 3 --warmup 1 --skip-oracle --calib-copy",
     "mfma": "--pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_WAVES --output-format csv "
             "-d {dir}/mfma -o run -- python -u bench.py --config {config} --steps 3 --warmup 1 --skip-oracle",
+    "waves": "--pmc SQ_WAVES SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_BUSY_CYCLES SQ_INSTS_VMEM_RD "
+             "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE --output-format csv "
+             "-d {dir}/waves -o run -- python -u bench.py --config {config} --steps 3 --warmup 1 --skip-oracle",
+    "l2": "--pmc TCC_HIT_sum TCC_MISS_sum TCC_EA0_RDREQ_sum GRBM_GUI_ACTIVE --output-format csv "
+          "-d {dir}/l2 -o run -- python -u bench.py --config {config} --steps 3 --warmup 1 --skip-oracle",
 }
 
 
@@ -747,6 +752,12 @@ def summarize_profiles(d, config, fmt_override=None):
     print("\n".join(lines))
     if os.path.isdir(os.path.join(d, "mfma")):
         summarize_mfma(d, key, M, N, K, r, fmt, kb_names, kb_avg, cmds["mfma"], short)
+    if os.path.isdir(os.path.join(d, "waves")) and os.path.isdir(os.path.join(d, "l2")):
+        ka_avg = next((float(col(row, "AverageNs")) / 1e3 for row in rows
+                       if _matches(col(row, "Name", "KernelName"), ka_names)), None)
+        summarize_waves(d, key, M, N, K, r, fmt, {"K-A (ka_kernel)": (ka_names, ka_avg),
+                                                   f"K-B ({kb_names[0]})": (kb_names, kb_avg)},
+                        (cmds["waves"], cmds["l2"]))
 
 
 def summarize_mfma(d, key, M, N, K, r, fmt, kb_names, kb_avg, cmd, short):
@@ -788,6 +799,54 @@ def summarize_mfma(d, key, M, N, K, r, fmt, kb_names, kb_avg, cmd, short):
                      (f"; GRBM_GUI_ACTIVE per XCD ({xcc}) over the same: "
                       f"{mean['GRBM_GUI_ACTIVE'] / xcc / (kb_avg * 1e3):.2f} GHz." if xcc else "."))
     _write(os.path.join(ROOT, "profiles", f"{short}_{key}_mfma.md"), "\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_waves(d, key, M, N, K, r, fmt, kernels, cmds):
+    """Residency, waiting and cache behaviour of K-A and K-B from counters.
+    SQ_WAVE_CYCLES and SQ_WAIT_* count wave-cycles in the same unit, so their
+    ratio is the share of a resident wave's life spent waiting (on anything,
+    or on an s_waitcnt); SQ_WAVE_CYCLES over the engines' busy cycles and the
+    CU count gives the mean number of resident waves per CU in that unit
+    (one wave-cycle is counted per 4 clocks on this agent when the figure
+    comes out a quarter of the launch's known waves per CU). TCC_HIT /
+    (TCC_HIT + TCC_MISS) is the L2 hit rate of the kernel's requests."""
+    agent = [a for a in _csv(_find(os.path.join(d, "waves"), "agent_info.csv")) if int(a.get("Simd_Count", 0) or 0) > 0]
+    engines = int(agent[0]["Num_Shader_Banks"])
+    cus = int(agent[0].get("Cu_Count", 0) or 0) or 256
+    lines = [f"# Residency, waits and L2 hits of K-A and K-B, {key} (M={M} K={K} N={N} rank={r} {fmt})", "",
+             "Commands (from the repository root, TMPDIR=/tmp):", "", "    " + cmds[0], "    " + cmds[1], ""]
+    for label, (names, avg) in kernels.items():
+        vals = {}
+        grid = wg = None
+        for which in ("waves", "l2"):
+            for row in _csv(_find(os.path.join(d, which), "counter_collection.csv")):
+                if _matches(row["Kernel_Name"], names):
+                    vals.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+                    grid, wg = int(row["Grid_Size"]), int(row["Workgroup_Size"])
+        if not vals:
+            continue
+        m = {k: float(np.mean(v)) for k, v in vals.items()}
+        busy_se = m["SQ_BUSY_CYCLES"] / engines
+        waves_per_cu = m["SQ_WAVE_CYCLES"] / busy_se / cus
+        hit = m["TCC_HIT_sum"] / max(1.0, m["TCC_HIT_sum"] + m["TCC_MISS_sum"])
+        lines += [f"## {label}", "",
+                  f"Launch: {grid // wg} workgroups of {wg // 64} waves ({grid // 64} waves, "
+                  f"{grid // 64 / cus:.2f} per CU). Means over {len(vals['SQ_WAVES'])} dispatches.", "",
+                  "| counter | per dispatch |", "|---|---|"]
+        lines += [f"| {k} | {v:.4g} |" for k, v in sorted(m.items())]
+        lines += ["",
+                  f"- waiting (any) / wave-cycles: {m['SQ_WAIT_ANY'] / m['SQ_WAVE_CYCLES']:.3f}",
+                  f"- waiting on s_waitcnt / wave-cycles: {m['SQ_WAIT_INST_ANY'] / m['SQ_WAVE_CYCLES']:.3f}",
+                  f"- wave-cycles per CU per engine-busy cycle: {waves_per_cu:.2f}",
+                  f"- LDS bank-conflict cycles / LDS-active cycles: "
+                  f"{m['SQ_LDS_BANK_CONFLICT'] / max(1.0, m['SQ_LDS_IDX_ACTIVE']):.3f}",
+                  f"- L2 hit rate: {hit:.3f}; L2-to-memory read requests: {m['TCC_EA0_RDREQ_sum']:.4g}"]
+        if avg:
+            lines.append(f"- engine-busy clock over the kernel-trace average ({avg:.2f} us): "
+                         f"{busy_se / (avg * 1e3):.2f} GHz")
+        lines.append("")
+    _write(os.path.join(ROOT, "profiles", f"ka_kb_{key}_waves.md"), "\n".join(lines))
     print("\n".join(lines))
 
 
