@@ -22,7 +22,7 @@ def test_profile_commands_name_committed_files_only():
     r = _run("--print-profile-commands", "gpurun_out/prof_x")
     assert r.returncode == 0, r.stderr
     lines = [l.split("\t") for l in r.stdout.strip().splitlines()]
-    assert [k for k, _ in lines] == ["stats", "fetch", "write", "mfma"]
+    assert [k for k, _ in lines] == ["stats", "fetch", "write", "mfma", "waves", "l2"]
     for _, cmd in lines:
         assert cmd.startswith("rocprofv3 ") and " -- python -u bench.py " in cmd
         assert "_work" not in cmd
@@ -30,3 +30,7 @@ def test_profile_commands_name_committed_files_only():
     for k, cmd in lines:
         if k != "stats":
             assert "--pmc" in cmd and "--kernel-trace" not in cmd and "--sys-trace" not in cmd
+            counters = cmd.split("--pmc ")[1].split(" --")[0].split()
+            assert sum(c.startswith("SQ_") for c in counters) <= 8
+            assert sum(c.startswith("TCC_") for c in counters) <= 4
+            assert sum(c.startswith("GRBM_") for c in counters) <= 2
