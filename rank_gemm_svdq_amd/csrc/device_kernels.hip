@@ -19,21 +19,22 @@
 //
 // Layouts (offsets in layout.h; K split into steps of 64 code bytes per
 // row: 128 4-bit elements or 64 int8 elements):
-//   Codes (activations and weights, every format): 1 KB units of 16 rows x
-//     one step, ordered [row / 16][step]; inside a unit, 16-byte slot
-//     4 (row % 16) + q holds chunk q ^ swz(row % 32) of the row-step.  MXFP4
-//     and W8A8 keep canonical byte order inside a row-step; INT4 places
-//     element k (G = k / 64, g = k % 64 / 16, j = k % 16) at byte
-//     16 g + 8 G + j / 2, nibble j % 2, so the 16 bytes of lane group g
-//     hold 16 elements of each of the step's two 64-element groups.
-//   Scale records (MXFP4 both operands, INT4 activations): 1 KB units of 64
-//     rows x 4 steps ordered [row / 64][4-step group]; dword d of row r sits
-//     at unit dword 64 (r % 64 / 16) + 16 d + r % 16.  MXFP4: dword d holds
-//     the E8M0 scales of 32-element block d of the 4 steps (byte t % 4), the
-//     weight rows permuted inside their 64-row group (wrec_row); INT4: dword
-//     t % 4 is the fp16 pair of step t.
-//   INT4 weight scales: 2 KB units of 128 rows x 4 steps, [4-row block]
-//     [step % 4][row % 4][group of 64] fp16.
+//   Codes (MXFP4 and W8A8, activations and weights): 1 KB units of 16 rows
+//     x one step, ordered [row / 16][step]; inside a unit, 16-byte slot
+//     4 (row % 16) + q holds chunk q ^ swz(row % 32) of the row-step, in
+//     canonical byte order.
+//   INT4 codes: FP6 E2M3 (exact for -7..7), 32 six-bit codes of a 32-element
+//     slice s = 2 G + h packed in 6 dwords; dwords 0-3 of each slice in
+//     1 KB units of 16 rows x one step (slot 4 (row % 16) + (s ^ i4_swz)),
+//     dwords 4-5 after all of them in 1 KB units of 32 rows x one step.
+//   Scale records (MXFP4, both operands): 1 KB units of 64 rows x 4 steps
+//     ordered [row / 64][4-step group]; dword d of row r sits at unit dword
+//     64 (r % 64 / 16) + 16 d + r % 16 and holds the E8M0 scales of
+//     32-element block d of the 4 steps (byte t % 4); the weight rows are
+//     permuted inside their 64-row group (wrec_row).
+//   INT4 scales: 512-byte units of 128 rows x one step, [row / 128][step]:
+//     per token row one dword (the fp16 pair of the step's two groups), per
+//     out-feature fp16 index 128 G + row % 128.
 //   W8A8 scales: fp32 per token row (workspace) and per out-feature (layer).
 //   Down factor: L1' (bf16), ordered [step][s][n-tile < rank/16][lane][8]
 //     with k = 128 step + 32 (lane/16) + 8 s + i, n = 16 n-tile + lane % 16.
@@ -61,6 +62,8 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v6i __attribute__((ext_vector_type(6)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -928,7 +931,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
 constexpr int I4_BM = 128, I4_BN = 128, I4_WAVES = 4, I4_THREADS = 64 * I4_WAVES;
 // step buffer: token main | weight main | token tails | weight tails | token scales | weight scales
 constexpr int I4_BMAIN = 0, I4_AMAIN = 8192, I4_BTAIL = 16384, I4_ATAIL = 20480, I4_BSC = 24576, I4_ASC = 25088;
-constexpr int I4_STEP_BYTES = 25600;
+// then 512 zero bytes that no load writes: lanes 32-63 read their (zero)
+// scale-product operands there, so the loop selects nothing per lane
+constexpr int I4_ZPAD = 25600, I4_STEP_BYTES = 26112;
 constexpr int I4_LDS = 2 * I4_STEP_BYTES;
 // after the K loop: Z (128 rows x 32 hi + 32 lo bf16) in buffer 0, L2' (128 rows x 32 bf16) in buffer 1
 constexpr int I4_Z0 = 0, I4_L20 = I4_STEP_BYTES;
@@ -1022,6 +1027,13 @@ __global__ __launch_bounds__(I4_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
     }
   };
 
+  // the zero pads of both step buffers (visible after the loop's first barrier)
+  if (tid < 2 * 128) *reinterpret_cast<uint32_t*>(lds + (tid >> 7) * I4_STEP_BYTES + I4_ZPAD + 4 * (tid & 127)) = 0u;
+  // scale offsets inside a step buffer: a token row's fp16 pair (+ 128 per
+  // token tile) and a weight row's fp16 (+ 64 per weight tile, + 256 per
+  // group); lanes 32-63 point at the zero pad
+  const uint32_t sxo = h ? (uint32_t)I4_ZPAD : (uint32_t)(I4_BSC + 4 * (64 * wm + l32));
+  const uint32_t swo = h ? (uint32_t)I4_ZPAD : (uint32_t)(I4_ASC + 2 * (64 * wn + i4_nrow(l32)));
   // fragment offsets inside a step buffer, per tile and group G: the main
   // part of slice 2 G + h of the row, and its tail
   uint32_t amain[2][2], atail[2], bmain[2][2], btail[2];
@@ -1043,7 +1055,11 @@ __global__ __launch_bounds__(I4_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
   };
   auto frag = [&](uint32_t bo, uint32_t mo, uint32_t to) __attribute__((always_inline)) -> v8i {
     const v4i m4 = *reinterpret_cast<const v4i*>(lds + bo + mo);
-    const uint2 t2 = *reinterpret_cast<const uint2*>(lds + bo + to);
+    // an opaque address per tail read keeps the compiler from merging two
+    // tails into one ds_read2 and then copying them into the operands
+    uint32_t ta = bo + to;
+    asm volatile("" : "+v"(ta));
+    const uint2 t2 = *reinterpret_cast<const uint2*>(lds + ta);
     return (v8i){m4[0], m4[1], m4[2], m4[3], (int)t2.x, (int)t2.y, 0, 0};
   };
 
@@ -1067,7 +1083,7 @@ __global__ __launch_bounds__(I4_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
     uint32_t sx[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
-      sx[mt] = *reinterpret_cast<const uint32_t*>(lds + bo + I4_BSC + 4 * (64 * wm + 32 * mt + l32));
+      sx[mt] = *reinterpret_cast<const uint32_t*>(lds + bo + sxo + 128 * mt);
 #pragma unroll
     for (int G = 0; G < 2; ++G) {
       v8i af[2], bf[2];
@@ -1076,20 +1092,21 @@ __global__ __launch_bounds__(I4_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
         af[i] = frag(bo, amain[i][G], atail[i] + 512 * G);
         bf[i] = frag(bo, bmain[i][G], btail[i] + 512 * G);
       }
-      // operands of the scale-product MFMA (32x32x16 f16, K slot 0 only):
+      // operands of the scale-product MFMA (32x32x8 f16, K slot 0 only):
       // lanes 0-31 hold the fp16 scale of their weight row (MFMA row order)
-      // or token in element 0, every other element is zero, so the product
-      // is the outer product sw x sx, exact in fp32
-      v8h pa[2], pb[2];
+      // or token in element 0, every other element is zero (lanes 32-63
+      // read the zero pad), so the product is the outer product sw x sx,
+      // exact in fp32
+      v4h pa[2], pb[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const uint32_t w = *reinterpret_cast<const uint16_t*>(lds + bo + I4_ASC + 256 * G + 2 * (64 * wn + 32 * nt + i4_nrow(l32)));
-        pa[nt] = __builtin_bit_cast(v8h, (v4i){(int)(h == 0 ? w : 0u), 0, 0, 0});
+        const uint32_t w = *reinterpret_cast<const uint16_t*>(lds + bo + swo + 256 * G + 64 * nt);
+        pa[nt] = __builtin_bit_cast(v4h, (v2i){(int)w, 0});
       }
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         const uint32_t x = G == 0 ? (sx[mt] & 0xFFFFu) : (sx[mt] >> 16);
-        pb[mt] = __builtin_bit_cast(v8h, (v4i){(int)(h == 0 ? x : 0u), 0, 0, 0});
+        pb[mt] = __builtin_bit_cast(v4h, (v2i){(int)x, 0});
       }
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
@@ -1097,7 +1114,7 @@ __global__ __launch_bounds__(I4_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
         for (int mt = 0; mt < 2; ++mt) {
           const v16f I = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[nt], bf[mt], (v16f){}, 2, 2, 0, 127, 0,
                                                                           127);
-          const v16f P = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[nt], pb[mt], (v16f){}, 0, 0, 0);
+          const v16f P = __builtin_amdgcn_mfma_f32_32x32x8f16(pa[nt], pb[mt], (v16f){}, 0, 0, 0);
 #pragma unroll
           for (int i = 0; i < 16; ++i) acc[nt][mt][i] = __builtin_fmaf(I[i], P[i], acc[nt][mt][i]);
         }
