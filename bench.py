@@ -144,7 +144,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="flux_mlp_up")
-    ap.add_argument("--fmt", default=None, help="override the workload's format (int4 | mxfp4)")
+    ap.add_argument("--fmt", default=None, help="override the workload's format (int4 | mxfp4 | mxfp4_ocp | w8a8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rotate", action="store_true",
                     help="skip the cache-rotated run (distinct buffer sets cycled per step)")
@@ -365,8 +365,7 @@ def main():
         "kernel_us_spread": {"ka": [float(ka.min()) * 1e3, float(np.median(ka)) * 1e3, float(ka.max()) * 1e3],
                              "kb": [float(kb.min()) * 1e3, float(np.median(kb)) * 1e3, float(kb.max()) * 1e3],
                              "order": "min, median, max"},
-        "cache_state": "warm: the layer's X, weights, workspace and Y (about 150 MB for this workload) stay in "
-                       "the 256 MB last-level cache across back-to-back steps; see 'rotated' for a cold-cache run",
+        "cache_state": working_set_note(X, M, N, prep, layer),
         "rotated": rotated,
         "lowrank_overhead": t_stepr / t_step0 - 1.0, "rank0_layer_us": t_step0 * 1e6,
         "layer_us_interleaved": t_stepr * 1e6,
@@ -380,6 +379,21 @@ def main():
     print(json.dumps(out))
 
 
+def working_set_note(X, M, N, prep, layer):
+    """How much of one step's data the 256 MB last-level cache can hold
+    across back-to-back steps (the warm headline's residency)."""
+    import rank_gemm_svdq_amd as B
+    per = X.numel() * 2 + M * N * 2 + B.workspace_bytes(M, prep["K"], prep["rank"], prep["fmt"])
+    per += sum(t.numel() * t.element_size() for t in (layer.wq, layer.ws, layer.l1k, layer.l2k, layer.smooth_inv)
+               if t is not None)
+    mb = per / 1e6
+    if per <= (256 << 20):
+        return (f"warm: the layer's X, weights, workspace and Y ({mb:.0f} MB) fit in the 256 MB last-level cache "
+                f"across back-to-back steps; see 'rotated' for a cold-cache run")
+    return (f"partly warm: the layer's X, weights, workspace and Y ({mb:.0f} MB) exceed the 256 MB last-level "
+            f"cache; see 'rotated' for a cold-cache run")
+
+
 def rotated_run(args, torch, B, prep, bias_bits, X, M, N, stream):
     """The same forward with the last-level cache defeated: several complete
     sets of X, layer buffers, workspace and Y (distinct device memory, same
@@ -388,7 +402,8 @@ def rotated_run(args, torch, B, prep, bias_bits, X, M, N, stream):
     time as one timed region and per-kernel medians."""
     per_set = X.numel() * 2 + M * N * 2 + B.workspace_bytes(M, prep["K"], prep["rank"], prep["fmt"])
     lay0 = B.DeviceLayer(prep, bias_bits)
-    per_set += sum(t.numel() * t.element_size() for t in (lay0.wq, lay0.ws, lay0.l1k, lay0.l2k, lay0.smooth_inv))
+    per_set += sum(t.numel() * t.element_size() for t in (lay0.wq, lay0.ws, lay0.l1k, lay0.l2k, lay0.smooth_inv)
+                   if t is not None)
     n = args.rotate_sets or max(3, -(-(512 << 20) // per_set))
     sets = []
     for i in range(n):
