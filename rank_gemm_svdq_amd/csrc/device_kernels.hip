@@ -1036,6 +1036,9 @@ __global__ __launch_bounds__(I4_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
   const uint32_t swo = h ? (uint32_t)I4_ZPAD : (uint32_t)(I4_ASC + 2 * (64 * wn + i4_nrow(l32)));
   // fragment offsets inside a step buffer, per tile and group G: the main
   // part of slice 2 G + h of the row, and its tail
+  // (the second tile's main parts sit 2048 bytes after the first's: the
+  // loop forms one base per operand, group and step and reaches the second
+  // tile through the LDS instruction's immediate offset)
   uint32_t amain[2][2], atail[2], bmain[2][2], btail[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -1054,7 +1057,7 @@ __global__ __launch_bounds__(I4_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
     return bo;
   };
   auto frag = [&](uint32_t bo, uint32_t mo, uint32_t to) __attribute__((always_inline)) -> v8i {
-    const v4i m4 = *reinterpret_cast<const v4i*>(lds + bo + mo);
+    const v4i m4 = *reinterpret_cast<const v4i*>(lds + mo);
     // an opaque address per tail read keeps the compiler from merging two
     // tails into one ds_read2 and then copying them into the operands
     uint32_t ta = bo + to;
@@ -1079,18 +1082,23 @@ __global__ __launch_bounds__(I4_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
     __syncthreads();
     if (t + 1 < steps) issue_step(t + 1);
     const uint32_t bo = buf_of(t);
+    // this step's bases of the main parts (per operand and group) and of the
+    // scales; the tails keep one address per read (frag)
+    uint32_t vam[2] = {bo + amain[0][0], bo + amain[0][1]}, vbm[2] = {bo + bmain[0][0], bo + bmain[0][1]};
+    uint32_t vsx = bo + sxo, vsw = bo + swo;
+    asm volatile("" : "+v"(vam[0]), "+v"(vam[1]), "+v"(vbm[0]), "+v"(vbm[1]), "+v"(vsx), "+v"(vsw));
     // token scales: the fp16 pair (group 0, group 1) of the lane's token per tile
     uint32_t sx[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
-      sx[mt] = *reinterpret_cast<const uint32_t*>(lds + bo + sxo + 128 * mt);
+      sx[mt] = *reinterpret_cast<const uint32_t*>(lds + vsx + 128 * mt);
 #pragma unroll
     for (int G = 0; G < 2; ++G) {
       v8i af[2], bf[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        af[i] = frag(bo, amain[i][G], atail[i] + 512 * G);
-        bf[i] = frag(bo, bmain[i][G], btail[i] + 512 * G);
+        af[i] = frag(bo, vam[G] + 2048 * i, atail[i] + 512 * G);
+        bf[i] = frag(bo, vbm[G] + 2048 * i, btail[i] + 512 * G);
       }
       // operands of the scale-product MFMA (32x32x8 f16, K slot 0 only):
       // lanes 0-31 hold the fp16 scale of their weight row (MFMA row order)
@@ -1100,7 +1108,7 @@ __global__ __launch_bounds__(I4_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
       v4h pa[2], pb[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const uint32_t w = *reinterpret_cast<const uint16_t*>(lds + bo + swo + 256 * G + 64 * nt);
+        const uint32_t w = *reinterpret_cast<const uint16_t*>(lds + vsw + 256 * G + 64 * nt);
         pa[nt] = __builtin_bit_cast(v4h, (v2i){(int)w, 0});
       }
 #pragma unroll
