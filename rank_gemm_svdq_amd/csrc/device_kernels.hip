@@ -913,16 +913,17 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
 // The codes are FP6 E2M3 values (INT4 -7..7 exactly), the operands of the
 // scaled 32x32x64 MFMA (unit E8M0 scales), whose K extent is one 64-element
 // group: one MFMA gives the group's exact integer dot product I as fp32.  A
-// second MFMA (32x32x16 f16 with one non-zero K slot) gives the outer
+// second MFMA (32x32x8 f16 with one non-zero K slot) gives the outer
 // product P = sw x sx of the group's fp16 scales, exact in fp32 and in the
 // same register layout, and the accumulator takes fma(I, P, acc): one VALU
 // operation per output and group.  (The per-group fp16 scales are not
 // powers of two, so they cannot ride in the MFMA's block scales.)
 //
 // Each step (128 elements = 2 groups) travels global -> LDS by direct-to-LDS
-// loads into a ring of two 25 KB step buffers, one step ahead: the code main
-// parts (16 + 16 units of 1 KB), the code tails (4 + 4 units) and the
-// step's scales (512 B of token rows, 512 B of weight rows).
+// loads into a ring of two 25.5 KB step buffers, one step ahead: the code
+// main parts (16 + 16 units of 1 KB), the code tails (4 + 4 units) and the
+// step's scales (512 B of token rows, 512 B of weight rows), followed by a
+// 512-byte zero pad that no load writes.
 //
 // Weight rows are read in a permuted order inside each 32-row tile: MFMA row
 // q holds out-feature i4_nrow(q), so the 16 accumulators a lane holds for a
