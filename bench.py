@@ -676,7 +676,7 @@ def summarize_profiles(d, config, fmt_override=None):
     ka_names = ("ka_kernel",)
     short = {"mxfp4": "kb_mx", "mxfp4_ocp": "kb_mx", "int4": "kb_int4", "w8a8": "kb_w8a8"}[fmt]
     key = s.name if not fmt_override else f"{s.name}_{fmt}"
-    cmds = profile_commands("gpurun_out/prof_" + key, config + (f" --fmt {fmt_override}" if fmt_override else ""))
+    cmds = profile_commands(os.path.normpath(d), config + (f" --fmt {fmt_override}" if fmt_override else ""))
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
 
     # kernel stats

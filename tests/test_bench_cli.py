@@ -19,7 +19,7 @@ def test_more_than_one_gpu_exits_with_a_message():
 
 
 def test_profile_commands_name_committed_files_only():
-    r = _run("--print-profile-commands", "gpurun_out/prof_x")
+    r = _run("--print-profile-commands", "prof_out/x")
     assert r.returncode == 0, r.stderr
     lines = [l.split("\t") for l in r.stdout.strip().splitlines()]
     assert [k for k, _ in lines] == ["stats", "fetch", "write", "mfma", "waves", "l2"]
