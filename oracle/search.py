@@ -36,8 +36,9 @@ S4  Reading: Algorithm R (Vitter, "Random sampling with a reservoir", ACM
 Pins (tests/test_oracle_search.py): the candidate set against the pages'
 count and description, the selection rule on hand-made score lists, an
 exactly representable layer for which only (0, 0) is lossless, an
-outlier-activation layer for which smoothing must win, and the reservoir's
-inclusion frequencies (k / n for every call) over many seeds.
+outlier-activation layer for which smoothing must win, the reservoir's
+inclusion frequencies (k / n for every call) over many seeds, and SplitMix64
+against its published first outputs for two seeds (tests/golden/splitmix64.json).
 """
 
 import numpy as np

@@ -151,3 +151,16 @@ def test_splitmix64_is_a_bijective_mixer_on_small_states():
     # and the output bits are balanced
     bits = np.array([[(SR.splitmix64(s)[1] >> b) & 1 for b in range(64)] for s in range(2000)])
     assert np.all(np.abs(bits.mean(0) - 0.5) < 0.06)
+
+
+def test_splitmix64_reproduces_the_published_outputs():
+    # tests/golden/splitmix64.json: the generator's first outputs for two
+    # seeds as published with its reference implementations
+    import json, os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "splitmix64.json")) as fh:
+        golden = json.load(fh)
+    for seed, outs in golden["outputs"].items():
+        state = int(seed)
+        for want in outs:
+            state, got = SR.splitmix64(state)
+            assert got == int(want, 0), (seed, hex(got), want)
