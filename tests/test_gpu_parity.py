@@ -116,6 +116,42 @@ def test_workspace_reuse_and_determinism():
     assert bool((run.Y == y1).all())
 
 
+def _rows_past_one_block_per_cu():
+    # more 16-row K-A blocks than compute units (ragged last block): K-A runs
+    # its ring-free variant, two blocks per unit
+    import torch
+    return 16 * torch.cuda.get_device_properties(0).multi_processor_count + 17
+
+
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4", "mxfp4_ocp"])
+@pytest.mark.parametrize("rank", [16, 32, 48])
+def test_more_ka_blocks_than_compute_units(fmt, rank):
+    M = _rows_past_one_block_per_cu()
+    s = S.spec("tiny", M=M, K=512, N=256, rank=rank, fmt=fmt)
+    d = S.make_layer(s)
+    run = GpuRun(d, fmt, rank, s.alpha).forward()
+    po = oracle_layer(d, fmt, rank, s.alpha)
+    _check_full(run, po, d["X"], d["bias"])
+
+
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+def test_more_ka_blocks_than_compute_units_unfused(fmt):
+    """The unfused baseline's separate down-projection pass at the same
+    token count."""
+    import torch
+    M = _rows_past_one_block_per_cu()
+    s = S.spec("tiny", M=M, K=384, N=144, rank=32, fmt=fmt)
+    d = S.make_layer(s)
+    run = GpuRun(d, fmt, 32, s.alpha).forward()
+    y_fused = run.y()
+    B.linear_forward_unfused(run.layer, run.X, run.Y, run.ws)
+    torch.cuda.synchronize()
+    po = oracle_layer(d, fmt, 32, s.alpha)
+    of = F.forward(d["X"], po, d["bias"])
+    assert rel_fro(run.y(), of["y"]) <= Y_TOL
+    assert rel_fro(run.y(), y_fused) <= 4e-3
+
+
 @pytest.mark.parametrize("fmt", ["int4", "mxfp4", "w8a8", "mxfp4_ocp"])
 @pytest.mark.parametrize("M,K,N,rank", [(300, 1024, 400, 32), (17, 512, 272, 48), (130, 640, 144, 0)])
 def test_unfused_baseline(fmt, M, K, N, rank):
