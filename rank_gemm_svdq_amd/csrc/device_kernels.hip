@@ -75,6 +75,25 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
   return u >> 16;
 }
 
+#define SVDQ_AS3 __attribute__((address_space(3)))
+
+// One wave-wide 1 KB direct-to-LDS copy: lane i's 16 bytes at sbase + voff
+// (sbase wave-uniform, voff per lane) land at LDS byte lds_base + 16 i.
+// Issued from asm so that the compiler does not serialise it against
+// unrelated LDS reads; completion is tracked with explicit vmcnt waits.
+// M0 is restored before the asm block ends.
+__device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(sbase)
+      : "memory");
+}
+
 // ----------------------------------------------------------------- K-A
 
 constexpr int KA_WAVES = 8;
@@ -138,13 +157,20 @@ __global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __res
     }
   };
   if constexpr (SL) {
-    for (int i = 4 * (int)threadIdx.x; i < K; i += 4 * 64 * KA_WAVES)
-      *reinterpret_cast<v4f*>(svl + i) = *reinterpret_cast<const v4f*>(sinv + i);
+    // each wave stages 1/lambda of its own steps, 128 (t1 - t0) floats, by
+    // direct-to-LDS loads issued ahead of its X loads; only the wave itself
+    // reads them (no block barrier), each read after the wait for its step's
+    // X, which completes after them (loads complete in issue order)
+    const uint32_t sdst = (uint32_t)(size_t)(SVDQ_AS3 float*)svl + 512u * (uint32_t)t0;
+    for (int u = 0; 2 * u < t1 - t0; ++u) {
+      // an odd count ends with half a kilobyte: lanes 0-31 only
+      if (2 * u + 1 < t1 - t0 || lane < 32)
+        dma16(reinterpret_cast<const uint8_t*>(sinv), 512u * (uint32_t)t0 + 1024u * u + 16u * lane, sdst + 1024u * u);
+    }
   }
   Slot ring[2];
   if (t0 < t1) load(t0, ring[0]);
   if (t0 + 1 < t1) load(t0 + 1, ring[1]);
-  if constexpr (SL) __syncthreads();
 
   v4f acc[NTZ];
 #pragma unroll
@@ -153,7 +179,14 @@ __global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __res
 
   // x^ = fp32(x * 1/lambda) for the lane's 32 elements of step t
   auto smooth = [&](int t, const Slot& sl, float* xh) __attribute__((always_inline)) {
-    const int k0 = t * 128 + 32 * g;
+    int k0 = t * 128 + 32 * g;
+    if constexpr (SL) {
+      // a zero that depends on this step's X: the LDS reads below cannot be
+      // issued before the X loads (and the older staging loads) are done
+      int dep;
+      asm volatile("v_and_b32 %0, 0, %1" : "=v"(dep) : "v"(sl.x[0][0]));
+      k0 += dep << 5;   // keeps the 16-byte alignment of the reads visible
+    }
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const v4f iv = SL ? *reinterpret_cast<const v4f*>(svl + k0 + 4 * c) : sl.s[SL ? 0 : c];
@@ -412,25 +445,6 @@ constexpr int MX_SC_BYTES = (MX_BM + MX_BN) * 16;     // scale dwords of one 4-s
 constexpr int MX_DUMMY = MX_NBUF * MX_STEP_BYTES + 2 * MX_SC_BYTES;   // 1 KB per wave, see below
 constexpr int MX_LDS = MX_DUMMY + 8 * 1024;
 constexpr int MX_LDS_LRF = MX_DUMMY + 16 * 1024;   // the dummy region doubles as the first L2' chunk
-
-#define SVDQ_AS3 __attribute__((address_space(3)))
-
-// One wave-wide 1 KB direct-to-LDS copy: lane i's 16 bytes at sbase + voff
-// (sbase wave-uniform, voff per lane) land at LDS byte lds_base + 16 i.
-// Issued from asm so that the compiler does not serialise it against
-// unrelated LDS reads; completion is tracked with explicit vmcnt waits.
-// M0 is restored before the asm block ends.
-__device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, uint32_t lds_base) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dwordx4 %2, %3\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(sbase)
-      : "memory");
-}
 
 // Blocks are dealt to the 8 XCDs round robin; give each XCD a contiguous run
 // of tile ids (a band of out-feature tiles, all token tiles), and order the
