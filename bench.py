@@ -306,6 +306,8 @@ def main():
     t_stepr = float(np.median(msr_chunks)) * 1e-3
     t_stepu = float(np.median(msu_chunks)) * 1e-3
 
+    sustained = sustained_peak(torch, B, fmt, stream, kb_achieved)
+
     cpu, parity = None, None
     if not args.no_cpu_baseline and not args.skip_oracle:
         # The CPU-baseline leg: the fp64 oracle prepares the same layer and
@@ -355,6 +357,7 @@ def main():
                      "frac": kb_achieved / PEAK[fmt],
                      "traffic": traffic, "kernel": kb_kernel_names(fmt, K, r)[0] + " (quantized GEMM + lora_up + bias)",
                      "algorithmic_ops_per_launch": ops, "algorithmic_bytes_per_launch": kb_b},
+        "sustained_peak": sustained,
         "ka": {"us": t_ka * 1e6, "algorithmic_bytes": ka_b, "GB_per_s": ka_b / t_ka / 1e9,
                "frac_of_hbm": ka_b / t_ka / HBM_PEAK},
         "kb_us": t_kb * 1e6,
@@ -378,6 +381,40 @@ def main():
     }
     print(json.dumps(out))
 
+
+def sustained_peak(torch, B, fmt, stream, kb_achieved):
+    """What the matrix units sustain on this device, beside the datasheet
+    peak: every compute unit issuing MFMAs of K-B's arithmetic (FP4 for
+    MXFP4, int8 for INT4 and W8A8) back to back on changing operands, with
+    no memory traffic (svdq_mfma_rate_probe). Random operand bytes toggle
+    the most and bound what real data gets; zero operands the least."""
+    kind = 0 if fmt in ("mxfp4", "mxfp4_ocp") else 1
+    blocks = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    iters = 2000
+    per_iter = 32 if kind == 0 else 16
+    ops = blocks * 8 * per_iter * iters * 65536
+    sink = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+    marks = torch.zeros(blocks * 16, dtype=torch.int64, device="cuda")
+    res = {}
+    for name, zero in (("random_operands", 0), ("zero_operands", 1)):
+        B.mfma_rate_probe(kind, zero, blocks, iters, sink, marks, stream)
+        times = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            B.mfma_rate_probe(kind, zero, blocks, iters, sink, marks, stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e-3)
+        m = marks.view(-1, 2).cpu().numpy().astype(np.float64)
+        clock = float(np.median(m[:, 0] / (m[:, 1] / 100e6))) / 1e9
+        res[name] = {"rate": ops / float(np.median(times)) / 1e12, "clock_GHz": clock}
+    rnd = res["random_operands"]["rate"]
+    return {"mfma": "scaled 16x16x128 FP4" if kind == 0 else "32x32x32 int8", "unit": "TFLOP/s",
+            "random_operands": res["random_operands"], "zero_operands": res["zero_operands"],
+            "kb_frac_of_random_operands": kb_achieved / 1e12 / rnd,
+            "how": f"{blocks} blocks of two waves per SIMD, {per_iter} MFMAs per wave and iteration, {iters} "
+                   "iterations, operands changing every MFMA, no memory traffic; median of 3 launches"}
 
 def working_set_note(X, M, N, prep, layer):
     """How much of one step's data the 256 MB last-level cache can hold

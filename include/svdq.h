@@ -370,6 +370,26 @@ int32_t svdq_abi_version(void);
  * SVDQ_ERR_DEVICE if HIP cannot be queried (e.g. no GPU present). */
 svdq_status svdq_device_check(int32_t device);
 
+/* Sustained matrix-unit rate of the current device, a diagnostic for pricing
+ * the GEMM kernels against what the chip delivers beside its datasheet peak
+ * (not part of the layer).  `blocks` blocks of 512 threads (two waves per
+ * SIMD; one block per compute unit covers the chip) each issue MFMAs back to
+ * back for `iters` iterations with independent accumulators, on operands
+ * that change every MFMA (bytes from a fixed integer hash, or all zero when
+ * zero_operands != 0) and with no memory traffic in the loop:
+ *   kind 0: scaled 16x16x128 FP4 (E2M1, unit scales), 32 per wave and iteration;
+ *   kind 1: 32x32x32 int8, 16 per wave and iteration.
+ * Each MFMA is 65536 operations, so one launch does blocks * 8 * 32 * iters
+ * (kind 0) or blocks * 8 * 16 * iters (kind 1) of them; the caller times the
+ * launch on `stream`.  sink: device, blocks * 512 floats, written so the
+ * work is kept.  marks: device, blocks * 16 uint64 (per wave: shader-clock
+ * cycles, then 100 MHz wall-clock ticks, of its loop), or NULL.
+ * Errors: ARG (kind not 0/1, blocks outside 1..65535, iters outside
+ * 1..2^20, NULL sink), ALIGN (sink not 4-byte or marks not 8-byte aligned),
+ * UNSUPPORTED (not gfx950), DEVICE. */
+svdq_status svdq_mfma_rate_probe(int32_t kind, int32_t zero_operands, int32_t blocks, int32_t iters,
+                                 float* sink, uint64_t* marks, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

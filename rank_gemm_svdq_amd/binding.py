@@ -18,7 +18,7 @@ __all__ = [
     "prepare", "attach_lora", "kernel_layout", "unpack_activations", "DeviceLayer",
     "quantize_lora_down", "gemm_lora_up", "linear_forward", "linear_forward_unfused", "linear_forward_noalloc",
     "NOALLOC_MAX_WORKSPACE", "fmt_code", "LIB_PATH",
-    "ABI_VERSION", "reservoir_select", "smooth_candidates", "search_workspace_bytes", "smooth_search", "SearchOpts", "SearchResult",
+    "ABI_VERSION", "mfma_rate_probe", "reservoir_select", "smooth_candidates", "search_workspace_bytes", "smooth_search", "SearchOpts", "SearchResult",
 ]
 
 INT4 = 0
@@ -125,6 +125,7 @@ def lib():
     if L.svdq_abi_version() != ABI_VERSION:
         raise RuntimeError(f"libsvdq.so ABI {L.svdq_abi_version()} != {ABI_VERSION}: rebuild the library")
     L.svdq_device_check.argtypes = [i32]
+    L.svdq_mfma_rate_probe.argtypes = [i32, i32, i32, i32, vp, vp, vp]
     L.svdq_layer_sizes.argtypes = [i32, i32, i32, i32, C.POINTER(Sizes)]
     L.svdq_workspace_layout.argtypes = [i32, i32, i32, i32, C.POINTER(WsLayout)]
     L.svdq_workspace_bytes.restype = sz
@@ -374,6 +375,24 @@ def _stream(stream):
     torch = _torch()
     s = torch.cuda.current_stream() if stream is None else stream
     return C.c_void_p(s.cuda_stream)
+
+
+def mfma_rate_probe(kind, zero_operands, blocks, iters, sink, marks=None, stream=None):
+    """svdq_mfma_rate_probe (a diagnostic, not part of the layer): sink a
+    contiguous float32 CUDA tensor of at least blocks * 512 elements, marks
+    None or a contiguous int64 CUDA tensor of at least blocks * 16."""
+    torch = _torch()
+    where = "svdq_mfma_rate_probe"
+    if not (isinstance(sink, torch.Tensor) and sink.is_cuda and sink.dtype == torch.float32 and sink.is_contiguous()
+            and sink.numel() >= blocks * 512):
+        raise SvdqError(1, f"{where}: sink must be a contiguous float32 CUDA tensor of >= blocks * 512 elements")
+    if marks is not None and not (isinstance(marks, torch.Tensor) and marks.is_cuda and marks.dtype == torch.int64
+                                  and marks.is_contiguous() and marks.numel() >= blocks * 16
+                                  and marks.device == sink.device):
+        raise SvdqError(1, f"{where}: marks must be None or a contiguous int64 CUDA tensor of >= blocks * 16 "
+                           "elements on the sink's device")
+    _check(lib().svdq_mfma_rate_probe(kind, zero_operands, blocks, iters, sink.data_ptr(),
+                                      None if marks is None else marks.data_ptr(), _stream(stream)), where)
 
 
 def quantize_lora_down(layer, X, ws, stream=None):

@@ -24,6 +24,7 @@ UNITS = [
     ("host_eigen.cpp", ["g++"] + HOST_FLAGS + ["-ffp-contract=fast"]),
     ("device_kernels.hip", [HIPCC] + DEVICE_FLAGS),
     ("device_search.hip", [HIPCC] + DEVICE_FLAGS),
+    ("device_probe.hip", [HIPCC] + DEVICE_FLAGS),
 ]
 
 

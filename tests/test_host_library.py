@@ -222,6 +222,17 @@ def test_error_codes_device_entry_points_validate_before_hip():
     assert lib.svdq_gemm_lora_up(C.byref(badf), 0x3000, ws, 64, 0x2000, None) == 4
     mis = B.binding.Layer(256, 256, 32, 1, 0x1004, 0x2000, 0x3000, 0x4000, 0x5000, None)
     assert lib.svdq_gemm_lora_up(C.byref(mis), 0x3000, ws, 64, 0x2000, None) == 3
+    # the matrix-unit rate probe: kind, blocks, iterations, sink, alignment
+    pr = lib.svdq_mfma_rate_probe
+    assert pr(2, 0, 256, 100, 0x1000, None, None) == 1
+    assert pr(-1, 0, 256, 100, 0x1000, None, None) == 1
+    assert pr(0, 0, 0, 100, 0x1000, None, None) == 1
+    assert pr(0, 0, 65536, 100, 0x1000, None, None) == 1
+    assert pr(1, 0, 256, 0, 0x1000, None, None) == 1
+    assert pr(1, 0, 256, (1 << 20) + 1, 0x1000, None, None) == 1
+    assert pr(0, 0, 256, 100, None, None, None) == 1
+    assert pr(0, 0, 256, 100, 0x1002, None, None) == 3
+    assert pr(0, 1, 256, 100, 0x1000, 0x2004, None) == 3
 
 
 def _code_off(row, t, b, steps):
