@@ -113,6 +113,39 @@ def kb_kernel_names(fmt, K, rank):
     return (f"kb_i4_kernel<{ntr}>", f"kb_i4_kernelILi{ntr}E")
 
 
+def kb_uses_tail(fmt, M, N, cus):
+    """The library's split (kb_mx_main_cols): with 256 x 256 tiles whose last
+    round would fill at most a quarter of the compute units, the last columns
+    run as a second launch of 128 x 128 tiles."""
+    if fmt not in ("mxfp4", "mxfp4_ocp", "w8a8"):
+        return False
+    tm, tn = (M + 255) // 256, (N + 255) // 256
+    tiles = tm * tn
+    tail = tiles % cus
+    return tiles > cus and tail != 0 and 4 * tail <= cus and (tiles // cus) * cus // tm < tn
+
+
+def kb_label(fmt, M, N, K, rank, torch):
+    main = kb_kernel_names(fmt, K, rank)[0]
+    cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    if kb_uses_tail(fmt, M, N, cus):
+        return f"{main} + {kb_tail_names(fmt, K, rank)[0]} (last columns, 128 x 128 tiles)"
+    return main
+
+
+def kb_tail_names(fmt, K, rank):
+    """Names of the 128 x 128-tile K-B kernel that takes the last columns
+    when 256 x 256 tiles would leave a mostly idle last round (MXFP4 and
+    W8A8), or None."""
+    if fmt not in ("mxfp4", "mxfp4_ocp", "w8a8"):
+        return None
+    ntr = ((rank + 31) // 32 * 32) // 32
+    w8 = fmt == "w8a8"
+    odd = 0 if w8 else (K // 128) % 2
+    return (f"kb_mx_tail_kernel<{ntr}, {'true' if odd else 'false'}, {'true' if w8 else 'false'}>",
+            f"kb_mx_tail_kernelILi{ntr}ELb{odd}ELb{int(w8)}E")
+
+
 def oracle_sample(F, X, po, bias, seconds):
     """(rows, passes, seconds) of oracle forward work that takes about
     `seconds`: the first n token rows, n grown until it does, or whole-layer
@@ -355,7 +388,7 @@ def main():
         "pct_of_peak": 100.0 * tops / PEAK[fmt], "peak_name": PEAK_NAME[fmt],
         "roofline": {"bound": "mfma", "achieved": kb_achieved / 1e12, "peak": PEAK[fmt] / 1e12, "unit": "TFLOP/s",
                      "frac": kb_achieved / PEAK[fmt],
-                     "traffic": traffic, "kernel": kb_kernel_names(fmt, K, r)[0] + " (quantized GEMM + lora_up + bias)",
+                     "traffic": traffic, "kernel": kb_label(fmt, M, N, K, r, torch) + " (quantized GEMM + lora_up + bias)",
                      "algorithmic_ops_per_launch": ops, "algorithmic_bytes_per_launch": kb_b},
         "sustained_peak": sustained,
         "ka": {"us": t_ka * 1e6, "algorithmic_bytes": ka_b, "GB_per_s": ka_b / t_ka / 1e9,
@@ -722,7 +755,8 @@ def summarize_profiles(d, config, fmt_override=None):
     lines = [f"# Kernel time, {key} (M={M} K={K} N={N} rank={r} {fmt})", "",
              "Command (from the repository root, TMPDIR=/tmp):", "", "    " + cmds["stats"], "",
              "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
-    kb_avg = None
+    kb_avg = tail_avg = None
+    tail_names = kb_tail_names(fmt, K, r)
     for row in rows:
         name = col(row, "Name", "KernelName")
         calls = int(float(col(row, "Calls")))
@@ -733,16 +767,25 @@ def summarize_profiles(d, config, fmt_override=None):
         lines.append(f"| {short_name} | {calls} | {avg:.2f} | {mn:.2f} | {mx:.2f} | {pct:.1f} |")
         if _matches(name, kb_names):
             kb_avg = avg
+        if tail_names and _matches(name, tail_names):
+            tail_avg = avg
     bench_json = os.path.join(d, "stats.json")
     if os.path.exists(bench_json):
         with open(bench_json) as fh:
             b = json.loads(fh.read().strip().splitlines()[-1])
         lines += ["", f"bench.py under the profiler: K-B median {b['kb_us']:.2f} us (HIP events on the launch "
                       f"stream), K-A median {b['ka']['us']:.2f} us, layer {b['value']:.0f} TOPS."]
-    if kb_avg is not None:
+    if kb_avg is not None and tail_avg is not None:
+        ops = main_ops(M, N, K)
+        tot = kb_avg + tail_avg
+        lines += [f"K-B is two launches here: {kb_names[0]} (256 x 256 tiles, the full rounds) {kb_avg:.2f} us + "
+                  f"{tail_names[0]} (128 x 128 tiles, the last columns) {tail_avg:.2f} us = {tot:.2f} us -> "
+                  f"{ops / (tot * 1e-6) / 1e12:.0f} TOP/s of 2MNK = {ops:.4g} ops per layer."]
+    elif kb_avg is not None:
         ops = main_ops(M, N, K)
         lines += [f"{kb_names[0]}: average {kb_avg:.2f} us -> {ops / (kb_avg * 1e-6) / 1e12:.0f} TOP/s of "
                   f"2MNK = {ops:.4g} ops per launch."]
+    kb_layer_avg = None if kb_avg is None else kb_avg + (tail_avg or 0.0)
     _write(os.path.join(ROOT, "profiles", f"{short}_{key}_kernel_stats.md"), "\n".join(lines) + "\n")
 
     # HBM traffic: FETCH_SIZE / WRITE_SIZE (KiB per dispatch), scaled by a
@@ -760,11 +803,13 @@ def summarize_profiles(d, config, fmt_override=None):
         big = max(copy) if copy else None           # the 256 MiB calibration copy
         factor = CALIB_BYTES / big if big else None
         kb = [v for n, vs in per.items() if _matches(n, kb_names) for v in vs]
+        kt = [v for n, vs in per.items() if tail_names and _matches(n, tail_names) for v in vs]
         ka = [v for n, vs in per.items() if _matches(n, ka_names) for v in vs]
+        # per layer: the main launch plus, when there is one, the tail launch
         out[which] = {"copy_counter_bytes": big, "factor": factor,
-                      "kb_counter_bytes": float(np.mean(kb)) if kb else None,
+                      "kb_counter_bytes": (float(np.mean(kb)) + (float(np.mean(kt)) if kt else 0.0)) if kb else None,
                       "ka_counter_bytes": float(np.mean(ka)) if ka else None,
-                      "kb_dispatches": len(kb), "ka_dispatches": len(ka)}
+                      "kb_dispatches": len(kb), "kb_tail_dispatches": len(kt), "ka_dispatches": len(ka)}
     f_, w_ = out["fetch"], out["write"]
     kb_alg = kb_bytes(M, N, K, r, fmt)
     ka_alg = ka_bytes(M, K, r, fmt)
@@ -781,8 +826,9 @@ def summarize_profiles(d, config, fmt_override=None):
              "| | FETCH_SIZE | WRITE_SIZE |", "|---|---|---|",
              f"| calibration copy, counter | {fmtb(f_['copy_counter_bytes'])} | {fmtb(w_['copy_counter_bytes'])} |",
              f"| scale factor | {f_['factor'] or float('nan'):.4f} | {w_['factor'] or float('nan'):.4f} |",
-             f"| {kb_names[0]}, counter (mean of {f_['kb_dispatches']}) | {fmtb(f_['kb_counter_bytes'])} | "
-             f"{fmtb(w_['kb_counter_bytes'])} |",
+             f"| {kb_names[0]}{' + ' + tail_names[0] if f_['kb_tail_dispatches'] else ''}, counter (mean of "
+             f"{f_['kb_dispatches']}{' + ' + str(f_['kb_tail_dispatches']) if f_['kb_tail_dispatches'] else ''}) | "
+             f"{fmtb(f_['kb_counter_bytes'])} | {fmtb(w_['kb_counter_bytes'])} |",
              f"| ka_kernel, counter (mean of {f_['ka_dispatches']}) | {fmtb(f_['ka_counter_bytes'])} | "
              f"{fmtb(w_['ka_counter_bytes'])} |", "",
              f"K-B scaled traffic {fmtb(kb_traffic)} against {fmtb(kb_alg)} algorithmic "
@@ -795,7 +841,8 @@ def summarize_profiles(d, config, fmt_override=None):
             t = json.load(fh)
     except (OSError, ValueError):
         t = {}
-    t[key] = {"kernel": kb_names[0], "kernel_source_sha256_16": kernel_source_hash(),
+    t[key] = {"kernel": kb_names[0] + (" + " + tail_names[0] if f_["kb_tail_dispatches"] else ""),
+              "kernel_source_sha256_16": kernel_source_hash(),
               "bytes_per_launch": kb_traffic, "ka_bytes_per_launch": ka_traffic,
               "kb_algorithmic_bytes": kb_alg, "ka_algorithmic_bytes": ka_alg,
               "fetch": f_, "write": w_, "commands": [cmds["fetch"], cmds["write"]]}
@@ -803,16 +850,17 @@ def summarize_profiles(d, config, fmt_override=None):
         json.dump(t, fh, indent=1, sort_keys=True)
     print("\n".join(lines))
     if os.path.isdir(os.path.join(d, "mfma")):
-        summarize_mfma(d, key, M, N, K, r, fmt, kb_names, kb_avg, cmds["mfma"], short)
+        summarize_mfma(d, key, M, N, K, r, fmt, kb_names, kb_layer_avg, cmds["mfma"], short, tail_names)
     if os.path.isdir(os.path.join(d, "waves")) and os.path.isdir(os.path.join(d, "l2")):
         ka_avg = next((float(col(row, "AverageNs")) / 1e3 for row in rows
                        if _matches(col(row, "Name", "KernelName"), ka_names)), None)
-        summarize_waves(d, key, M, N, K, r, fmt, {"K-A (ka_kernel)": (ka_names, ka_avg),
-                                                   f"K-B ({kb_names[0]})": (kb_names, kb_avg)},
-                        (cmds["waves"], cmds["l2"]))
+        kernels = {"K-A (ka_kernel)": (ka_names, ka_avg), f"K-B ({kb_names[0]})": (kb_names, kb_avg)}
+        if tail_names and tail_avg is not None:
+            kernels[f"K-B, last columns ({tail_names[0]})"] = (tail_names, tail_avg)
+        summarize_waves(d, key, M, N, K, r, fmt, kernels, (cmds["waves"], cmds["l2"]))
 
 
-def summarize_mfma(d, key, M, N, K, r, fmt, kb_names, kb_avg, cmd, short):
+def summarize_mfma(d, key, M, N, K, r, fmt, kb_names, kb_avg, cmd, short, tail_names=None):
     """MFMA utilisation of K-B from counters: SQ_VALU_MFMA_BUSY_CYCLES (summed
     over the SIMDs) per SIMD against SQ_BUSY_CYCLES (summed over the shader
     engines) per engine, i.e. the share of busy cycles in which a SIMD's
@@ -822,11 +870,14 @@ def summarize_mfma(d, key, M, N, K, r, fmt, kb_names, kb_avg, cmd, short):
     agent = [a for a in _csv(_find(os.path.join(d, "mfma"), "agent_info.csv")) if int(a.get("Simd_Count", 0) or 0) > 0]
     simds = int(agent[0]["Simd_Count"])
     engines = int(agent[0]["Num_Shader_Banks"])
-    vals = {}
+    vals, tvals = {}, {}
     for row in cc:
         if _matches(row["Kernel_Name"], kb_names):
             vals.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
-    mean = {k: float(np.mean(v)) for k, v in vals.items()}
+        elif tail_names and _matches(row["Kernel_Name"], tail_names):
+            tvals.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+    # per layer: the main launch plus the tail launch when there is one
+    mean = {k: float(np.mean(v)) + (float(np.mean(tvals[k])) if k in tvals else 0.0) for k, v in vals.items()}
     busy_simd = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / simds
     busy_se = mean["SQ_BUSY_CYCLES"] / engines
     ops = main_ops(M, N, K)
@@ -834,7 +885,9 @@ def summarize_mfma(d, key, M, N, K, r, fmt, kb_names, kb_avg, cmd, short):
     lines = [f"# MFMA utilisation of K-B, {key} (M={M} K={K} N={N} rank={r} {fmt})", "",
              "Command (from the repository root, TMPDIR=/tmp):", "", "    " + cmd, "",
              f"Agent: {simds} SIMDs, {engines} shader engines. Means over {len(vals.get('SQ_BUSY_CYCLES', []))} "
-             f"dispatches of {kb_names[0]}.", "",
+             f"dispatches of {kb_names[0]}" +
+             (f", plus those of {tail_names[0]} (the last columns; {len(tvals.get('SQ_BUSY_CYCLES', []))} "
+              "dispatches), summed per layer." if tvals else "."), "",
              "| counter | per dispatch | per SIMD or engine |", "|---|---|---|",
              f"| SQ_VALU_MFMA_BUSY_CYCLES | {mean['SQ_VALU_MFMA_BUSY_CYCLES']:.4g} | {busy_simd:.0f} per SIMD |",
              f"| SQ_BUSY_CYCLES | {mean['SQ_BUSY_CYCLES']:.4g} | {busy_se:.0f} per engine |",

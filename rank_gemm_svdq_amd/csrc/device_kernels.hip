@@ -435,16 +435,18 @@ __device__ __forceinline__ int swz(int r, int c) { return r * 64 + 16 * (c ^ chu
 // the 4 + 4 accumulators a lane holds for the pair are 8 consecutive
 // out-features of one token: one 16-byte store.
 
-constexpr int MX_BM = 256, MX_BN = 256;
-#ifndef SVDQ_MX_WAVES
-#define SVDQ_MX_WAVES 8
-#endif
-constexpr int MX_STEP_BYTES = (MX_BM + MX_BN) * 64;   // codes of one step, both operands
+constexpr int MX_BM = 256, MX_BN = 256;   // the main tile; the tail tile is 128 x 128
 constexpr int MX_NBUF = 4;
-constexpr int MX_SC_BYTES = (MX_BM + MX_BN) * 16;     // scale dwords of one 4-step group
-constexpr int MX_DUMMY = MX_NBUF * MX_STEP_BYTES + 2 * MX_SC_BYTES;   // 1 KB per wave, see below
-constexpr int MX_LDS = MX_DUMMY + 8 * 1024;
-constexpr int MX_LDS_LRF = MX_DUMMY + 16 * 1024;   // the dummy region doubles as the first L2' chunk
+constexpr int MX_SC_BYTES = 8 * 1024;     // scale records of one 4-step group: one 1 KB slot per wave
+// LDS plan of a TB x TB tile
+template <int TB>
+struct MxTile {
+  static constexpr int STEP = 2 * TB * 64;                          // codes of one step, both operands
+  static constexpr int DUMMY = MX_NBUF * STEP + 2 * MX_SC_BYTES;   // 1 KB per wave, see below
+  static constexpr int LDS = DUMMY + 8 * 1024;
+  // with the low-rank product first, the dummy region also takes the first L2' chunk (TB rows x 64 B)
+  static constexpr int LDS_LRF = DUMMY + (TB * 64 > 8 * 1024 ? TB * 64 : 8 * 1024);
+};
 
 // Blocks are dealt to the 8 XCDs round robin; give each XCD a contiguous run
 // of tile ids (a band of out-feature tiles, all token tiles), and order the
@@ -482,32 +484,39 @@ __device__ __forceinline__ int mx_nrow(int nt, int q) {
   return 32 * (nt >> 1) + 8 * (q >> 2) + 4 * (nt & 1) + (q & 3);
 }
 
-template <int NTR, bool ODD, int WAVES, bool W8 = false>
-__global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
-    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const float* __restrict__ zp,
-    const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws, const uint16_t* __restrict__ l2k,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int M, int N, int K, int rpad) {
+// The block covers out-features [n0, n1) of Y in TB-wide tiles (and all
+// token rows in TB-high tiles).
+template <int NTR, bool ODD, bool W8, int TB>
+__device__ __forceinline__ void kb_mx_body(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
+                                           const float* __restrict__ zp, const uint8_t* __restrict__ wq,
+                                           const uint8_t* __restrict__ ws, const uint16_t* __restrict__ l2k,
+                                           const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int M,
+                                           int N, int K, int rpad, int n0, int n1) {
+  static_assert(TB == 256 || TB == 128, "tile side");
+  using G = MxTile<TB>;
+  constexpr int WAVES = 8;
   // LRF: the low-rank product Z L2' is formed first, while the first code
   // steps are in flight (float accumulators only, so not for W8)
   constexpr bool LRF = !W8 && NTR > 0;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[LRF ? MX_LDS_LRF : MX_LDS];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[LRF ? G::LDS_LRF : G::LDS];
   const uint32_t lds_u32 = (uint32_t)(size_t)(SVDQ_AS3 uint8_t*)lds;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // WAVES = 8: waves own 128 tokens x 64 out-features; WAVES = 4: 128 x 128
-  constexpr int NTW = 32 / WAVES;        // 16-row weight tiles per wave
-  constexpr int UPW = 32 / WAVES;        // 1 KB code units per wave and step
-  constexpr int RPW = 8 / WAVES;         // 1 KB scale records per wave and 4 steps
+  // waves own TB/2 tokens x TB/4 out-features
+  constexpr int NTW = TB / 64;           // 16-row weight tiles per wave
+  constexpr int TM = TB / 32;            // 16-row token tiles per wave
+  constexpr int UPW = TB / 64;           // 1 KB code units per wave and step
+  constexpr int RECS = TB / 64;          // 1 KB scale records per operand and 4 steps
   const int wm = wave & 1, wn = wave >> 1;
   const int l16 = lane & 15, g = lane >> 4;
-  const int tiles_m = (M + MX_BM - 1) / MX_BM, tiles_n = (N + MX_BN - 1) / MX_BN;
+  const int tiles_m = (M + TB - 1) / TB, tiles_n = (n1 - n0 + TB - 1) / TB;
   int tm, tn;
   mx_tile_of(blockIdx.x, tiles_m, tiles_n, &tm, &tn);
-  const int tile_m = tm * MX_BM, tile_n = tn * MX_BN;
+  const int tile_m = tm * TB, tile_n = n0 + tn * TB;
   // 64-byte code steps: 128 FP4 elements, or 64 int8 elements (W8)
   const int steps = W8 ? K / 64 : K / 128;
   const int ks4 = (steps + 3) / 4;
-  const int m_base = tile_m + 128 * wm, n_base = tile_n + 16 * NTW * wn;
+  const int m_base = tile_m + (TB / 2) * wm, n_base = tile_n + 16 * NTW * wn;
 
   // ---- DMA plan.  Codes are stored in 1 KB units of 16 rows x one step, in
   // the order the step buffers hold them (codes layout), so every load is
@@ -523,31 +532,27 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
   uint32_t coff[UPW];
 #pragma unroll
   for (int j = 0; j < UPW; ++j) {
-    const int grp16 = min(g0 + ((UPW * wave + j) & 15), gmax);
+    const int grp16 = min(g0 + UPW * (wave & 3) + j, gmax);
     coff[j] = (uint32_t)grp16 * (uint32_t)steps * 1024u + 16u * lane;
   }
-  // Scales: 1 KB records of 64 rows x 4 steps, 8 per 4-step group (records
-  // 0-3 token rows, 4-7 weight rows); wave w moves records RPW w ..
+  // Scales: 1 KB records of 64 rows x 4 steps, RECS per operand and 4-step
+  // group, into slots 0-3 (token rows) and 4-7 (weight rows) of the group's
+  // buffer: wave w moves record w & 3 of its operand into slot w.  With
+  // fewer than 4 records (TB = 128) the other waves re-read the last one into
+  // their own slot, which nothing reads, so every wave issues one load.
   const uint8_t* sbase = tokw ? xs : ws;
   const int smax = tokw ? (M + 63) / 64 - 1 : (N + 63) / 64 - 1;
-  uint32_t soff[RPW];
-#pragma unroll
-  for (int j = 0; j < RPW; ++j) {
-    const int grp64 = min(((tokw ? tile_m : tile_n) >> 6) + ((RPW * wave + j) & 3), smax);
-    soff[j] = (uint32_t)grp64 * (uint32_t)ks4 * 1024u + 16u * lane;
-  }
-  const uint32_t scale_lds = lds_u32 + MX_NBUF * MX_STEP_BYTES;
+  const int grp64 = min(((tokw ? tile_m : tile_n) >> 6) + min(wave & 3, RECS - 1), smax);
+  const uint32_t soff = (uint32_t)grp64 * (uint32_t)ks4 * 1024u + 16u * lane;
+  const uint32_t scale_lds = lds_u32 + MX_NBUF * G::STEP;
   auto issue_codes = [&](int t) __attribute__((always_inline)) {
-    const uint32_t b = lds_u32 + (uint32_t)(t % MX_NBUF) * MX_STEP_BYTES + (uint32_t)wave * (1024u * UPW);
+    const uint32_t b = lds_u32 + (uint32_t)(t % MX_NBUF) * G::STEP + (uint32_t)wave * (1024u * UPW);
 #pragma unroll
     for (int j = 0; j < UPW; ++j) dma16(cbase + (size_t)t * 1024, coff[j], b + 1024u * j);
   };
   auto issue_scales = [&](int grp) __attribute__((always_inline)) {
     if constexpr (W8) return;   // W8: per-row scales, applied after the K loop
-#pragma unroll
-    for (int j = 0; j < RPW; ++j)
-      dma16(sbase + (size_t)grp * 1024, soff[j],
-            scale_lds + (uint32_t)(grp & 1) * MX_SC_BYTES + (uint32_t)(RPW * wave + j) * 1024u);
+    dma16(sbase + (size_t)grp * 1024, soff, scale_lds + (uint32_t)(grp & 1) * MX_SC_BYTES + (uint32_t)wave * 1024u);
   };
 
   // fragment addresses (without the step-buffer offset): token fragment q
@@ -555,14 +560,14 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
   // fragment nt reads the permuted row 16 NTW wn + mx_nrow(nt, l16)
   uint32_t boff[2], aoff[NTW];
 #pragma unroll
-  for (int par = 0; par < 2; ++par) boff[par] = (uint32_t)swz(128 * wm + 16 * par + l16, g) - 1024u * par;
+  for (int par = 0; par < 2; ++par) boff[par] = (uint32_t)swz((TB / 2) * wm + 16 * par + l16, g) - 1024u * par;
 #pragma unroll
-  for (int nt = 0; nt < NTW; ++nt) aoff[nt] = (uint32_t)(MX_BM * 64 + swz(16 * NTW * wn + mx_nrow(nt, l16), g));
+  for (int nt = 0; nt < NTW; ++nt) aoff[nt] = (uint32_t)(TB * 64 + swz(16 * NTW * wn + mx_nrow(nt, l16), g));
   // bo: byte offset of a step buffer, kept opaque to the optimiser so that
   // it does not hoist one address register per (buffer, fragment) pair out
   // of the unrolled loop
   auto buf_of = [&](int t) __attribute__((always_inline)) -> uint32_t {
-    uint32_t bo = (uint32_t)(t % MX_NBUF) * MX_STEP_BYTES;
+    uint32_t bo = (uint32_t)(t % MX_NBUF) * G::STEP;
     asm volatile("" : "+s"(bo));
     return bo;
   };
@@ -576,52 +581,56 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
   // steps of a group; it is read at the group's first pair (tp % 4 == 0)
   // and shifted down by 16 bits for its second, so that the bytes of steps
   // (tp, tp+1) always sit in the low half and the MFMA's op_sel picks byte J.
-  uint32_t asc[NTW], bsc[8];
+  uint32_t asc[NTW], bsc[TM];
   auto read_scales = [&](int tp) __attribute__((always_inline)) {
     if constexpr (W8) return;
     if ((tp & 3) != 0) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) bsc[q] >>= 16;
+      for (int q = 0; q < TM; ++q) bsc[q] >>= 16;
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) asc[nt] >>= 16;
       return;
     }
-    uint32_t so = (uint32_t)(MX_NBUF * MX_STEP_BYTES + ((tp >> 2) & 1) * MX_SC_BYTES);
+    uint32_t so = (uint32_t)(MX_NBUF * G::STEP + ((tp >> 2) & 1) * MX_SC_BYTES);
     asm volatile("" : "+s"(so));
     const uint8_t* sc = lds + so;
     // 1 KB records of 64 rows: token fragment q is rows 16 (q % 4) .. of
-    // record 2 wm + q / 4; the weight records hold the wave's fragments in
-    // order (16 rows per tile nt); dword g of 16 rows = 256 contiguous bytes
+    // the record in slot (TB / 128) wm + q / 4; the weight records (slots
+    // 4 ..) hold the fragments in order, 16 rows per tile, so the wave's
+    // tile nt is 16-row block (16 NTW wn + 16 nt) % 64 / 16 of slot
+    // 4 + (16 NTW wn + 16 nt) / 64; dword g of 16 rows = 256 contiguous bytes
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      bsc[q] = *reinterpret_cast<const uint32_t*>(sc + 1024 * (2 * wm + (q >> 2)) + 4 * (64 * (q & 3) + 16 * g + l16));
+    for (int q = 0; q < TM; ++q)
+      bsc[q] = *reinterpret_cast<const uint32_t*>(sc + 1024 * ((TB / 128) * wm + (q >> 2)) +
+                                                  4 * (64 * (q & 3) + 16 * g + l16));
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt)
-      asc[nt] = *reinterpret_cast<const uint32_t*>(sc + 1024 * ((MX_BM + 16 * NTW * wn) / 64 + (nt >> 2)) +
-                                                   4 * (64 * (nt & 3) + 16 * g + l16));
+    for (int nt = 0; nt < NTW; ++nt) {
+      const int wr = 16 * NTW * wn + 16 * nt;
+      asc[nt] = *reinterpret_cast<const uint32_t*>(sc + 1024 * (4 + wr / 64) + 4 * (64 * ((wr & 63) >> 4) + 16 * g + l16));
+    }
   };
   // The lane index is made opaque in these two so that their address
   // arithmetic is redone where they are called instead of being hoisted out
   // of the main loop into live registers.
   auto issue_z = [&](int u, uint32_t zdst) __attribute__((always_inline)) {
-    // Z: 32 units of 8 rows x 128 B; wave w moves units 32/WAVES each
+    // Z: TB/8 units of 8 rows x 128 B; wave w moves TB/64 of them
     int ln = lane;
     asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int j = 0; j < 32 / WAVES; ++j) {
-      const int unit = (32 / WAVES) * wave + j, row = 8 * unit + (ln >> 3);
+    for (int j = 0; j < TB / 64; ++j) {
+      const int unit = (TB / 64) * wave + j, row = 8 * unit + (ln >> 3);
       const int m = min(tile_m + row, M - 1);
       dma16(reinterpret_cast<const uint8_t*>(zp),
             ((uint32_t)m * (uint32_t)rpad + 32u * u) * 4u + 16u * ((ln & 7) ^ zswz(row)), zdst + 1024u * unit);
     }
   };
   auto issue_l2 = [&](int u, uint32_t ldst) __attribute__((always_inline)) {
-    // L2'^T: 16 units of 16 rows x 64 B; wave w moves units 16/WAVES each
+    // L2'^T: TB/16 units of 16 rows x 64 B; wave w moves TB/128 of them
     int ln = lane;
     asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int j = 0; j < 16 / WAVES; ++j) {
-      const int unit = (16 / WAVES) * wave + j, row = 16 * unit + (ln >> 2);
+    for (int j = 0; j < TB / 128; ++j) {
+      const int unit = (TB / 128) * wave + j, row = 16 * unit + (ln >> 2);
       const int n = min(tile_n + row, N - 1);
       dma16(reinterpret_cast<const uint8_t*>(l2k),
             ((uint32_t)n * (uint32_t)rpad + 32u * u) * 2u + 16u * ((ln & 3) ^ lswz(row)), ldst + 1024u * unit);
@@ -629,14 +638,14 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
   };
   // acc += Z L2' for one 32-column chunk of the rank, from Z (rows of the
   // wave's tokens, bf16 hi and lo) and L2'^T (rows of its out-features) in LDS
-  auto lr_mfma = [&](uint32_t zoff, uint32_t loff, v4f (&ac)[NTW][8]) __attribute__((always_inline)) {
+  auto lr_mfma = [&](uint32_t zoff, uint32_t loff, v4f (&ac)[NTW][TM]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int mh = 0; mh < 2; ++mh) {
+    for (int mh = 0; mh < TM / 4; ++mh) {
       v8bf bh[4], bl[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int mt = 4 * mh + k;
-        const int zrow = 128 * wm + 16 * mt + l16;
+        const int zrow = (TB / 2) * wm + 16 * mt + l16;
         bh[k] = *reinterpret_cast<const v8bf*>(lds + zoff + zrow * 128 + 16 * (g ^ zswz(zrow)));
         bl[k] = *reinterpret_cast<const v8bf*>(lds + zoff + zrow * 128 + 16 * ((4 + g) ^ zswz(zrow)));
       }
@@ -653,18 +662,18 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
     }
   };
 
-  v4f acc[NTW][8];   // [weight tile][token tile]
+  v4f acc[NTW][TM];   // [weight tile][token tile]
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) acc[nt][mt] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < TM; ++mt) acc[nt][mt] = (v4f){0.f, 0.f, 0.f, 0.f};
 
   // Prologue.  LRF: chunk 0 of Z goes to ring buffer 3 and of L2' to the
   // dummy region (neither is written by code loads before step 0 has passed
   // its barrier), ahead of the scales and code steps 0-1; the low-rank MFMAs
   // run as soon as those two have landed, while the code steps are still in
   // flight.
-  constexpr uint32_t LR_Z = 3 * MX_STEP_BYTES, LR_L = MX_DUMMY;
+  constexpr uint32_t LR_Z = 3 * G::STEP, LR_L = G::DUMMY;
   if constexpr (LRF) {
     issue_z(0, lds_u32 + LR_Z);
     issue_l2(0, lds_u32 + LR_L);
@@ -678,10 +687,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
       if (u == 0) {
         // everything issued after the Z / L2' loads may still be in flight
         if (steps >= 2) {
-          if constexpr (WAVES == 8)
+          if constexpr (UPW == 4)
             asm volatile("s_waitcnt vmcnt(9)" ::: "memory");    // 1 scale record + 2 x 4 code units
           else
-            asm volatile("s_waitcnt vmcnt(18)" ::: "memory");   // 2 + 2 x 8
+            asm volatile("s_waitcnt vmcnt(5)" ::: "memory");    // 1 + 2 x 2
         } else {
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
@@ -712,8 +721,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
   // which no load targets any more.
   const int t_last = (steps - 1) & ~1;
   const bool lr_prefetch = !LRF && NTR > 0 && t_last >= 2;
-  const uint32_t zpre = (uint32_t)((t_last + 2) % MX_NBUF) * MX_STEP_BYTES;
-  const uint32_t lpre = (uint32_t)((t_last + 3) % MX_NBUF) * MX_STEP_BYTES;
+  const uint32_t zpre = (uint32_t)((t_last + 2) % MX_NBUF) * G::STEP;
+  const uint32_t lpre = (uint32_t)((t_last + 3) % MX_NBUF) * G::STEP;
   auto pair_top = [&](int t) __attribute__((always_inline)) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -742,29 +751,28 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
     const uint32_t bc = buf_of(t), bn = buf_of(t + 1);
     const bool more = t + 2 < steps, more2 = t + 3 < steps;
     const uint8_t* csrc = cbase + (size_t)(more ? t + 2 : steps - 1) * 1024;
-    const uint32_t cdst = more ? lds_u32 + (uint32_t)((t + 2) % MX_NBUF) * MX_STEP_BYTES + (uint32_t)wave * (1024u * UPW)
-                               : lds_u32 + MX_DUMMY + (uint32_t)wave * 1024u;
+    const uint32_t cdst = more ? lds_u32 + (uint32_t)((t + 2) % MX_NBUF) * G::STEP + (uint32_t)wave * (1024u * UPW)
+                               : lds_u32 + G::DUMMY + (uint32_t)wave * 1024u;
     const uint32_t cinc = more ? 1024u : 0u;
     const uint8_t* csrc2 = cbase + (size_t)(more2 ? t + 3 : steps - 1) * 1024;
-    const uint32_t cdst2 = more2 ? lds_u32 + (uint32_t)((t + 3) % MX_NBUF) * MX_STEP_BYTES + (uint32_t)wave * (1024u * UPW)
-                                 : lds_u32 + MX_DUMMY + (uint32_t)wave * 1024u;
+    const uint32_t cdst2 = more2 ? lds_u32 + (uint32_t)((t + 3) % MX_NBUF) * G::STEP + (uint32_t)wave * (1024u * UPW)
+                                 : lds_u32 + G::DUMMY + (uint32_t)wave * 1024u;
     const uint32_t cinc2 = more2 ? 1024u : 0u;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
+    for (int mt = 0; mt < TM; ++mt) {
       if constexpr (!LAST) {
-        // groups 0-3 load step t+2, groups 4-7 step t+3; UPW / 4 units each
-#pragma unroll
-        for (int j = 0; j < UPW / 4; ++j) {
-          const int u = (UPW / 4) * (mt & 3) + j;
-          if (mt < 4)
-            dma16(csrc, coff[u], cdst + cinc * u);
-          else
-            dma16(csrc2, coff[u], cdst2 + cinc2 * u);
-        }
+        // the first half of the MFMA groups loads step t+2, the second half
+        // step t+3, one unit per group
+        constexpr int HALF = TM / 2;
+        static_assert(UPW == HALF, "one code unit per MFMA group");
+        if (mt < HALF)
+          dma16(csrc, coff[mt], cdst + cinc * mt);
+        else
+          dma16(csrc2, coff[mt - HALF], cdst2 + cinc2 * (mt - HALF));
         if (mt < NTW) wf[J ^ 1][mt] = read_a(bn, mt);
-        tk[(mt + 3) & 3] = mt + 3 < 8 ? read_b(bc, mt + 3) : read_b(bn, mt - 5);
+        tk[(mt + 3) & 3] = mt + 3 < TM ? read_b(bc, mt + 3) : read_b(bn, mt + 3 - TM);
       } else {
-        if (mt + 3 < 8) tk[(mt + 3) & 3] = read_b(bc, mt + 3);
+        if (mt + 3 < TM) tk[(mt + 3) & 3] = read_b(bc, mt + 3);
       }
       const v4i bq = tk[mt & 3];
       if constexpr (W8) {
@@ -807,16 +815,16 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
     // 4 g + i of tile nt, per-token scale of the lane's column
     const float* sxp = reinterpret_cast<const float*>(xs);
     const float* swp = reinterpret_cast<const float*>(ws);
-    float sxv[8];
+    float sxv[TM];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) sxv[mt] = sxp[min(m_base + 16 * mt + l16, M - 1)];
+    for (int mt = 0; mt < TM; ++mt) sxv[mt] = sxp[min(m_base + 16 * mt + l16, M - 1)];
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float sw = swp[min(n_base + mx_nrow(nt, 4 * g + i), N - 1)];
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
+        for (int mt = 0; mt < TM; ++mt)
           acc[nt][mt][i] = (float)__builtin_bit_cast(v4i, acc[nt][mt])[i] * (sw * sxv[mt]);
       }
   }
@@ -835,7 +843,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
         // (or finished the previous chunk)
         __syncthreads();
         zoff = 0;
-        loff = MX_STEP_BYTES;
+        loff = G::STEP;
         issue_z(u, lds_u32 + zoff);
         issue_l2(u, lds_u32 + loff);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -881,7 +889,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
     bias8(n01, bv1);
     const bool lo8 = l16 < 8;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
+    for (int mt = 0; mt < TM; ++mt) {
       const v4i P0 = pack8(0, mt, bv0), P1 = pack8(1, mt, bv1);
       v4i S, R;
 #pragma unroll
@@ -903,17 +911,38 @@ __global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
   } else {
 #pragma unroll
     for (int p2 = 0; p2 < NTW / 2; ++p2) {
-      const int n0 = n_base + 32 * p2 + 8 * g;
+      const int nc0 = n_base + 32 * p2 + 8 * g;
       float bv[8];
-      bias8(n0, bv);
+      bias8(nc0, bv);
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
+      for (int mt = 0; mt < TM; ++mt) {
         const int m = m_base + 16 * mt + l16;
-        if (m >= M || n0 >= N) continue;
-        *reinterpret_cast<v4i*>(Y + (size_t)m * N + n0) = pack8(p2, mt, bv);
+        if (m >= M || nc0 >= N) continue;
+        *reinterpret_cast<v4i*>(Y + (size_t)m * N + nc0) = pack8(p2, mt, bv);
       }
     }
   }
+}
+
+// 256 x 256 tiles over out-features [n0, n1)
+template <int NTR, bool ODD, int WAVES, bool W8 = false>
+__global__ __launch_bounds__(WAVES * 64, 1) void kb_mx_kernel(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const float* __restrict__ zp,
+    const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws, const uint16_t* __restrict__ l2k,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int M, int N, int K, int rpad, int n0, int n1) {
+  static_assert(WAVES == 8, "8 waves, two per SIMD");
+  kb_mx_body<NTR, ODD, W8, 256>(xq, xs, zp, wq, ws, l2k, bias, Y, M, N, K, rpad, n0, n1);
+}
+
+// 128 x 128 tiles over out-features [n0, n1): the columns left over when
+// whole rounds of 256 x 256 tiles would leave most compute units idle in a
+// last, partial round
+template <int NTR, bool ODD, bool W8 = false>
+__global__ __launch_bounds__(512, 1) void kb_mx_tail_kernel(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const float* __restrict__ zp,
+    const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws, const uint16_t* __restrict__ l2k,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int M, int N, int K, int rpad, int n0, int n1) {
+  kb_mx_body<NTR, ODD, W8, 128>(xq, xs, zp, wq, ws, l2k, bias, Y, M, N, K, rpad, n0, n1);
 }
 
 // ------------------------------------------------------------ K-B, INT4
@@ -1343,26 +1372,52 @@ static hipError_t launch_ka(const svdq_layer& L, const uint16_t* X, int M, uint8
   return hipGetLastError();
 }
 
+// Out-features covered by 256-wide tiles; the rest go to 128-wide tiles.
+// When the 256 x 256 tiles leave a last round that fills at most a quarter
+// of the compute units, whole 256-wide columns are kept for the full rounds
+// and the remaining columns are cut into 128 x 128 tiles (four per 256 x 256
+// tile), one round of them over all units.  A 128 x 128 tile does about half
+// the work per unit time of a 256 x 256 one (eight waves with a quarter of
+// the MFMAs each per barrier), so it only pays against a mostly idle round.
+static int kb_mx_main_cols(int M, int N) {
+  const int cus = device_cus();
+  const int tm = (M + MX_BM - 1) / MX_BM, tn = (N + MX_BN - 1) / MX_BN, tiles = tm * tn;
+  const int tail = tiles % cus;
+  if (tiles <= cus || tail == 0 || 4 * tail > cus) return N;
+  const int cols = (tiles / cus) * cus / tm;   // 256-wide columns within the full rounds
+  return cols >= tn ? N : cols * MX_BN;
+}
+
 template <int NTR, bool W8 = false>
 static void launch_kb_mx(const svdq_layer& L, const uint8_t* ws, const svdq_ws_layout& W, int M, uint16_t* Y,
                          hipStream_t st) {
   const int rp = rank_pad(L.rank);
-  const int tiles = ((M + MX_BM - 1) / MX_BM) * ((L.N + MX_BN - 1) / MX_BN);
+  const int n_main = kb_mx_main_cols(M, L.N);
+  const int tiles = ((M + MX_BM - 1) / MX_BM) * ((n_main + MX_BN - 1) / MX_BN);
+  const int tail_tiles = ((M + 127) / 128) * ((L.N - n_main + 127) / 128);
+  const uint8_t *xq = ws + W.xq_off, *xs = ws + W.xs_off;
+  const float* zp = reinterpret_cast<const float*>(ws + W.z_off);
   // the K loop runs in pairs of 64-byte steps; an odd step count takes the
   // variant with one trailing step (8-bit codes always have an even count)
-  constexpr int WV = SVDQ_MX_WAVES;
-  if constexpr (W8)
-    hipLaunchKernelGGL((kb_mx_kernel<NTR, false, WV, true>), dim3(tiles), dim3(WV * 64), 0, st, ws + W.xq_off,
-                       ws + W.xs_off, reinterpret_cast<const float*>(ws + W.z_off), L.wq, L.ws, L.l2k,
-                       L.bias, Y, M, L.N, L.K, rp);
-  else if ((L.K / 128) % 2 == 0)
-    hipLaunchKernelGGL((kb_mx_kernel<NTR, false, WV>), dim3(tiles), dim3(WV * 64), 0, st, ws + W.xq_off,
-                       ws + W.xs_off, reinterpret_cast<const float*>(ws + W.z_off), L.wq, L.ws, L.l2k,
-                       L.bias, Y, M, L.N, L.K, rp);
-  else
-    hipLaunchKernelGGL((kb_mx_kernel<NTR, true, WV>), dim3(tiles), dim3(WV * 64), 0, st, ws + W.xq_off,
-                       ws + W.xs_off, reinterpret_cast<const float*>(ws + W.z_off), L.wq, L.ws, L.l2k,
-                       L.bias, Y, M, L.N, L.K, rp);
+  const bool odd = (L.K / 128) % 2 != 0;
+#define SVDQ_KB_MX(ODDV)                                                                                         \
+  do {                                                                                                           \
+    if (tiles > 0)                                                                                               \
+      hipLaunchKernelGGL((kb_mx_kernel<NTR, ODDV, 8, W8>), dim3(tiles), dim3(512), 0, st, xq, xs, zp, L.wq, L.ws, \
+                         L.l2k, L.bias, Y, M, L.N, L.K, rp, 0, n_main);                                          \
+    if (tail_tiles > 0)                                                                                          \
+      hipLaunchKernelGGL((kb_mx_tail_kernel<NTR, ODDV, W8>), dim3(tail_tiles), dim3(512), 0, st, xq, xs, zp, L.wq, \
+                         L.ws, L.l2k, L.bias, Y, M, L.N, L.K, rp, n_main, L.N);                                  \
+  } while (0)
+  if constexpr (W8) {
+    SVDQ_KB_MX(false);
+  } else {
+    if (odd)
+      SVDQ_KB_MX(true);
+    else
+      SVDQ_KB_MX(false);
+  }
+#undef SVDQ_KB_MX
 }
 
 template <int FMT>

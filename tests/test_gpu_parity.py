@@ -153,6 +153,30 @@ def test_more_ka_blocks_than_compute_units_unfused(fmt):
     assert rel_fro(run.y(), y_fused) <= 4e-3
 
 
+def _n_with_partial_round(M):
+    """An N whose 256 x 256 tiles leave a last round at most a quarter full,
+    so that K-B runs the last 256-wide columns as 128 x 128 tiles."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tm = (M + 255) // 256
+    tn = 2 * cus // tm + max(1, cus // (4 * tm))
+    assert 0 < (tm * tn) % cus <= cus // 4
+    return 256 * tn
+
+
+@pytest.mark.parametrize("fmt,M,K,rank", [
+    ("mxfp4", 4096, 256, 32), ("mxfp4", 4000, 384, 48),     # ragged token count, odd step count
+    ("mxfp4", 4096, 256, 0), ("mxfp4_ocp", 4096, 256, 32), ("w8a8", 4096, 256, 16),
+])
+def test_partial_last_round_runs_as_small_tiles(fmt, M, K, rank):
+    N = _n_with_partial_round(M)
+    s = S.spec("tiny", M=M, K=K, N=N, rank=rank, fmt=fmt)
+    d = S.make_layer(s)
+    run = GpuRun(d, fmt, rank, s.alpha).forward()
+    po = oracle_layer(d, fmt, rank, s.alpha)
+    _check_full(run, po, d["X"], d["bias"])
+
+
 @pytest.mark.parametrize("fmt", ["int4", "mxfp4", "w8a8", "mxfp4_ocp"])
 @pytest.mark.parametrize("M,K,N,rank", [(300, 1024, 400, 32), (17, 512, 272, 48), (130, 640, 144, 0)])
 def test_unfused_baseline(fmt, M, K, N, rank):
