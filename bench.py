@@ -179,6 +179,8 @@ def main():
     ap.add_argument("--config", default="flux_mlp_up")
     ap.add_argument("--fmt", default=None, help="override the workload's format (int4 | mxfp4 | mxfp4_ocp | w8a8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sustained-peak", action="store_true",
+                    help="skip the matrix-unit rate probe (profiling runs leave it out)")
     ap.add_argument("--no-rotate", action="store_true",
                     help="skip the cache-rotated run (distinct buffer sets cycled per step)")
     ap.add_argument("--rotate-sets", type=int, default=0,
@@ -339,7 +341,7 @@ def main():
     t_stepr = float(np.median(msr_chunks)) * 1e-3
     t_stepu = float(np.median(msu_chunks)) * 1e-3
 
-    sustained = sustained_peak(torch, B, fmt, stream, kb_achieved)
+    sustained = None if args.no_sustained_peak else sustained_peak(torch, B, fmt, stream, kb_achieved)
 
     cpu, parity = None, None
     if not args.no_cpu_baseline and not args.skip_oracle:
@@ -519,18 +521,18 @@ def rotated_run(args, torch, B, prep, bias_bits, X, M, N, stream):
 
 PROFILE_STEPS = {
     "stats": "--kernel-trace --stats --output-format csv -d {dir}/stats -o run -- "
-             "python -u bench.py --config {config} --steps 20 --warmup 5 --skip-oracle",
+             "python -u bench.py --config {config} --steps 20 --warmup 5 --skip-oracle --no-sustained-peak",
     "fetch": "--pmc FETCH_SIZE --output-format csv -d {dir}/fetch -o run -- "
-             "python -u bench.py --config {config} --steps 3 --warmup 1 --skip-oracle --calib-copy",
+             "python -u bench.py --config {config} --steps 3 --warmup 1 --skip-oracle --no-sustained-peak --calib-copy",
     "write": "--pmc WRITE_SIZE --output-format csv -d {dir}/write -o run -- "
-             "python -u bench.py --config {config} --steps 3 --warmup 1 --skip-oracle --calib-copy",
+             "python -u bench.py --config {config} --steps 3 --warmup 1 --skip-oracle --no-sustained-peak --calib-copy",
     "mfma": "--pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_WAVES --output-format csv "
-            "-d {dir}/mfma -o run -- python -u bench.py --config {config} --steps 3 --warmup 1 --skip-oracle",
+            "-d {dir}/mfma -o run -- python -u bench.py --config {config} --steps 3 --warmup 1 --skip-oracle --no-sustained-peak",
     "waves": "--pmc SQ_WAVES SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_BUSY_CYCLES SQ_INSTS_VMEM_RD "
              "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE --output-format csv "
-             "-d {dir}/waves -o run -- python -u bench.py --config {config} --steps 3 --warmup 1 --skip-oracle",
+             "-d {dir}/waves -o run -- python -u bench.py --config {config} --steps 3 --warmup 1 --skip-oracle --no-sustained-peak",
     "l2": "--pmc TCC_HIT_sum TCC_MISS_sum TCC_EA0_RDREQ_sum GRBM_GUI_ACTIVE --output-format csv "
-          "-d {dir}/l2 -o run -- python -u bench.py --config {config} --steps 3 --warmup 1 --skip-oracle",
+          "-d {dir}/l2 -o run -- python -u bench.py --config {config} --steps 3 --warmup 1 --skip-oracle --no-sustained-peak",
 }
 
 

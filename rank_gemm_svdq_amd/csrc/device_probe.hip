@@ -17,14 +17,13 @@
 #include "host_internal.h"
 
 namespace svdq {
-namespace {
 
 typedef int p4i __attribute__((ext_vector_type(4)));
 typedef int p8i __attribute__((ext_vector_type(8)));
 typedef float p4f __attribute__((ext_vector_type(4)));
 typedef int p16i __attribute__((ext_vector_type(16)));
 
-__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+static __device__ __forceinline__ uint32_t mix32(uint32_t x) {
   x ^= x >> 16;
   x *= 0x7feb352dU;
   x ^= x >> 15;
@@ -88,7 +87,6 @@ __global__ __launch_bounds__(512) void mfma_rate_kernel(int zero, int iters, flo
   }
 }
 
-}  // namespace
 }  // namespace svdq
 
 extern "C" svdq_status svdq_mfma_rate_probe(int32_t kind, int32_t zero_operands, int32_t blocks, int32_t iters,
