@@ -410,25 +410,30 @@ __global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __res
 // reads free of LDS bank conflicts)
 __device__ __forceinline__ int swz(int r, int c) { return r * 64 + 16 * (c ^ chunk_swz(r)); }
 
-// ----------------------------------------------------- K-B, MXFP4, large tile
+// ----------------------------------------------------- K-B, MXFP4 and W8A8
 //
 // 256 (tokens) x 256 (out-features) per block of 8 waves, two per SIMD; wave
 // w owns tokens 128 (w & 1) .. +128 and out-features 64 (w >> 1) .. +64, i.e.
-// 4 x 8 MFMA tiles of 16 x 16 (128 fp32 accumulators per lane).
+// 4 x 8 MFMA tiles of 16 x 16 (128 fp32 accumulators per lane).  The body is
+// a template on the tile side: kb_mx_kernel runs 256 x 256 tiles, and
+// kb_mx_tail_kernel 128 x 128 tiles (waves own 64 tokens x 32 out-features)
+// for the last columns when the large tiles would leave a mostly idle last
+// round.
 //
 // Codes travel global -> LDS by direct-to-LDS loads (no register staging)
-// into a ring of four 32 KB step buffers; scale dwords (one per row and 4
-// steps) travel the same way into a double buffer.  The K loop runs in
-// pairs of steps with one barrier per pair: the first step of a pair loads
-// the next pair into the two buffers the previous pair has left.  The
-// weight fragments of the next step are read into the other half of a
-// two-deep register set while the current MFMAs run, and token fragments
-// stream through four registers three MFMA groups ahead, so no fragment is
-// ever copied between registers.  A 16-bit LDS read per pair gives each
-// scale register the E8M0 bytes of both steps; the MFMA's op_sel picks the
-// byte.  The low-rank product Z L2' is formed before the K loop while the
-// first code steps are in flight (MXFP4), or after it from Z and L2' tiles
-// loaded into ring buffers the last pair no longer uses (W8A8).
+// into a ring of four step buffers (32 KB for the large tile); scale dwords
+// (one per row and 4 steps) travel the same way into a double buffer.  The
+// K loop runs in pairs of steps with one barrier per pair: the first step of
+// a pair loads the next pair into the two buffers the previous pair has
+// left.  The weight fragments of the next step are read into the other half
+// of a two-deep register set while the current MFMAs run, and token
+// fragments stream through four registers three MFMA groups ahead, so no
+// fragment is ever copied between registers.  One 32-bit LDS read per 4-step
+// group gives each scale register the E8M0 bytes of its four steps; it is
+// shifted down by 16 bits for the group's second pair, and the MFMA's op_sel
+// picks the byte.  The low-rank product Z L2' is formed before the K loop
+// while the first code steps are in flight (MXFP4), or after it from Z and
+// L2' tiles loaded into ring buffers the last pair no longer uses (W8A8).
 //
 // Weight rows are permuted inside each pair of 16-row MFMA tiles (2p, 2p+1):
 // MFMA row q of tile 2p + h is out-feature 32 p + 8 (q / 4) + 4 h + q % 4, so
