@@ -27,6 +27,12 @@ Workloads (M tokens, K in-features, N out-features):
                8-bit per-token activations and per-channel weights
 A bias ~ N(0, 0.1^2) is drawn for every layer.  The calibration draw has
 min(M, 1024) rows from the same distribution and the same outlier channels.
+
+Activations too large to draw on the host (the largest shapes the device
+path accepts, gigabytes of X) come from device_normal_bf16: torch's seeded
+Philox generator on the device, N(0, 1) in fp32, rounded to bfloat16 by
+torch (RNE); tests copy the rows they check back to the host, so both sides
+see the same values.
 """
 
 from dataclasses import dataclass, field, replace
@@ -147,3 +153,19 @@ def random_f32(seed, shape, lo, hi):
     """Uniform fp32 values in [lo, hi), for kernel-level tests."""
     rng = np.random.default_rng(np.random.SeedSequence(SEED_BASE + 2000 + seed))
     return rng.uniform(lo, hi, size=shape).astype(np.float32)
+
+
+def device_normal_bf16(seed, M, K, device="cuda", chunk_rows=1 << 16):
+    """[M, K] N(0, 1) bf16 values drawn on the device (torch's seeded
+    generator, fp32 rounded to bf16), returned as an int16 tensor of bf16 bit
+    patterns.  Drawn in row chunks so that the fp32 draw stays small."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(SEED_BASE + 3000 + seed)
+    out = torch.empty((M, K), dtype=torch.int16, device=device)
+    for r0 in range(0, M, chunk_rows):
+        r1 = min(M, r0 + chunk_rows)
+        v = torch.randn((r1 - r0, K), generator=g, device=device, dtype=torch.float32)
+        out[r0:r1] = v.to(torch.bfloat16).view(torch.int16)
+        del v
+    return out
