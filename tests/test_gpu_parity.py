@@ -57,6 +57,8 @@ def test_tiny_layer(fmt, use_bias):
     (4200, 256, 160, 48),                                          # more 16-row blocks than compute units
     (24, 16384, 64, 16),                                           # K = 16384: 16 steps of 1/lambda staged per wave
     (40, 16512, 64, 16),                                           # K above 16384: 1/lambda not staged in LDS
+    (3, 65536, 16, 16),                                            # the largest K with the smallest N
+    (20, 128, 262144, 16),                                         # the largest N with the smallest K
 ])
 def test_shapes_and_tails(fmt, M, K, N, rank):
     s = S.spec("tiny", M=M, K=K, N=N, rank=rank, fmt=fmt)
