@@ -99,7 +99,8 @@ __device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, uint3
 constexpr int KA_WAVES = 8;
 constexpr int KA_SL_MAX_K = 16384;   // 1/lambda is staged in LDS up to this K
 
-// One block handles 16 rows; its 8 waves split the K steps evenly and the
+// One block handles 16 rows; its NWV waves (8, or 4 when there are more
+// blocks than compute units) split the K steps evenly and the
 // down-projection partial sums are reduced in LDS, so Z leaves the kernel
 // once.  Lane l owns row l % 16 and the 32 consecutive elements
 // 32 (l / 16) .. +32 of each 128-element step.  Each wave keeps the next
@@ -109,20 +110,21 @@ constexpr int KA_SL_MAX_K = 16384;   // 1/lambda is staged in LDS up to this K
 // smoothed x^ = x / lambda, split into bf16 hi + lo, by the bf16 factor
 // L1', so it runs on bf16 MFMA with fp32 accumulation.  ZONLY drops the
 // quantisation (the unfused baseline's separate down-projection pass).
-template <int FMT, int NT, bool SL, bool ZONLY = false, bool RING = true>
-__global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __restrict__ X, int M, int K,
+template <int FMT, int NT, bool SL, bool ZONLY = false, bool RING = true, int NWV = KA_WAVES>
+__global__ __launch_bounds__(64 * NWV, 2) void ka_kernel(const uint16_t* __restrict__ X, int M, int K,
                                                           const float* __restrict__ sinv,
                                                           const v8bf* __restrict__ l1k,
                                                           uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
                                                           float* __restrict__ zout, int rpad) {
   constexpr int NTZ = NT > 0 ? NT : 1;
-  // down-factor fragments in the ring (RING: chosen when one block per
-  // compute unit runs; without them the kernel fits two blocks per unit)
+  // down-factor fragments in the ring (RING; without them the 8-wave
+  // kernel fits two blocks per unit, the W8A8 setting's choice when there
+  // are more blocks than compute units)
   constexpr bool WRING = RING && NT > 0 && NT <= (SL ? 4 : 2);
   constexpr int NW = WRING ? 4 * NT : 1;
   constexpr bool W8 = FMT == SVDQ_W8A8 && !ZONLY;
-  __shared__ float zred[NT > 0 ? KA_WAVES * 16 * NT * 16 : 1];
-  __shared__ float mred[W8 ? KA_WAVES * 16 : 1];
+  __shared__ float zred[NT > 0 ? NWV * 16 * NT * 16 : 1];
+  __shared__ float mred[W8 ? NWV * 16 : 1];
   extern __shared__ __attribute__((aligned(16))) float svl[];   // K floats when SL
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __res
   const int steps = K / 128;
   const int ks4 = (steps + 3) / 4;
   const size_t i4_tail = code_bytes(M, steps);   // INT4: the code tails follow the main parts
-  const int spw = (steps + KA_WAVES - 1) / KA_WAVES;
+  const int spw = (steps + NWV - 1) / NWV;
   const int t0 = wave * spw;
   const int t1 = min(steps, t0 + spw);
   const uint16_t* xrow = X + (size_t)rowc * K + 32 * g;
@@ -337,12 +339,12 @@ __global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __res
     // columns from the rank up to WP = rpad (the rank rounded up to 32) are
     // written as 0
     constexpr int WP = (W + 31) / 32 * 32;
-    for (int idx = threadIdx.x; idx < 16 * WP; idx += 64 * KA_WAVES) {
+    for (int idx = threadIdx.x; idx < 16 * WP; idx += 64 * NWV) {
       const int rr = idx / WP, cc = idx % WP;
       float sum = 0.f;
       if (cc < W) {
 #pragma unroll
-        for (int w = 0; w < KA_WAVES; ++w) sum += zred[(w * 16 + rr) * W + cc];
+        for (int w = 0; w < NWV; ++w) sum += zred[(w * 16 + rr) * W + cc];
       }
       // Z leaves as the bf16 pair hi + lo the up projection multiplies with:
       // per row and 32-column chunk, 32 hi values then 32 lo values
@@ -364,7 +366,7 @@ __global__ __launch_bounds__(64 * KA_WAVES) void ka_kernel(const uint16_t* __res
     __syncthreads();
     float am = 0.f;
 #pragma unroll
-    for (int w = 0; w < KA_WAVES; ++w) am = fmaxf(am, mred[w * 16 + r]);
+    for (int w = 0; w < NWV; ++w) am = fmaxf(am, mred[w * 16 + r]);
     const float sc = am / 127.0f;
     if (wave == 0 && g == 0 && live) reinterpret_cast<float*>(xs)[row] = sc;
     const float rcp = 1.0f / sc;   // sc == 0 only for an all-zero row
@@ -1318,46 +1320,57 @@ static int device_cus() {
   return v;
 }
 
-template <int FMT, int NT, bool SL, bool ZONLY, bool RING>
-static void launch_ka_one(dim3 grid, dim3 block, size_t lds, hipStream_t st, const uint16_t* X, int M,
-                          const svdq_layer& L, const v8bf* l1, uint8_t* xq, uint8_t* xs, float* z, int rp) {
-  hipLaunchKernelGGL((ka_kernel<FMT, NT, SL, ZONLY, RING>), grid, block, lds, st, X, M, L.K, L.smooth_inv, l1, xq,
-                     xs, z, rp);
+template <int FMT, int NT, bool SL, bool ZONLY, bool RING, int NWV = KA_WAVES>
+static void launch_ka_one(dim3 grid, size_t lds, hipStream_t st, const uint16_t* X, int M, const svdq_layer& L,
+                          const v8bf* l1, uint8_t* xq, uint8_t* xs, float* z, int rp) {
+  hipLaunchKernelGGL((ka_kernel<FMT, NT, SL, ZONLY, RING, NWV>), grid, dim3(64 * NWV), lds, st, X, M, L.K,
+                     L.smooth_inv, l1, xq, xs, z, rp);
 }
 
 template <int FMT, bool ZONLY = false>
 static hipError_t launch_ka(const svdq_layer& L, const uint16_t* X, int M, uint8_t* ws, const svdq_ws_layout& W,
                             hipStream_t st) {
   const int rp = rank_pad(L.rank);
-  dim3 grid((M + 15) / 16), block(64 * KA_WAVES);
+  dim3 grid((M + 15) / 16);
   uint8_t* xq = ws + W.xq_off;
   uint8_t* xs = ws + W.xs_off;
   float* z = reinterpret_cast<float*>(ws + W.z_off);
   const v8bf* l1 = reinterpret_cast<const v8bf*>(L.l1k);
   // With at most one block per compute unit the register ring of down-factor
-  // fragments hides their L2 latency; with more blocks than units the
-  // ring-free kernel (about 110 VGPRs) runs two blocks per unit, which
-  // hides it better.
+  // fragments hides their L2 latency.  With more blocks than units, blocks
+  // of 4 waves keep the ring (two blocks per unit, two waves per SIMD, each
+  // wave with twice the K steps to pipeline); blocks of 8 would either drop
+  // to one block per unit or, without the ring, wait for every step's
+  // fragments where they are used.  W8A8, whose second pass over X makes
+  // each wave's chain longer, keeps the ring-free 8-wave blocks (two per
+  // unit), measured slightly faster there.
   const bool ring = (int)grid.x <= device_cus();
+  constexpr bool W8P = FMT == SVDQ_W8A8 && !ZONLY;
 #define SVDQ_KA(NTV)                                                                                      \
   do {                                                                                                    \
     if (L.K <= KA_SL_MAX_K) {                                                                             \
       const size_t lds = (size_t)L.K * 4;                                                                 \
       if constexpr (NTV > 0 && NTV <= 4) {                                                                \
         if (!ring) {                                                                                      \
-          launch_ka_one<FMT, NTV, true, ZONLY, false>(grid, block, lds, st, X, M, L, l1, xq, xs, z, rp);  \
+          if constexpr (W8P)                                                                              \
+            launch_ka_one<FMT, NTV, true, ZONLY, false>(grid, lds, st, X, M, L, l1, xq, xs, z, rp);       \
+          else                                                                                            \
+            launch_ka_one<FMT, NTV, true, ZONLY, true, 4>(grid, lds, st, X, M, L, l1, xq, xs, z, rp);     \
           break;                                                                                          \
         }                                                                                                 \
       }                                                                                                   \
-      launch_ka_one<FMT, NTV, true, ZONLY, true>(grid, block, lds, st, X, M, L, l1, xq, xs, z, rp);       \
+      launch_ka_one<FMT, NTV, true, ZONLY, true>(grid, lds, st, X, M, L, l1, xq, xs, z, rp);              \
     } else {                                                                                              \
       if constexpr (NTV > 0 && NTV <= 2) {                                                                \
         if (!ring) {                                                                                      \
-          launch_ka_one<FMT, NTV, false, ZONLY, false>(grid, block, 0, st, X, M, L, l1, xq, xs, z, rp);   \
+          if constexpr (W8P)                                                                              \
+            launch_ka_one<FMT, NTV, false, ZONLY, false>(grid, 0, st, X, M, L, l1, xq, xs, z, rp);        \
+          else                                                                                            \
+            launch_ka_one<FMT, NTV, false, ZONLY, true, 4>(grid, 0, st, X, M, L, l1, xq, xs, z, rp);      \
           break;                                                                                          \
         }                                                                                                 \
       }                                                                                                   \
-      launch_ka_one<FMT, NTV, false, ZONLY, true>(grid, block, 0, st, X, M, L, l1, xq, xs, z, rp);        \
+      launch_ka_one<FMT, NTV, false, ZONLY, true>(grid, 0, st, X, M, L, l1, xq, xs, z, rp);               \
     }                                                                                                     \
   } while (0)
   // one 16-column MFMA tile of the down factor per 16 of the rank
