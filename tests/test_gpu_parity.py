@@ -55,6 +55,8 @@ def test_tiny_layer(fmt, use_bias):
     (70, 640, 384, 96), (257, 512, 400, 128),                      # ranks 96 and 128 (the maximum)
     (50, 512, 160, 80), (70, 384, 144, 112),                       # ranks 80 and 112 (odd 16-column tiles)
     (4200, 256, 160, 48),                                          # more 16-row blocks than compute units
+    (4200, 256, 160, 64),                                          # the same at rank 64 (4 fragment tiles in the ring)
+    (4200, 16512, 64, 32),                                         # the same with 1/lambda not staged in LDS
     (24, 16384, 64, 16),                                           # K = 16384: 16 steps of 1/lambda staged per wave
     (40, 16512, 64, 16),                                           # K above 16384: 1/lambda not staged in LDS
     (3, 65536, 16, 16),                                            # the largest K with the smallest N
