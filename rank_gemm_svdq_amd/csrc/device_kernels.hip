@@ -1250,12 +1250,14 @@ __global__ __launch_bounds__(I4_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
 // ------------------------------------------------- unfused baseline: up + add
 //
 // Y += Z L2' as its own pass over Y, for measuring what fusing the branch
-// into the GEMM epilogue saves.  A block of 4 waves covers 64 tokens x 64
-// out-features: wave w forms tokens 16 w .. +16 on bf16 MFMA (Z hi and lo
-// against L2'^T rows), the fp32 products pass through LDS, and the
-// read-modify-write of Y runs with 8 consecutive bf16 per lane, so every
-// load and store instruction covers whole 128-byte lines of Y rows.
-constexpr int KUP_LD = 68;   // LDS row stride (floats) of the 64 x 64 product tile
+// into the GEMM epilogue saves.  A block of 4 waves covers 64 tokens x 256
+// out-features as four 64-wide sub-tiles: wave w loads the Z fragments
+// (hi and lo) of tokens 16 w .. +16 once and forms each sub-tile's products
+// on bf16 MFMA against L2'^T rows; the fp32 products pass through LDS, and
+// the read-modify-write of Y runs with 8 consecutive bf16 per lane, so
+// every load and store instruction covers whole 128-byte lines of Y rows.
+constexpr int KUP_LD = 68;    // LDS row stride (floats) of the 64 x 64 product tile
+constexpr int KUP_SUB = 4;    // 64-wide sub-tiles per block
 
 template <int NTR>
 __global__ __launch_bounds__(256) void kup_kernel(const uint16_t* __restrict__ zp, const uint16_t* __restrict__ l2k,
@@ -1263,44 +1265,64 @@ __global__ __launch_bounds__(256) void kup_kernel(const uint16_t* __restrict__ z
   __shared__ float tile[64 * KUP_LD];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int tiles_n = (N + 63) / 64;
-  const int m0 = (blockIdx.x / tiles_n) * 64, n0 = (blockIdx.x % tiles_n) * 64;
+  const int tiles_n = (N + 64 * KUP_SUB - 1) / (64 * KUP_SUB);
+  const int m0 = (blockIdx.x / tiles_n) * 64, n0 = (blockIdx.x % tiles_n) * (64 * KUP_SUB);
   const int m = min(m0 + 16 * wave + l16, M - 1);
-  v4f acc[4];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) acc[nt] = (v4f){0.f, 0.f, 0.f, 0.f};
+  // the wave's Z fragments, reused by every sub-tile
+  v8bf bh[NTR], bl[NTR];
 #pragma unroll
   for (int u = 0; u < NTR; ++u) {
     const uint16_t* zr = zp + (size_t)m * 2 * rpad + 64 * u + 8 * g;
-    const v8bf bh = *reinterpret_cast<const v8bf*>(zr);
-    const v8bf bl = *reinterpret_cast<const v8bf*>(zr + 32);
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int n = min(n0 + 16 * nt + l16, N - 1);
-      const v8bf af = *reinterpret_cast<const v8bf*>(l2k + (size_t)n * rpad + 32 * u + 8 * g);
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bh, acc[nt], 0, 0, 0);
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bl, acc[nt], 0, 0, 0);
-    }
+    bh[u] = *reinterpret_cast<const v8bf*>(zr);
+    bl[u] = *reinterpret_cast<const v8bf*>(zr + 32);
   }
-  // lane holds out-features 16 nt + 4 g + i of token 16 wave + l16
+  for (int sub = 0; sub < KUP_SUB; ++sub) {
+    const int ns = n0 + 64 * sub;
+    if (ns >= N) break;   // uniform over the block
+    // 512 pieces of 8 outputs: row c / 8, columns 8 (c % 8) .. +8; the
+    // thread's two pieces of Y are loaded before the products are formed,
+    // so that their latency overlaps the L2' loads and MFMAs (each piece is
+    // read and written by this thread only)
+    v4i yin[2];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
-    *reinterpret_cast<v4f*>(&tile[(16 * wave + l16) * KUP_LD + 16 * nt + 4 * g]) = acc[nt];
-  __syncthreads();
-  // 512 pieces of 8 outputs: row c / 8, columns 8 (c % 8) .. +8
+    for (int j = 0; j < 2; ++j) {
+      const int c = (int)threadIdx.x + 256 * j, row = c >> 3, col = 8 * (c & 7);
+      const int mm = m0 + row, nn = ns + col;
+      yin[j] = (mm < M && nn < N) ? *reinterpret_cast<const v4i*>(Y + (size_t)mm * N + nn) : (v4i){0, 0, 0, 0};
+    }
+    v4f acc[4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int c = (int)threadIdx.x + 256 * j, row = c >> 3, col = 8 * (c & 7);
-    const int mm = m0 + row, nn = n0 + col;
-    if (mm >= M || nn >= N) continue;
-    v4i* yp = reinterpret_cast<v4i*>(Y + (size_t)mm * N + nn);
-    const v4i y = *yp;
-    const float* a = &tile[row * KUP_LD + col];
-    v4i o;
+    for (int nt = 0; nt < 4; ++nt) acc[nt] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      o[i] = (int)(bf16_rne(bf16_lo((uint32_t)y[i]) + a[2 * i]) | (bf16_rne(bf16_hi((uint32_t)y[i]) + a[2 * i + 1]) << 16));
-    *yp = o;
+    for (int u = 0; u < NTR; ++u) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int n = min(ns + 16 * nt + l16, N - 1);
+        const v8bf af = *reinterpret_cast<const v8bf*>(l2k + (size_t)n * rpad + 32 * u + 8 * g);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bh[u], acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bl[u], acc[nt], 0, 0, 0);
+      }
+    }
+    // lane holds out-features 16 nt + 4 g + i of token 16 wave + l16
+    if (sub > 0) __syncthreads();   // the previous sub-tile's reads of the tile are done
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+      *reinterpret_cast<v4f*>(&tile[(16 * wave + l16) * KUP_LD + 16 * nt + 4 * g]) = acc[nt];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = (int)threadIdx.x + 256 * j, row = c >> 3, col = 8 * (c & 7);
+      const int mm = m0 + row, nn = ns + col;
+      if (mm >= M || nn >= N) continue;
+      v4i* yp = reinterpret_cast<v4i*>(Y + (size_t)mm * N + nn);
+      const v4i y = yin[j];
+      const float* a = &tile[row * KUP_LD + col];
+      v4i o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[i] = (int)(bf16_rne(bf16_lo((uint32_t)y[i]) + a[2 * i]) | (bf16_rne(bf16_hi((uint32_t)y[i]) + a[2 * i + 1]) << 16));
+      *yp = o;
+    }
   }
 }
 
@@ -1648,7 +1670,7 @@ svdq_status svdq_linear_forward_unfused(const svdq_layer* layer, const uint16_t*
   });
   if (e == hipSuccess && layer->rank > 0) {
     const int rp = rank_pad(layer->rank);
-    const int tiles = ((M + 63) / 64) * ((layer->N + 63) / 64);
+    const int tiles = ((M + 63) / 64) * ((layer->N + 64 * KUP_SUB - 1) / (64 * KUP_SUB));
     const uint16_t* zp = reinterpret_cast<const uint16_t*>(w8 + W.z_off);
     switch (rp / 32) {
       case 1: hipLaunchKernelGGL(kup_kernel<1>, dim3(tiles), dim3(256), 0, st, zp, layer->l2k, Y, M, layer->N, rp); break;
